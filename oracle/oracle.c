@@ -1,0 +1,214 @@
+/*
+ * oracle.c -- plain, slow CPU reference for one paged GQA decode step.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  The GPU library never
+ * calls it and shares no code, header or table with it.
+ *
+ * What it computes, and where the pages define it:
+ *
+ *   Cache write.  "Tiny-vLLM: 거대 LLM 추론, 작은 엔진이..." page, second Q&A
+ *   ("'Tiny-vLLM'은 이 거대한 복잡성을..."): before the model runs, a
+ *   slot_mapping tells the KV store where each new token's key/value vectors go.
+ *   Slot encoding (our reading, the pages are silent): slot = block * BS + offset;
+ *   a slot < 0 or >= NB * BS is padding and is skipped.
+ *
+ *   Paging.  "vLLM" page, section "가상 메모리 방식의 해결": the cache is cut
+ *   into fixed blocks of 16 tokens and a table per sequence maps logical
+ *   positions to physical blocks, like an OS page table.  Position t of
+ *   sequence s lives in block block_tables[s][t / BS] at offset t % BS.
+ *
+ *   Attention.  "vLLM" page, section "Flash Attention": standard attention is
+ *   S = Q K^T, P = softmax(S), O = P V.  The query is the newest token's; it
+ *   attends to every cached position 0..n-1 of its sequence (decoder-only,
+ *   causal: "tiny-vllm 씹뜯맛즐 - (1)" page, section 1).  Scores carry the
+ *   factor 1/sqrt(head_dim) (0.125 for head_dim 64 = 2048 / 32, same page,
+ *   dimension list after section 6).
+ *
+ *   GQA.  "tiny-vllm 씹뜯맛즐 - (1)" page, section "2. Multi-Head Attention
+ *   대신 GQA", figure: query heads 0-3 share K/V head 0, heads 4-7 share K/V
+ *   head 1, ...; so query head h reads K/V head h / (Hq / Hkv).
+ *
+ * Cache layout (part of the library's interface, indexed here on its own):
+ *   K pool: [NB][Hkv][BS][D]   (one block and head = BS rows of D values)
+ *   V pool: [NB][Hkv][D][BS]   (the same tile stored dimension-major)
+ *   bf16 values are raw uint16 bit patterns.
+ *
+ * Arithmetic: double precision from the exact bf16 values; the two-pass
+ * softmax of the definition (max, then exponentials, then their sum); no
+ * blocking, no online update, no partitions.  The parallel loop runs over
+ * (sequence, query head) pairs only, so results do not depend on the thread
+ * count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/*
+ * Copy token i's K and V rows (k, v: [T][Hkv][D]) into the slot
+ * slot_mapping[i] of the pools.  Returns the number of tokens written,
+ * -1 on a bad argument, -2 if two tokens name the same slot (no pool is
+ * touched in either error case).
+ */
+long oracle_cache_write(const uint16_t *k, const uint16_t *v,
+                        uint16_t *k_cache, uint16_t *v_cache,
+                        const int64_t *slot_mapping, long num_tokens,
+                        int num_kv_heads, int head_dim, int block_size,
+                        long num_blocks)
+{
+    if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+        return -1;
+    long num_slots = num_blocks * (long)block_size;
+    unsigned char *taken = calloc((size_t)num_slots, 1);
+    if (!taken)
+        return -1;
+    for (long i = 0; i < num_tokens; ++i) {
+        int64_t slot = slot_mapping[i];
+        if (slot < 0 || slot >= num_slots)
+            continue;
+        if (taken[slot]) {
+            free(taken);
+            return -2;
+        }
+        taken[slot] = 1;
+    }
+    free(taken);
+
+    long written = 0;
+    for (long i = 0; i < num_tokens; ++i) {
+        int64_t slot = slot_mapping[i];
+        if (slot < 0 || slot >= num_slots)
+            continue;
+        long blk = (long)(slot / block_size);
+        long off = (long)(slot % block_size);
+        for (int h = 0; h < num_kv_heads; ++h) {
+            for (int d = 0; d < head_dim; ++d) {
+                long src = ((long)i * num_kv_heads + h) * head_dim + d;
+                long kdst = ((blk * num_kv_heads + h) * block_size + off) * head_dim + d;
+                long vdst = ((blk * num_kv_heads + h) * head_dim + d) * block_size + off;
+                k_cache[kdst] = k[src];
+                v_cache[vdst] = v[src];
+            }
+        }
+        ++written;
+    }
+    return written;
+}
+
+/*
+ * out[s][h][d] (double, [S][Hq][D]) = softmax over t < n of
+ * scale * q[s][h] . K_t, applied to V_t, with K_t, V_t read from the pools
+ * through block_tables (int32 [S][max_blocks]) and n = context_lens[s].
+ * n = 0 gives a zero row.  Returns 0, or -1 on a bad argument (including a
+ * context longer than the table or a table entry outside the pool).
+ */
+int oracle_paged_attention(double *out, const uint16_t *q,
+                           const uint16_t *k_cache, const uint16_t *v_cache,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads,
+                           int head_dim, int block_size, int max_blocks,
+                           long num_blocks, double scale, int num_threads)
+{
+    if (num_seqs < 0 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
+        head_dim < 1 || block_size < 1 || max_blocks < 1 || num_blocks < 1)
+        return -1;
+    for (int s = 0; s < num_seqs; ++s) {
+        int n = context_lens[s];
+        if (n < 0 || n > max_blocks * block_size)
+            return -1;
+        for (int b = 0; b < (n + block_size - 1) / block_size; ++b) {
+            int32_t phys = block_tables[(long)s * max_blocks + b];
+            if (phys < 0 || phys >= num_blocks)
+                return -1;
+        }
+    }
+    const int group = num_q_heads / num_kv_heads;
+    const long pairs = (long)num_seqs * num_q_heads;
+    int bad = 0;
+
+#ifdef _OPENMP
+    if (num_threads < 1)
+        num_threads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads) reduction(| : bad)
+#endif
+    for (long pair = 0; pair < pairs; ++pair) {
+        const int s = (int)(pair / num_q_heads);
+        const int h = (int)(pair % num_q_heads);
+        const int g = h / group;                      /* the K/V head this query head reads */
+        const int n = context_lens[s];
+        double *o = out + pair * head_dim;
+        for (int d = 0; d < head_dim; ++d)
+            o[d] = 0.0;
+        if (n == 0)
+            continue;
+
+        double *score = malloc(sizeof(double) * (size_t)n);
+        double *qv = malloc(sizeof(double) * (size_t)head_dim);
+        if (!score || !qv) {
+            free(score);
+            free(qv);
+            bad = 1;
+            continue;
+        }
+        for (int d = 0; d < head_dim; ++d)
+            qv[d] = bf16_value(q[pair * head_dim + d]);
+
+        /* S = scale * q K^T over the n cached positions, gathered through the table. */
+        for (int t = 0; t < n; ++t) {
+            long blk = block_tables[(long)s * max_blocks + t / block_size];
+            long off = t % block_size;
+            const uint16_t *krow = k_cache + ((blk * num_kv_heads + g) * block_size + off) * head_dim;
+            double dot = 0.0;
+            for (int d = 0; d < head_dim; ++d)
+                dot += qv[d] * bf16_value(krow[d]);
+            score[t] = scale * dot;
+        }
+
+        /* P = softmax(S): subtract the maximum, exponentiate, normalise. */
+        double m = score[0];
+        for (int t = 1; t < n; ++t)
+            if (score[t] > m)
+                m = score[t];
+        double l = 0.0;
+        for (int t = 0; t < n; ++t) {
+            score[t] = exp(score[t] - m);
+            l += score[t];
+        }
+
+        /* O = P V. */
+        for (int t = 0; t < n; ++t) {
+            long blk = block_tables[(long)s * max_blocks + t / block_size];
+            long off = t % block_size;
+            const uint16_t *vtile = v_cache + (blk * num_kv_heads + g) * (long)head_dim * block_size;
+            double p = score[t] / l;
+            for (int d = 0; d < head_dim; ++d)
+                o[d] += p * bf16_value(vtile[(long)d * block_size + off]);
+        }
+        free(score);
+        free(qv);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Number of OpenMP threads the library would use by default (1 without OpenMP). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,371 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` (the real build, or a build of a
+deliberately broken copy in the mutation test) and raises AssertionError when
+the oracle disagrees with:
+  * brute-force contiguous, unpaged attention on tiny inputs;
+  * ``torch.nn.functional.scaled_dot_product_attention`` (a library routine)
+    in float64 with grouped K/V heads;
+  * closed forms: one-token context, constant V, zero query (mean of V),
+    two-token logistic weights, one dominant key;
+  * invariances: physical block permutation, a constant shift of all scores,
+    thread count;
+  * the pages' worked paging example (300 tokens -> 19 blocks) and the GQA
+    grouping figure, stored under tests/golden/ with their citations;
+  * a hand-derived literal cache layout (tests/golden/cache_layout_tiny.json).
+
+Run as a script (``python tests/oracle_pins.py LIB``) it executes every pin
+against the oracle library LIB and prints one line per pin: the mutation test
+uses that so that a crashing broken oracle counts as detected.
+"""
+
+from __future__ import annotations
+
+import json
+import os
+import sys
+
+import numpy as np
+
+_ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if _ROOT not in sys.path:
+    sys.path.insert(0, _ROOT)
+
+import oracle as O  # noqa: E402
+from paged_kv_cache_tv_amd import workloads as W  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f64(bits):
+    return W.bf16_bits_to_float32(bits).astype(np.float64)
+
+
+def _run(orc, batch, num_threads=2):
+    return O.decode_step(orc, batch, num_threads)
+
+
+def _kv_of_head():
+    return np.asarray(_golden("attention_shape.json")["gqa_figure"]["kv_head_of_query_head"])
+
+
+def _contiguous_reference(batch):
+    """softmax(q K^T * scale) V on the unpaged sequences, plain numpy float64."""
+    kv_of = _kv_of_head() if batch.num_q_heads == 32 and batch.num_kv_heads == 8 else \
+        np.repeat(np.arange(batch.num_kv_heads), batch.num_q_heads // batch.num_kv_heads)
+    out = np.zeros((batch.num_seqs, batch.num_q_heads, batch.head_dim))
+    for s in range(batch.num_seqs):
+        n = int(batch.context_lens[s])
+        if n == 0:
+            continue
+        k, v = batch.logical_kv(s)
+        k, v = _f64(k), _f64(v)
+        q = _f64(batch.q[s])
+        for h in range(batch.num_q_heads):
+            g = kv_of[h]
+            sc = (k[:, g, :] @ q[h]) * batch.scale
+            w = np.exp(sc - sc.max())
+            out[s, h] = (w @ v[:, g, :]) / w.sum()
+    return out
+
+
+def _sdpa_reference(batch):
+    import torch
+    import torch.nn.functional as F
+    out = np.zeros((batch.num_seqs, batch.num_q_heads, batch.head_dim))
+    for s in range(batch.num_seqs):
+        n = int(batch.context_lens[s])
+        if n == 0:
+            continue
+        k, v = batch.logical_kv(s)
+        qt = torch.from_numpy(_f64(batch.q[s]))[None, :, None, :]            # [1, Hq, 1, D]
+        kt = torch.from_numpy(_f64(k)).permute(1, 0, 2)[None].contiguous()    # [1, Hkv, n, D]
+        vt = torch.from_numpy(_f64(v)).permute(1, 0, 2)[None].contiguous()
+        o = F.scaled_dot_product_attention(qt, kt, vt, enable_gqa=True)     # scale = 1/sqrt(D)
+        out[s] = o[0, :, 0, :].numpy()
+    return out
+
+
+# --------------------------------------------------------------------------- pins
+
+
+def pin_contiguous_bruteforce(orc):
+    """Paged oracle == unpaged brute force on tiny ragged batches."""
+    for seed, lens in ((11, [1, 17, 45, 64]), (12, [2, 16, 31, 33, 48, 5])):
+        b = W.make_batch(lens, seed)
+        out, _, _ = _run(orc, b)
+        ref = _contiguous_reference(b)
+        err = np.abs(out - ref).max()
+        assert err <= 1e-12, f"brute force mismatch {err}"
+
+
+def pin_torch_sdpa(orc):
+    """Paged oracle == torch SDPA (float64, grouped K/V heads) on the unpaged data."""
+    b = W.make_batch([3, 16, 33, 100], 13)
+    out, _, _ = _run(orc, b)
+    ref = _sdpa_reference(b)
+    err = np.abs(out - ref).max()
+    assert err <= 1e-12, f"SDPA mismatch {err}"
+
+
+def pin_block_permutation(orc):
+    """Moving physical blocks (and rewriting the tables) leaves the output bit-identical."""
+    b = W.make_batch([40, 77, 16, 129], 14)
+    out, kc, vc = _run(orc, b)
+    perm = np.random.default_rng(99).permutation(b.num_blocks)
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm] = kc
+    vc2[perm] = vc
+    bt2 = perm[b.block_tables].astype(np.int32)
+    out2 = orc.paged_attention(b.q, kc2, vc2, bt2, b.context_lens, b.scale, 2)
+    assert np.array_equal(out, out2), "output changed under block permutation"
+
+
+def pin_single_token(orc):
+    """A one-token context returns exactly that token's V (per the GQA figure's head map)."""
+    b = W.make_batch([1, 1, 1], 15)
+    out, _, _ = _run(orc, b)
+    kv_of = _kv_of_head()
+    for s in range(3):
+        _, v = b.logical_kv(s)
+        expect = _f64(v[0])[kv_of]                       # [Hq, D]
+        assert np.array_equal(out[s], expect), "n=1 must return V exactly"
+
+
+def _with_values(batch, k_fn=None, v_fn=None, q=None):
+    if k_fn is not None:
+        batch.kv_k = k_fn(batch.kv_k)
+    if v_fn is not None:
+        batch.kv_v = v_fn(batch.kv_v)
+    if q is not None:
+        batch.q = q
+    return batch
+
+
+def pin_constant_v(orc):
+    """V identically c gives c, whatever the scores."""
+    c = np.float32(0.75)
+    bits = W.round_to_bf16_bits(np.array([c]))[0]
+    b = _with_values(W.make_batch([5, 40, 300], 16), v_fn=lambda v: np.full_like(v, bits))
+    out, _, _ = _run(orc, b)
+    assert np.abs(out - 0.75).max() <= 1e-12, "constant V not reproduced"
+
+
+def pin_zero_query_mean(orc):
+    """q = 0 makes every score 0: the output is the plain mean of V over exactly n tokens.
+    Unused slots hold NaN, so reading one position too many shows as NaN."""
+    lens = [1, 15, 16, 17, 31, 33]
+    b = _with_values(W.make_batch(lens, 17), q=None)
+    b.q = np.zeros_like(b.q)
+    out, _, _ = _run(orc, b)
+    kv_of = _kv_of_head()
+    for s, n in enumerate(lens):
+        _, v = b.logical_kv(s)
+        mean = _f64(v).mean(axis=0)[kv_of]
+        assert np.isfinite(out[s]).all(), "stray read of a poisoned slot"
+        assert np.abs(out[s] - mean).max() <= 1e-12, f"mean of V over {n} tokens wrong"
+
+
+def pin_gqa_figure(orc):
+    """K/V head g filled with the constant (g+1)/2: query head h must return the
+    constant of the K/V head the GQA figure assigns to it; equal queries inside a
+    group give bit-equal outputs."""
+    b = W.make_batch([23, 50], 18)
+    consts = ((np.arange(8) + 1) * 0.5).astype(np.float32)
+    cbits = W.round_to_bf16_bits(consts)
+
+    def v_fn(v):
+        v = v.copy()
+        v[:] = cbits[None, :, None]
+        return v
+    b = _with_values(b, v_fn=v_fn)
+    q = b.q.copy()
+    for g in range(8):
+        q[:, 4 * g + 1:4 * g + 4] = q[:, 4 * g:4 * g + 1]
+    b.q = q
+    out, _, _ = _run(orc, b)
+    kv_of = _kv_of_head()
+    for h in range(32):
+        assert np.abs(out[:, h] - consts[kv_of[h]]).max() <= 1e-12, f"head {h} reads the wrong K/V head"
+    b2 = W.make_batch([23, 50], 18)
+    b2.q = q
+    out2, _, _ = _run(orc, b2)
+    for g in range(8):
+        for j in range(1, 4):
+            assert np.array_equal(out2[:, 4 * g], out2[:, 4 * g + j]), "equal queries in a group differ"
+
+
+def pin_one_dominant_key(orc):
+    """One key far more aligned with the query than the rest takes all the weight.
+    Its score (about 0.125 * 256 * |u|^2, i.e. ~2000) exceeds every other by far
+    more than exp() can span in double precision, so the softmax must also be
+    taken relative to the true maximum, not to an arbitrary score."""
+    b = W.make_batch([50], 19)
+    q = b.q.copy()
+    q[0, :] = q[0, 0:1]                                   # every head asks the same question
+    b.q = q
+    u = W.bf16_bits_to_float32(q[0, 0])
+    j = 29
+    k = b.kv_k.copy()
+    k[b.token_rows[0][j], :, :] = W.round_to_bf16_bits(256.0 * u)[None, :]  # exact: power-of-2 scale
+    b.kv_k = k
+    out, _, _ = _run(orc, b)
+    _, v = b.logical_kv(0)
+    expect = _f64(v[j])[_kv_of_head()]
+    assert np.abs(out[0] - expect).max() <= 1e-14, "dominant key must win"
+
+
+def pin_two_token_logistic(orc):
+    """Two tokens with scores s0, s1: weights are logistic(s0-s1) and logistic(s1-s0).
+    q = 2 e_0, K_0 = e_0, K_1 = -3 e_0 give s0 = 0.125*2*1 = 0.25 and s1 = -0.75."""
+    from scipy.special import expit
+    b = W.make_batch([2], 20)
+    q = np.zeros_like(b.q)
+    q[..., 0] = W.round_to_bf16_bits(np.array([2.0], np.float32))[0]
+    k = np.zeros_like(b.kv_k)
+    rows = b.token_rows[0]
+    k[rows[0], :, 0] = W.round_to_bf16_bits(np.array([1.0], np.float32))[0]
+    k[rows[1], :, 0] = W.round_to_bf16_bits(np.array([-3.0], np.float32))[0]
+    b.q, b.kv_k = q, k
+    out, _, _ = _run(orc, b)
+    _, v = b.logical_kv(0)
+    v = _f64(v)
+    w0, w1 = expit(1.0), expit(-1.0)
+    expect = (w0 * v[0] + w1 * v[1])[_kv_of_head()]
+    assert np.abs(out[0] - expect).max() <= 1e-12, "two-token weights wrong (scale or sign)"
+
+
+def pin_score_shift(orc):
+    """Adding the same amount (here 1024) to every score changes nothing: the
+    softmax must be computed relative to the largest score."""
+    b = W.make_batch([9, 70], 21)
+    one = W.round_to_bf16_bits(np.array([1.0], np.float32))[0]
+    k = b.kv_k.copy()
+    k[:, :, 0] = one
+    b.kv_k = k
+    q = b.q.copy()
+    q[..., 0] = 0
+    b.q = q
+    base, _, _ = _run(orc, b)
+    q2 = q.copy()
+    q2[..., 0] = W.round_to_bf16_bits(np.array([8192.0], np.float32))[0]   # +0.125*8192 = +1024
+    b.q = q2
+    shifted, _, _ = _run(orc, b)
+    assert np.isfinite(shifted).all(), "overflow: scores not taken relative to their maximum"
+    assert np.abs(shifted - base).max() <= 1e-12, "shift of all scores changed the output"
+
+
+def pin_paging_example(orc):
+    """The pages' worked example: 300 tokens occupy 19 blocks of 16 with 4 slots
+    free in the last one.  The oracle must read all 300 and nothing else."""
+    g = _golden("paging_examples.json")
+    bs, n = g["block_size"], g["on_demand"]["tokens"]
+    assert W.blocks_needed(n, bs) == g["on_demand"]["blocks"]
+    assert W.paged_waste(n, bs) == g["on_demand"]["free_slots_in_last_block"]
+    assert W.contiguous_waste(g["contiguous"]["max_length"], n) == g["contiguous"]["wasted_slots"]
+    b = W.make_batch([n], 22, table_width=g["on_demand"]["blocks"] + 5)
+    out, kc, vc = _run(orc, b)
+    assert np.isfinite(out).all(), "a poisoned slot or table entry was read"
+    assert np.abs(out - _contiguous_reference(b)).max() <= 1e-12
+    # The 300th token (offset 11 of the 19th block) is read ...
+    last_blk = b.block_tables[0, g["on_demand"]["blocks"] - 1]
+    kc2 = kc.copy()
+    kc2[last_blk, :, (n - 1) % bs, :] = W.round_to_bf16_bits(np.array([4.0], np.float32))[0]
+    out2 = orc.paged_attention(b.q, kc2, vc, b.block_tables, b.context_lens, b.scale, 2)
+    assert not np.array_equal(out, out2), "the last token was not read"
+    # ... and table entries past the 19th are not.
+    bt = b.block_tables.copy()
+    bt[0, g["on_demand"]["blocks"]:] = b.block_tables[0, 0]
+    out3 = orc.paged_attention(b.q, kc, vc, bt, b.context_lens, b.scale, 2)
+    assert np.array_equal(out, out3), "an unused table entry was read"
+
+
+def pin_cache_layout_literal(orc):
+    """Writes land exactly where the hand-derived literal pools say; padding and
+    out-of-pool slots are skipped."""
+    g = _golden("cache_layout_tiny.json")
+    nb, hkv, bs, d = g["num_blocks"], g["num_kv_heads"], g["block_size"], g["head_dim"]
+    kc, vc = O.Oracle.new_pools(nb, hkv, d, bs, fill=0)
+    k = np.array([t["k"] for t in g["tokens"]], np.uint16)
+    v = np.array([t["v"] for t in g["tokens"]], np.uint16)
+    slots = np.array([t["slot"] for t in g["tokens"]], np.int64)
+    written = orc.cache_write(k, v, kc, vc, slots)
+    assert written == g["written"]
+    assert kc.ravel().tolist() == g["expected_k_pool"], "K pool layout"
+    assert vc.ravel().tolist() == g["expected_v_pool"], "V pool layout"
+
+
+def pin_cache_write_untouched(orc):
+    """Only the named slots change; every other element keeps its (NaN) bits;
+    a repeated slot is refused."""
+    b = W.make_batch([20, 3, 47], 23)
+    kc, vc = O.Oracle.new_pools(b.num_blocks, 8, 64, 16)
+    k, v, slots = b.fill_inputs()
+    slots = slots.copy()
+    slots[0] = -1                                         # padding
+    slots[1] = b.num_blocks * 16                          # past the pool
+    written = orc.cache_write(k, v, kc, vc, slots)
+    assert written == len(slots) - 2
+    changed = (kc != W.BF16_NAN).sum() + (vc != W.BF16_NAN).sum()
+    expect_changed = ((k[2:] != W.BF16_NAN).sum() + (v[2:] != W.BF16_NAN).sum())
+    assert changed == expect_changed, "elements outside the written slots changed"
+    dup = np.array([5, 9, 5], np.int64)
+    kc2, vc2 = O.Oracle.new_pools(b.num_blocks, 8, 64, 16)
+    try:
+        orc.cache_write(k[:3], v[:3], kc2, vc2, dup)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("duplicate slot accepted")
+    assert (kc2 == W.BF16_NAN).all(), "refused write touched the pool"
+
+
+def pin_empty(orc):
+    """A sequence with no context yields zeros; an empty batch yields nothing."""
+    b = W.make_batch([0, 5, 0], 24)
+    out, _, _ = _run(orc, b)
+    assert (out[0] == 0).all() and (out[2] == 0).all()
+    assert np.abs(out[1] - _contiguous_reference(b)[1]).max() <= 1e-12
+    kc, vc = O.Oracle.new_pools(4, 8, 64, 16)
+    e = orc.paged_attention(np.zeros((0, 32, 64), np.uint16), kc, vc,
+                            np.zeros((0, 1), np.int32), np.zeros(0, np.int32), 0.125, 1)
+    assert e.shape == (0, 32, 64)
+
+
+def pin_thread_invariance(orc):
+    """Results do not depend on the number of threads."""
+    b = W.make_batch([33, 250, 64, 17, 100], 25)
+    kc, vc = O.build_pools(orc, b)
+    a = orc.paged_attention(b.q, kc, vc, b.block_tables, b.context_lens, b.scale, 1)
+    c = orc.paged_attention(b.q, kc, vc, b.block_tables, b.context_lens, b.scale, 4)
+    assert np.array_equal(a, c)
+
+
+ALL_PINS = [
+    pin_contiguous_bruteforce, pin_torch_sdpa, pin_block_permutation, pin_single_token,
+    pin_constant_v, pin_zero_query_mean, pin_gqa_figure, pin_one_dominant_key,
+    pin_two_token_logistic, pin_score_shift, pin_paging_example, pin_cache_layout_literal,
+    pin_cache_write_untouched, pin_empty, pin_thread_invariance,
+]
+
+
+def main(argv):
+    orc = O.Oracle(argv[1])
+    failed = 0
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+            print(f"PASS {pin.__name__}", flush=True)
+        except (AssertionError, ValueError) as e:
+            failed += 1
+            print(f"FAIL {pin.__name__}: {e}", flush=True)
+    return 1 if failed else 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv))

@@ -1,0 +1,80 @@
+"""Each plausible mistake planted in a copy of the oracle must fail at least one pin.
+
+The mistakes are planted by text substitution in a temporary copy of
+``oracle/oracle.c``, compiled with gcc, and the pins of ``oracle_pins.py`` run
+against that build in a child process (a crash counts as detected).  The real
+oracle source is never modified.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+PINS = os.path.join(ROOT, "tests", "oracle_pins.py")
+
+# (name, text in oracle.c, replacement)
+MUTANTS = [
+    ("gqa-modulo-mapping", "const int g = h / group;", "const int g = h % num_kv_heads;"),
+    ("gqa-wrong-group-size", "const int g = h / group;", "const int g = h / (group * 2);"),
+    ("scale-dropped", "score[t] = scale * dot;", "score[t] = dot;"),
+    ("scale-squared", "score[t] = scale * dot;", "score[t] = scale * scale * dot;"),
+    ("context-one-short", "const int n = context_lens[s];",
+     "const int n = context_lens[s] - (context_lens[s] > 1);"),
+    ("context-one-long", "const int n = context_lens[s];",
+     "const int n = context_lens[s] + (context_lens[s] % 16 != 0);"),
+    ("v-read-row-major", "vtile[(long)d * block_size + off]", "vtile[off * head_dim + d]"),
+    ("k-offset-dropped",
+     "const uint16_t *krow = k_cache + ((blk * num_kv_heads + g) * block_size + off) * head_dim;",
+     "const uint16_t *krow = k_cache + ((blk * num_kv_heads + g) * block_size) * head_dim;"),
+    ("softmax-sign", "score[t] = exp(score[t] - m);", "score[t] = exp(m - score[t]);"),
+    ("max-not-subtracted", "score[t] = exp(score[t] - m);", "score[t] = exp(score[t]);"),
+    ("not-normalised", "double p = score[t] / l;", "double p = score[t];"),
+    ("table-index-by-offset", "block_tables[(long)s * max_blocks + t / block_size]",
+     "block_tables[(long)s * max_blocks + t % block_size]"),
+    ("table-ignored", "long blk = block_tables[(long)s * max_blocks + t / block_size];",
+     "long blk = t / block_size;"),
+    ("query-of-group-leader", "qv[d] = bf16_value(q[pair * head_dim + d]);",
+     "qv[d] = bf16_value(q[(pair - h + g * group) * head_dim + d]);"),
+    ("dot-drops-last-dim", "for (int d = 0; d < head_dim; ++d)\n                dot +=",
+     "for (int d = 0; d < head_dim - 1; ++d)\n                dot +="),
+    ("max-is-first-score", "if (score[t] > m)\n                m = score[t];",
+     "if (0)\n                m = score[t];"),
+    ("write-v-row-major",
+     "long vdst = ((blk * num_kv_heads + h) * head_dim + d) * block_size + off;",
+     "long vdst = ((blk * num_kv_heads + h) * block_size + off) * head_dim + d;"),
+    ("write-offset-zero", "long off = (long)(slot % block_size);", "long off = 0;"),
+    ("write-head-swap",
+     "long kdst = ((blk * num_kv_heads + h) * block_size + off) * head_dim + d;",
+     "long kdst = ((blk * num_kv_heads + (num_kv_heads - 1 - h)) * block_size + off) * head_dim + d;"),
+    ("write-keeps-padding", "if (slot < 0 || slot >= num_slots)\n            continue;\n        long blk",
+     "if (slot >= num_slots)\n            continue;\n        if (slot < 0) slot = 0;\n        long blk"),
+    ("pv-uses-first-token", "o[d] += p * bf16_value(vtile[(long)d * block_size + off]);",
+     "o[d] += p * bf16_value(v_cache[(long)d * block_size]);"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, source, name, old, new):
+    assert old in source, f"mutation site for {name} not found in oracle.c"
+    mutated = source.replace(old, new)
+    src = tmp_path / "oracle_mutant.c"
+    src.write_text(mutated)
+    lib = tmp_path / "liboracle_mutant.so"
+    cc = shutil.which("gcc") or "cc"
+    subprocess.run([cc, "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", str(src), "-o",
+                    str(lib), "-lm"], check=True, capture_output=True)
+    r = subprocess.run([sys.executable, PINS, str(lib)], capture_output=True, text=True,
+                       timeout=300, cwd=ROOT)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout}"
+    assert "FAIL" in r.stdout or r.returncode < 0 or r.returncode > 1, r.stdout + r.stderr
