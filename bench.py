@@ -1,0 +1,228 @@
+"""Decode-step benchmark: paged GQA decode attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
+
+One step = the whole path for one attention layer of a decode step: cache
+write of the batch's new tokens (tv_cache_write), partition pass
+(tv_paged_attention_decode) and merge (tv_paged_attention_reduce).  The
+default workload is batch 64 with ragged contexts drawn from U[512, 4096]
+(32 query heads, 8 K/V heads, head_dim 64, bf16, 16-token blocks, 512-token
+partitions), built from a fixed seed.
+
+Timing: W untimed warm-up steps, then K timed steps.  Before every timed step
+an untimed 512 MiB write evicts the L2 and the 256 MB Infinity Cache, so the
+K/V bytes come from HBM ("cold" cache, the default); each step is bracketed by
+HIP events recorded on the stream the kernels run on, with one more event
+between each pair of kernels.  A back-to-back ("hot") figure is reported
+beside it.  Prints one JSON line.
+
+Throughput counts algorithmic bytes: K/V of every context token (2 x 8 heads x
+64 x 2 B = 2048 B per token), q (4 KiB per sequence), the block-table entries
+and context lengths read, the fp32 output (8 KiB per sequence) and the cache
+write's 2 x 2 KiB per new token.  The partition workspace is implementation
+overhead and is not counted.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged GQA decode attention: achieved HBM GB/s (% of peak) and seq-tokens/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+FLUSH_BYTES = 512 << 20
+
+
+def algorithmic_bytes(batch):
+    """(decode kernel bytes, whole-step bytes) for one step of ``batch``."""
+    S = batch.num_seqs
+    lens = batch.context_lens.astype(np.int64)
+    kv_row = 2 * batch.num_kv_heads * batch.head_dim * 2           # K+V bytes per token
+    blocks = (lens + batch.block_size - 1) // batch.block_size
+    decode = int(lens.sum()) * kv_row + S * batch.num_q_heads * batch.head_dim * 2 \
+        + int(blocks.sum()) * 4 + S * 4
+    reduce_out = S * batch.num_q_heads * batch.head_dim * 4
+    live = int((batch.new_slots >= 0).sum())
+    write = live * (2 * kv_row) + S * 8
+    return decode, decode + reduce_out + write
+
+
+def cpu_baseline(batch, target_seconds: float):
+    """Time the CPU oracle doing the same step (cache write + attention) on this host."""
+    import oracle as O
+    orc = O.default()
+    threads = O.cpu_count()
+    kc, vc = O.build_pools(orc, batch, include_step=False)
+    sk, sv, ss = batch.step_inputs()
+    times, out = [], None
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        orc.cache_write(sk, sv, kc, vc, ss)
+        out = orc.paged_attention(batch.q, kc, vc, batch.block_tables, batch.context_lens,
+                                  batch.scale, threads)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= target_seconds and len(times) >= 1:
+            break
+    return out, times, threads
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-flush", action="store_true", help="skip the cold-cache flush")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the decode step is "
+                                   "measured on one GPU's share (see DESIGN.md for sharding)",
+                          "n_gpus": args.gpus}), flush=True)
+        return 2
+
+    import torch
+    import paged_kv_cache_tv_amd as tv
+    from paged_kv_cache_tv_amd import workloads as W
+    from paged_kv_cache_tv_amd.step import DeviceBatch
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        return 1
+    tv.lib()                                   # loud failure if libtv.so is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.perf_counter()
+    batch = W.make_workload(args.workload)
+    db = DeviceBatch(batch, dev, partition_size=args.partition_size)
+    db.fill()
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    print(f"# workload {batch.name}: {batch.num_seqs} seqs, {batch.total_tokens} context tokens, "
+          f"setup {setup_s:.1f}s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    def flush(i):
+        if not args.no_flush:
+            flush_buf.fill_(i & 0xFF)
+
+    for i in range(args.warmup):
+        flush(i)
+        db.step(stream)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        flush(i)
+        e = ev[i]
+        e[0].record(stream)
+        db.write_step(stream)
+        e[1].record(stream)
+        db.decode(stream)
+        e[2].record(stream)
+        db.reduce(stream)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    write_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    decode_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    reduce_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+
+    # Hot cache: the same steps back to back, one event pair around all of them.
+    h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hot_steps = max(10, args.steps)
+    torch.cuda.synchronize()
+    h0.record(stream)
+    for _ in range(hot_steps):
+        db.step(stream)
+    h1.record(stream)
+    torch.cuda.synchronize()
+    hot_ms = h0.elapsed_time(h1) / hot_steps
+
+    out = db.out.cpu().numpy()
+    dec_bytes, step_bytes = algorithmic_bytes(batch)
+    ms = float(step_ms.mean())
+    value = step_bytes / (ms * 1e-3) / 1e9
+    dec_gbs = dec_bytes / (float(decode_ms.mean()) * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": batch.name,
+            "num_seqs": batch.num_seqs,
+            "context_tokens": batch.total_tokens,
+            "context_len_range": [int(batch.context_lens.min()), int(batch.context_lens.max())],
+            "num_q_heads": batch.num_q_heads, "num_kv_heads": batch.num_kv_heads,
+            "head_dim": batch.head_dim, "block_size": batch.block_size,
+            "partition_size": args.partition_size,
+            "cache": "hot" if args.no_flush else "cold",
+            "parallelism": "single GPU",
+        },
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seq_tokens_per_s": round(batch.total_tokens / (ms * 1e-3), 1),
+        "decode_tokens_per_s": round(batch.num_seqs / (ms * 1e-3), 1),
+        "step_bytes": step_bytes,
+        "kernels_us": {"cache_write": round(float(write_ms.mean()) * 1e3, 2),
+                       "paged_decode": round(float(decode_ms.mean()) * 1e3, 2),
+                       "paged_reduce": round(float(reduce_ms.mean()) * 1e3, 2)},
+        "step_us_min_median_max": [round(float(x) * 1e3, 2) for x in
+                                   (step_ms.min(), np.median(step_ms), step_ms.max())],
+        "hot_cache": {"ms_per_step": round(hot_ms, 5),
+                      "GB_per_s": round(step_bytes / (hot_ms * 1e-3) / 1e9, 2)},
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "roofline": {"bound": "hbm", "kernel": "paged_decode_kernel",
+                     "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": dec_bytes,
+                     "avg_launch_us": round(float(decode_ms.mean()) * 1e3, 2)},
+    }
+
+    if not args.no_cpu_baseline:
+        ref, times, threads = cpu_baseline(batch, args.cpu_seconds)
+        t = float(np.median(times))
+        result["cpu_baseline"] = {
+            "value": round(step_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the full step of {batch.name} (cache write of {batch.num_seqs} tokens + "
+                      f"attention over {batch.total_tokens} context tokens, fp64), repeated "
+                      f"{len(times)}x for {sum(times):.1f}s; median step {t:.3f}s",
+        }
+        err = np.abs(out.astype(np.float64) - ref)
+        result["parity"] = {"max_abs": float(err.max()), "mean_abs": float(err.mean())}
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

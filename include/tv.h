@@ -1,0 +1,191 @@
+/*
+ * tv.h -- C interface of libtv: the decode step of a paged KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Three calls make one decode step for one attention layer:
+ *   1. tv_cache_write            -- store each new token's K and V in the slot
+ *                                   the engine chose for it;
+ *   2. tv_paged_attention_decode -- grouped-query attention of each sequence's
+ *                                   newest query over its whole cached context,
+ *                                   one partial result per context partition;
+ *   3. tv_paged_attention_reduce -- merge the partial results into the output.
+ *
+ * Sources (the pages this library is built from):
+ *   - "vLLM" (blog.rlaisqls.com), section "가상 메모리 방식의 해결": the KV
+ *     cache is split into fixed-size blocks (16 tokens by default) and each
+ *     sequence keeps a table from logical positions to physical blocks, which
+ *     need not be contiguous; blocks may be shared between sequences.
+ *   - "Tiny-vLLM: 거대 LLM 추론, 작은 엔진이..." (trendpick100.com), second
+ *     Q&A: before the model runs, the engine supplies a slot_mapping telling
+ *     the KV store where each token's key/value vectors are written.
+ *   - "vLLM", section "Flash Attention": attention is S = Q K^T,
+ *     P = softmax(S), O = P V, and can be accumulated block by block with a
+ *     running maximum and a running sum (online softmax).
+ *   - "tiny-vllm 씹뜯맛즐 - (1)" (geonuchoi.com), section "2. Multi-Head
+ *     Attention 대신 GQA": consecutive query heads share one K/V head
+ *     (query heads 0-3 -> K/V head 0, 4-7 -> K/V head 1, ...).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers on the current HIP device, except where
+ *     stated.  bf16 values travel as raw 16-bit patterns (uint16_t).
+ *   - The caller allocates and owns every buffer, including the partition
+ *     workspace.  The library allocates nothing, frees nothing and keeps no
+ *     state between calls; it is safe to call from several host threads.
+ *   - Work is queued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without waiting for it.  Buffers must stay alive
+ *     until the stream has passed the call.
+ *   - Arguments are checked on the host before anything is launched; on any
+ *     error nothing is launched and nothing is written.
+ *   - Device data cannot raise errors; the kernels' behaviour on odd data is
+ *     defined per call below and never reads or writes outside the buffers.
+ *
+ * Cache layout (a pool of num_blocks physical blocks; K and V pools separate):
+ *   K pool: [num_blocks][num_kv_heads][block_size][head_dim]
+ *   V pool: [num_blocks][num_kv_heads][head_dim][block_size]
+ * i.e. one (block, K/V head) tile of K is block_size rows of head_dim values,
+ * and the matching V tile holds the same values dimension-major.  Token
+ * position t of a sequence lives in physical block block_table[t / block_size]
+ * at offset t % block_size; its slot number is block * block_size + offset.
+ */
+#ifndef TV_H
+#define TV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tv_status {
+    TV_OK = 0,
+    TV_ERR_NULL = 1,         /* a required pointer is NULL */
+    TV_ERR_SHAPE = 2,        /* sizes are negative, zero where they must not be, or inconsistent */
+    TV_ERR_UNSUPPORTED = 3,  /* valid shape that this build does not implement */
+    TV_ERR_HIP = 4,          /* the HIP runtime reported an error when launching */
+    TV_ERR_ALIGNMENT = 5     /* a pointer is not aligned as required */
+} tv_status;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *tv_status_string(tv_status status);
+
+/*
+ * Number of context partitions the decode call uses for contexts of up to
+ * max_context_len tokens: ceil(max_context_len / partition_size).  Returns 0
+ * for max_context_len <= 0 and -1 if partition_size <= 0.  (Host-only.)
+ */
+int32_t tv_num_partitions(int32_t max_context_len, int32_t partition_size);
+
+/*
+ * Cache write ("Tiny-vLLM" page, slot_mapping; "vLLM" page, blocks).
+ *
+ * For every token i < num_tokens with 0 <= slot_mapping[i] < num_blocks *
+ * block_size, with b = slot_mapping[i] / block_size, o = slot_mapping[i] %
+ * block_size, for every K/V head h and dimension d:
+ *     k_cache[b][h][o][d] = k[i][h][d]
+ *     v_cache[b][h][d][o] = v[i][h][d]
+ * Other tokens (negative slots mark padding; slots past the pool) are
+ * skipped.  Every other element of the pools keeps its bits.  The copy is
+ * bit-exact.
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim] bf16, 16-byte aligned
+ *   k_cache       K pool (layout above), 16-byte aligned
+ *   v_cache       V pool (layout above), 2-byte aligned
+ *   slot_mapping  int64 [num_tokens], 8-byte aligned
+ *   head_dim      multiple of 8
+ *
+ * Two tokens naming the same slot is a caller error: which one lands is not
+ * specified.  num_tokens == 0 is a no-op (pointers may then be NULL).
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE (negative count, non-positive sizes),
+ * TV_ERR_UNSUPPORTED (head_dim not a multiple of 8), TV_ERR_ALIGNMENT,
+ * TV_ERR_HIP.
+ */
+tv_status tv_cache_write(const uint16_t *k, const uint16_t *v,
+                         uint16_t *k_cache, uint16_t *v_cache,
+                         const int64_t *slot_mapping, int64_t num_tokens,
+                         int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, void *stream);
+
+/*
+ * Paged decode attention, partition pass ("vLLM" page: PagedAttention and
+ * Flash Attention's online softmax; "tiny-vllm" page: GQA grouping).
+ *
+ * For every sequence s with n = context_lens[s] cached tokens (the token just
+ * written included), every query head h (K/V head g = h / (num_q_heads /
+ * num_kv_heads)) and every partition p < ceil(n / partition_size) covering
+ * token positions [p * partition_size, min((p+1) * partition_size, n)):
+ *     part_max[s][h][p]    = max over the partition of scale * q[s][h] . K_t,
+ *                            in base-2 units (multiplied by log2(e))
+ *     part_sum[s][h][p]    = sum over the partition of 2^(score_t - part_max)
+ *     part_acc[s][h][p][:] = sum over the partition of 2^(score_t - part_max) * V_t
+ * (score_t in the same base-2 units).  Entries for p >= ceil(n /
+ * partition_size) are not written.  tv_paged_attention_reduce turns these
+ * into softmax(scale * q K^T) V.
+ *
+ *   part_acc      float [num_seqs][num_q_heads][P][head_dim], P = tv_num_partitions(max_context_len, partition_size)
+ *   part_max      float [num_seqs][num_q_heads][P]
+ *   part_sum      float [num_seqs][num_q_heads][P]
+ *   q             bf16  [num_seqs][num_q_heads][head_dim], 16-byte aligned
+ *   k_cache, v_cache  pools as above, 16-byte aligned
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; only the first
+ *                 ceil(n / block_size) entries of a row are read
+ *   context_lens  int32 [num_seqs]
+ *   max_context_len  host-side upper bound of context_lens (sizes the launch);
+ *                 must be <= max_blocks_per_seq * block_size
+ *   partition_size   tokens per partition, a positive multiple of block_size
+ *   scale         score factor (1/sqrt(head_dim) for standard attention), > 0
+ *
+ * Supported shapes: head_dim == 64, block_size == 16, 1 <= num_q_heads /
+ * num_kv_heads <= 16 (num_q_heads a multiple of num_kv_heads).
+ * Odd device data: a context length below 0 counts as 0 and one above
+ * max_context_len is cut to max_context_len; a table entry outside
+ * [0, num_blocks) drops that block's tokens from the softmax (a partition with
+ * no usable token gets part_max = -inf, part_sum = 0, part_acc = 0).
+ * Tokens at positions >= n are never read, so stale or NaN data there and in
+ * unused table entries cannot reach the result.
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED, TV_ERR_ALIGNMENT,
+ * TV_ERR_HIP.  num_seqs == 0 or max_context_len == 0 is a no-op.
+ */
+tv_status tv_paged_attention_decode(float *part_acc, float *part_max, float *part_sum,
+                                    const uint16_t *q,
+                                    const uint16_t *k_cache, const uint16_t *v_cache,
+                                    const int32_t *block_tables, const int32_t *context_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    int32_t max_blocks_per_seq, int64_t num_blocks,
+                                    int32_t max_context_len, int32_t partition_size,
+                                    float scale, void *stream);
+
+/*
+ * Log-sum-exp merge of the partitions ("vLLM" page, Flash Attention: the
+ * running maximum / running sum rule applied across partitions).
+ *
+ * For every sequence s and query head h, with P_s = ceil(n / partition_size)
+ * partitions (n = context_lens[s], cut to [0, max_context_len]):
+ *     M = max_p part_max[s][h][p],  w_p = 2^(part_max[s][h][p] - M)
+ *     out[s][h][:] = (sum_p w_p * part_acc[s][h][p][:]) / (sum_p w_p * part_sum[s][h][p])
+ * over p < P_s.  A sequence with n == 0 (or whose partitions hold no usable
+ * token) gets a zero row.
+ *
+ *   out           float [num_seqs][num_q_heads][head_dim], 16-byte aligned
+ *   part_*        as written by tv_paged_attention_decode with the same
+ *                 num_seqs, num_q_heads, head_dim, max_context_len and
+ *                 partition_size; part_acc 16-byte aligned
+ *   context_lens  int32 [num_seqs]
+ *
+ * Supported shapes: head_dim == 64.
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED, TV_ERR_ALIGNMENT,
+ * TV_ERR_HIP.  num_seqs == 0 is a no-op.  With max_context_len == 0 every row
+ * of out is set to zero.
+ */
+tv_status tv_paged_attention_reduce(float *out, const float *part_acc,
+                                    const float *part_max, const float *part_sum,
+                                    const int32_t *context_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t max_context_len, int32_t partition_size,
+                                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TV_H */

@@ -1,0 +1,14 @@
+"""MI355X-native paged GQA decode attention: libtv (HIP, gfx950) and its Python binding.
+
+The three steps of one decode step -- cache write, partitioned paged attention,
+log-sum-exp merge -- run in the HIP kernels of ``libtv.so``; this package only
+marshals torch tensors into the C calls declared in ``include/tv.h``.
+"""
+
+from .binding import (LIB_PATH, TvError, cache_write, lib, load_library, new_workspace,
+                      num_partitions, paged_attention, paged_attention_decode,
+                      paged_attention_reduce)
+
+__all__ = ["LIB_PATH", "TvError", "cache_write", "lib", "load_library", "new_workspace",
+           "num_partitions", "paged_attention", "paged_attention_decode",
+           "paged_attention_reduce"]

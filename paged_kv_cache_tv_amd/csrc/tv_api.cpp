@@ -1,0 +1,150 @@
+// C entry points of libtv: host-side argument checks, then one launch each on
+// the caller's stream.  Nothing is allocated and no state is kept.
+#include "../../include/tv.h"
+#include "tv_internal.h"
+
+#include <cmath>
+#include <cstdint>
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+tv_status from_hip(hipError_t e) { return e == hipSuccess ? TV_OK : TV_ERR_HIP; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char *tv_status_string(tv_status status)
+{
+    switch (status) {
+    case TV_OK: return "TV_OK";
+    case TV_ERR_NULL: return "TV_ERR_NULL: a required pointer is NULL";
+    case TV_ERR_SHAPE: return "TV_ERR_SHAPE: invalid or inconsistent sizes";
+    case TV_ERR_UNSUPPORTED: return "TV_ERR_UNSUPPORTED: shape not implemented";
+    case TV_ERR_HIP: return "TV_ERR_HIP: HIP runtime error";
+    case TV_ERR_ALIGNMENT: return "TV_ERR_ALIGNMENT: misaligned pointer";
+    }
+    return "unknown tv_status";
+}
+
+int32_t tv_num_partitions(int32_t max_context_len, int32_t partition_size)
+{
+    if (partition_size <= 0)
+        return -1;
+    if (max_context_len <= 0)
+        return 0;
+    return (int32_t)ceil_div(max_context_len, partition_size);
+}
+
+tv_status tv_cache_write(const uint16_t *k, const uint16_t *v, uint16_t *k_cache,
+                         uint16_t *v_cache, const int64_t *slot_mapping, int64_t num_tokens,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int64_t num_blocks, void *stream)
+{
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return TV_ERR_SHAPE;
+    if (num_tokens == 0)
+        return TV_OK;
+    if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+        return TV_ERR_NULL;
+    if (head_dim % 8 != 0)
+        return TV_ERR_UNSUPPORTED;
+    if (num_blocks > INT64_MAX / block_size)
+        return TV_ERR_SHAPE;
+    if ((int64_t)num_kv_heads * head_dim > (1 << 24))
+        return TV_ERR_UNSUPPORTED;
+    if (ceil_div(num_tokens, 4) > 0x7fffffff)
+        return TV_ERR_UNSUPPORTED;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 2) ||
+        !aligned(slot_mapping, 8))
+        return TV_ERR_ALIGNMENT;
+    tv::CacheWriteArgs a{k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
+                         head_dim, block_size, num_blocks * block_size};
+    return from_hip(tv::launch_cache_write(a, static_cast<hipStream_t>(stream)));
+}
+
+tv_status tv_paged_attention_decode(float *part_acc, float *part_max, float *part_sum,
+                                    const uint16_t *q, const uint16_t *k_cache,
+                                    const uint16_t *v_cache, const int32_t *block_tables,
+                                    const int32_t *context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t max_blocks_per_seq,
+                                    int64_t num_blocks, int32_t max_context_len,
+                                    int32_t partition_size, float scale, void *stream)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 ||
+        partition_size <= 0)
+        return TV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0 || partition_size % block_size != 0)
+        return TV_ERR_SHAPE;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+        return TV_ERR_SHAPE;
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return TV_ERR_SHAPE;
+    if (head_dim != tv::kHeadDim || block_size != tv::kBlockSize ||
+        num_q_heads / num_kv_heads > tv::kMaxGroup)
+        return TV_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || max_context_len == 0)
+        return TV_OK;
+    if (!part_acc || !part_max || !part_sum || !q || !k_cache || !v_cache || !block_tables ||
+        !context_lens)
+        return TV_ERR_NULL;
+    const int64_t parts = ceil_div(max_context_len, partition_size);
+    if ((int64_t)num_kv_heads * num_seqs * parts > 0x7fffffff)
+        return TV_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(part_acc, 4) ||
+        !aligned(part_max, 4) || !aligned(part_sum, 4))
+        return TV_ERR_ALIGNMENT;
+    tv::DecodeArgs a{};
+    a.part_acc = part_acc;
+    a.part_max = part_max;
+    a.part_sum = part_sum;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_parts = (int32_t)parts;
+    a.part_tiles = partition_size / block_size;
+    a.max_context_len = max_context_len;
+    a.num_blocks = num_blocks;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);   // log2(e)
+    return from_hip(tv::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+tv_status tv_paged_attention_reduce(float *out, const float *part_acc, const float *part_max,
+                                    const float *part_sum, const int32_t *context_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t max_context_len, int32_t partition_size, void *stream)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+        partition_size <= 0)
+        return TV_ERR_SHAPE;
+    if (head_dim != tv::kHeadDim)
+        return TV_ERR_UNSUPPORTED;
+    if (num_seqs == 0)
+        return TV_OK;
+    const int64_t parts = ceil_div(max_context_len, partition_size);
+    if (!out || !context_lens || (parts > 0 && (!part_acc || !part_max || !part_sum)))
+        return TV_ERR_NULL;
+    if ((int64_t)num_seqs * num_q_heads > 0x7fffffff)
+        return TV_ERR_UNSUPPORTED;
+    if (!aligned(out, 16) || !aligned(part_acc, 16) || !aligned(part_max, 4) ||
+        !aligned(part_sum, 4) || !aligned(context_lens, 4))
+        return TV_ERR_ALIGNMENT;
+    tv::ReduceArgs a{out, part_acc, part_max, part_sum, context_lens, num_seqs, num_q_heads,
+                     (int32_t)parts, partition_size, max_context_len};
+    return from_hip(tv::launch_paged_reduce(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal launch interface between the C entry points (tv_api.cpp) and the
+// kernels.  Argument checking happens in tv_api.cpp; the launchers assume
+// valid, checked arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tv {
+
+// Shapes served by the decode kernels.
+constexpr int kHeadDim = 64;
+constexpr int kBlockSize = 16;
+constexpr int kMaxGroup = 16;   // query heads per K/V head (MFMA N dimension)
+
+struct CacheWriteArgs {
+    const uint16_t *k;
+    const uint16_t *v;
+    uint16_t *k_cache;
+    uint16_t *v_cache;
+    const int64_t *slot_mapping;
+    int64_t num_tokens;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int64_t num_slots;          // num_blocks * block_size
+};
+
+struct DecodeArgs {
+    float *part_acc;
+    float *part_max;
+    float *part_sum;
+    const uint16_t *q;
+    const uint16_t *k_cache;
+    const uint16_t *v_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    int32_t num_seqs;
+    int32_t num_kv_heads;
+    int32_t group;              // query heads per K/V head
+    int32_t max_blocks;         // row stride of block_tables
+    int32_t num_parts;          // P: partitions per (sequence, head) in the workspace
+    int32_t part_tiles;         // partition_size / block_size
+    int32_t max_context_len;
+    int64_t num_blocks;
+    float scale_log2;           // scale * log2(e)
+};
+
+struct ReduceArgs {
+    float *out;
+    const float *part_acc;
+    const float *part_max;
+    const float *part_sum;
+    const int32_t *context_lens;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_parts;
+    int32_t partition_size;
+    int32_t max_context_len;
+};
+
+hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream);
+hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_paged_reduce(const ReduceArgs &a, hipStream_t stream);
+
+}  // namespace tv

@@ -1,0 +1,123 @@
+"""The C interface on the CPU: libtv loads, exports every function include/tv.h
+declares, and rejects bad arguments before launching anything.
+
+Every call here fails host-side validation: arguments that would pass are
+never given, so no kernel is launched (the pointers are not real device
+memory)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tv.h")
+
+TV_OK, TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED, TV_ERR_HIP, TV_ERR_ALIGNMENT = range(6)
+BAD = 0x11          # a non-NULL, misaligned pointer: if a check were missed, the alignment check
+                    # (last before launch) still refuses the call
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from paged_kv_cache_tv_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return binding.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(tv_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared()
+    for n in ("tv_cache_write", "tv_paged_attention_decode", "tv_paged_attention_reduce"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.tv_status_string(code)
+    assert b"unknown" in lib.tv_status_string(99)
+
+
+def test_num_partitions(lib):
+    assert lib.tv_num_partitions(4096, 512) == 8
+    assert lib.tv_num_partitions(4097, 512) == 9
+    assert lib.tv_num_partitions(1, 512) == 1
+    assert lib.tv_num_partitions(0, 512) == 0
+    assert lib.tv_num_partitions(100, 0) == -1
+
+
+def _cw(lib, T=4, hkv=8, d=64, bs=16, nb=8, ptrs=(BAD,) * 5):
+    return lib.tv_cache_write(*ptrs, T, hkv, d, bs, nb, None)
+
+
+def test_cache_write_validation(lib):
+    assert _cw(lib, T=-1) == TV_ERR_SHAPE
+    assert _cw(lib, hkv=0) == TV_ERR_SHAPE
+    assert _cw(lib, bs=0) == TV_ERR_SHAPE
+    assert _cw(lib, nb=0) == TV_ERR_SHAPE
+    assert _cw(lib, T=0, ptrs=(None,) * 5) == TV_OK          # no-op, nothing launched
+    assert _cw(lib, ptrs=(None, BAD, BAD, BAD, BAD)) == TV_ERR_NULL
+    assert _cw(lib, ptrs=(BAD, BAD, BAD, BAD, None)) == TV_ERR_NULL
+    assert _cw(lib, d=60) == TV_ERR_UNSUPPORTED
+    assert _cw(lib) == TV_ERR_ALIGNMENT
+
+
+def _dec(lib, S=2, hq=32, hkv=8, d=64, bs=16, mb=4, nb=8, mctx=64, part=32, scale=0.125,
+         ptrs=(BAD,) * 8):
+    return lib.tv_paged_attention_decode(*ptrs, S, hq, hkv, d, bs, mb, nb, mctx, part, scale, None)
+
+
+def test_decode_validation(lib):
+    assert _dec(lib, S=-1) == TV_ERR_SHAPE
+    assert _dec(lib, hq=30) == TV_ERR_SHAPE                  # not a multiple of hkv
+    assert _dec(lib, part=24) == TV_ERR_SHAPE                # not a multiple of the block size
+    assert _dec(lib, part=0) == TV_ERR_SHAPE
+    assert _dec(lib, mctx=65) == TV_ERR_SHAPE                # beyond max_blocks * block_size
+    assert _dec(lib, mctx=-1) == TV_ERR_SHAPE
+    assert _dec(lib, scale=0.0) == TV_ERR_SHAPE
+    assert _dec(lib, scale=float("nan")) == TV_ERR_SHAPE
+    assert _dec(lib, scale=float("inf")) == TV_ERR_SHAPE
+    assert _dec(lib, d=128) == TV_ERR_UNSUPPORTED
+    assert _dec(lib, bs=32, part=64, mctx=64) == TV_ERR_UNSUPPORTED
+    assert _dec(lib, hq=8 * 17) == TV_ERR_UNSUPPORTED       # group of 17
+    assert _dec(lib, S=0) == TV_OK
+    assert _dec(lib, mctx=0) == TV_OK
+    assert _dec(lib, ptrs=(BAD,) * 7 + (None,)) == TV_ERR_NULL
+    assert _dec(lib) == TV_ERR_ALIGNMENT
+
+
+def _red(lib, S=2, hq=32, d=64, mctx=64, part=32, ptrs=(BAD,) * 5):
+    return lib.tv_paged_attention_reduce(*ptrs, S, hq, d, mctx, part, None)
+
+
+def test_reduce_validation(lib):
+    assert _red(lib, S=-1) == TV_ERR_SHAPE
+    assert _red(lib, part=0) == TV_ERR_SHAPE
+    assert _red(lib, mctx=-3) == TV_ERR_SHAPE
+    assert _red(lib, d=32) == TV_ERR_UNSUPPORTED
+    assert _red(lib, S=0) == TV_OK
+    assert _red(lib, ptrs=(None,) + (BAD,) * 4) == TV_ERR_NULL
+    assert _red(lib, ptrs=(BAD, None, BAD, BAD, BAD)) == TV_ERR_NULL
+    assert _red(lib) == TV_ERR_ALIGNMENT
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    import paged_kv_cache_tv_amd as tv
+    x = torch.zeros((1, 8, 64), dtype=torch.int16)
+    with pytest.raises(ValueError):
+        tv.cache_write(x, x, torch.zeros((2, 8, 16, 64), dtype=torch.int16),
+                       torch.zeros((2, 8, 64, 16), dtype=torch.int16),
+                       torch.zeros(1, dtype=torch.int64))

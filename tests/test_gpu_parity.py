@@ -1,0 +1,252 @@
+"""GPU path (libtv through its C interface) against the CPU oracle.
+
+Bars:
+  * cache writes: the whole K and V pools bit-exact against the oracle's pools;
+  * attention output (fp32 accumulation from bf16 inputs): max-abs <= 1e-2 and
+    mean-abs <= 1e-3 (the contract), plus a tighter internal bar, max-abs <=
+    1e-4, that a dropped or extra token would break (the GPU keeps P to ~16
+    mantissa bits and accumulates in fp32; expected error ~1e-6).
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from paged_kv_cache_tv_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+CONTRACT_MAX, CONTRACT_MEAN, INTERNAL_MAX = 1e-2, 1e-3, 1e-4
+
+
+@pytest.fixture(scope="session")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import paged_kv_cache_tv_amd as tv
+    tv.lib()                          # fails loudly if libtv.so is missing
+    return torch.device("cuda:0")
+
+
+def _gpu_step(batch, dev, partition_size=None, max_context_len=None):
+    import torch
+    from paged_kv_cache_tv_amd.step import DeviceBatch
+    db = DeviceBatch(batch, dev, partition_size=partition_size, max_context_len=max_context_len)
+    db.fill()
+    out = db.step().clone()
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), db
+
+
+def _errors(got, ref):
+    d = np.abs(got.astype(np.float64) - ref)
+    return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
+
+
+def _assert_close(got, ref, what):
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    mx, mean = _errors(got, ref)
+    print(f"{what}: max_abs={mx:.3e} mean_abs={mean:.3e}", flush=True)
+    assert mx <= CONTRACT_MAX and mean <= CONTRACT_MEAN, f"{what}: contract broken"
+    assert mx <= INTERNAL_MAX, f"{what}: internal bar broken ({mx:.3e})"
+
+
+_oracle_cache = {}
+
+
+def _oracle_step(orc, key, batch):
+    if key not in _oracle_cache:
+        _oracle_cache.clear()
+        _oracle_cache[key] = O.decode_step(orc, batch)
+    return _oracle_cache[key]
+
+
+@pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
+def test_workload_parity(dev, oracle_lib, index):
+    """Full-size workloads: bit-exact pools after the step's writes, output within the bars."""
+    print(f"workload {index}: {W.WORKLOADS[index]}", flush=True)
+    batch = W.make_workload(index)
+    ref, kc_ref, vc_ref = _oracle_step(oracle_lib, ("workload", index), batch)
+    got, db = _gpu_step(batch, dev)
+    kc, vc = db.pools_numpy()
+    assert np.array_equal(kc, kc_ref), "K pool differs from the oracle's"
+    assert np.array_equal(vc, vc_ref), "V pool differs from the oracle's"
+    del kc, vc, kc_ref, vc_ref
+    _assert_close(got, ref, f"workload {index}")
+
+
+RAGGED = [1, 15, 16, 17, 200, 511, 512, 513, 1024, 1500, 3001, 4096]
+
+
+@pytest.mark.parametrize("partition_size", [16, 64, 512, 4096, 8192])
+def test_partition_invariance(dev, oracle_lib, partition_size):
+    """Same answer for any partition size (one partition when >= the longest context)."""
+    batch = W.make_batch(RAGGED, 31)
+    ref, _, _ = _oracle_step(oracle_lib, ("ragged", 31), batch)
+    got, _ = _gpu_step(batch, dev, partition_size=partition_size)
+    _assert_close(got, ref, f"partition {partition_size}")
+    base, _ = _gpu_step(batch, dev, partition_size=512)
+    assert np.abs(got - base).max() <= 1e-5
+
+
+def test_block_permutation_and_determinism(dev, oracle_lib):
+    """Moving physical blocks leaves the GPU result bit-identical; so does re-running."""
+    batch = W.make_batch([70, 513, 1111, 16], 32)
+    a, _ = _gpu_step(batch, dev)
+    b, _ = _gpu_step(batch, dev)
+    assert np.array_equal(a, b), "run-to-run difference"
+    perm = np.random.default_rng(5).permutation(batch.num_blocks).astype(np.int32)
+    batch.block_tables = perm[batch.block_tables]
+    batch.fill_slots = perm[batch.fill_slots // 16].astype(np.int64) * 16 + batch.fill_slots % 16
+    ok = batch.new_slots >= 0
+    batch.new_slots[ok] = perm[batch.new_slots[ok] // 16].astype(np.int64) * 16 + batch.new_slots[ok] % 16
+    batch.poison_block = int(perm[batch.poison_block])
+    c, _ = _gpu_step(batch, dev)
+    assert np.array_equal(a, c), "block permutation changed the GPU result"
+
+
+def test_edge_lengths(dev, oracle_lib):
+    """Empty, single-token, block-boundary and partition-boundary contexts."""
+    lens = [0, 1, 2, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1023, 1024, 1025, 0]
+    batch = W.make_batch(lens, 33)
+    ref, _, _ = O.decode_step(oracle_lib, batch)
+    got, _ = _gpu_step(batch, dev)
+    assert (got[0] == 0).all() and (got[-1] == 0).all(), "empty context must give zeros"
+    _assert_close(got, ref, "edge lengths")
+    one = [i for i, n in enumerate(lens) if n == 1][0]
+    _, v = batch.logical_kv(one)
+    expect = W.bf16_bits_to_float32(v[0])[np.repeat(np.arange(8), 4)]
+    assert np.array_equal(got[one], expect), "a one-token context must return that V exactly"
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (12, 4), (32, 4), (32, 2), (64, 4)])
+def test_group_sizes(dev, oracle_lib, hq, hkv):
+    """Query heads per K/V head from 1 to 16."""
+    batch = W.make_batch([37, 300, 1000], 34, num_q_heads=hq, num_kv_heads=hkv)
+    ref, _, _ = O.decode_step(oracle_lib, batch)
+    got, _ = _gpu_step(batch, dev)
+    _assert_close(got, ref, f"Hq={hq} Hkv={hkv}")
+
+
+def test_zero_query_is_mean_of_v(dev, oracle_lib):
+    """q = 0: every weight equal, output = mean of exactly n V rows (NaN poison beyond)."""
+    lens = [1, 15, 17, 530, 1029]
+    batch = W.make_batch(lens, 35)
+    batch.q = np.zeros_like(batch.q)
+    got, _ = _gpu_step(batch, dev)
+    for s, n in enumerate(lens):
+        _, v = batch.logical_kv(s)
+        mean = W.bf16_bits_to_float32(v).astype(np.float64).mean(axis=0)[np.repeat(np.arange(8), 4)]
+        assert np.isfinite(got[s]).all()
+        assert np.abs(got[s] - mean).max() <= 2e-6, f"mean over {n} tokens"
+
+
+def test_gqa_equal_queries_equal_outputs(dev):
+    batch = W.make_batch([45, 700], 36)
+    q = batch.q.copy()
+    for g in range(8):
+        q[:, 4 * g + 1:4 * g + 4] = q[:, 4 * g:4 * g + 1]
+    batch.q = q
+    got, _ = _gpu_step(batch, dev)
+    for g in range(8):
+        for j in range(1, 4):
+            assert np.array_equal(got[:, 4 * g], got[:, 4 * g + j])
+
+
+def test_score_shift_stability(dev, oracle_lib):
+    """All scores raised by 1024: the online maximum keeps the result finite and unchanged."""
+    batch = W.make_batch([90, 1300], 37)
+    one = W.round_to_bf16_bits(np.array([1.0], np.float32))[0]
+    batch.kv_k[:, :, 0] = one
+    batch.q[..., 0] = 0
+    base, _ = _gpu_step(batch, dev)
+    batch.q[..., 0] = W.round_to_bf16_bits(np.array([8192.0], np.float32))[0]
+    shifted, _ = _gpu_step(batch, dev)
+    assert np.isfinite(shifted).all()
+    # fp32 scores near 1024 carry ~1e-4 relative rounding: stability, not precision, is tested
+    assert np.abs(shifted - base).max() <= 5e-3
+
+
+def test_context_len_clamp_and_bad_table_entries(dev, oracle_lib):
+    """Device data the kernels define: n < 0 -> zeros; n > max_context_len is cut;
+    a table entry outside the pool drops that block (memory-safe) without
+    touching other sequences."""
+    import torch
+    from paged_kv_cache_tv_amd.step import DeviceBatch
+    batch = W.make_batch([100, 64, 300], 38)
+    ref, _, _ = O.decode_step(oracle_lib, batch)
+    db = DeviceBatch(batch, dev)
+    db.fill()
+    db.write_step()
+    # sequence 1: negative length -> zero row
+    cl = db.context_lens.clone()
+    db.context_lens[1] = -7
+    # sequence 2: an entry past the pool and one negative entry
+    db.block_tables[2, 3] = batch.num_blocks + 11
+    db.block_tables[2, 5] = -2
+    db.decode()
+    db.reduce()
+    got = db.out.cpu().numpy()
+    torch.cuda.synchronize()
+    assert (got[1] == 0).all()
+    assert np.isfinite(got[2]).all()
+    _assert_close(got[0:1], ref[0:1], "untouched sequence")
+    # n above max_context_len is cut to max_context_len (= 300 here): same as n = 300
+    db.context_lens.copy_(cl)
+    db.block_tables.copy_(torch.from_numpy(batch.block_tables).to(dev))
+    db.context_lens[2] = 100000
+    db.decode()
+    db.reduce()
+    got2 = db.out.cpu().numpy()
+    _assert_close(got2, ref, "clamped length")
+
+
+def test_cache_write_skips_padding_and_out_of_pool(dev, oracle_lib):
+    import torch
+    import paged_kv_cache_tv_amd as tv
+    batch = W.make_batch([40, 3], 39)
+    k, v, slots = batch.fill_inputs()
+    slots = slots.copy()
+    slots[0] = -1
+    slots[5] = batch.num_blocks * 16
+    slots[7] = batch.num_blocks * 16 + 12345
+    kc_ref, vc_ref = O.Oracle.new_pools(batch.num_blocks, 8, 64, 16)
+    oracle_lib.cache_write(k, v, kc_ref, vc_ref, slots)
+    kc = torch.full((batch.num_blocks, 8, 16, 64), W.BF16_NAN, dtype=torch.int16, device=dev)
+    vc = torch.full((batch.num_blocks, 8, 64, 16), W.BF16_NAN, dtype=torch.int16, device=dev)
+    kt = torch.from_numpy(k.view(np.int16)).to(dev)
+    vt = torch.from_numpy(v.view(np.int16)).to(dev)
+    tv.cache_write(kt, vt, kc, vc, torch.from_numpy(slots).to(dev))
+    assert np.array_equal(kc.cpu().numpy().view(np.uint16), kc_ref)
+    assert np.array_equal(vc.cpu().numpy().view(np.uint16), vc_ref)
+
+
+def test_errors_are_raised_before_launch(dev):
+    import torch
+    import paged_kv_cache_tv_amd as tv
+    q = torch.zeros((2, 32, 64), dtype=torch.int16, device=dev)
+    kc = torch.zeros((4, 8, 16, 64), dtype=torch.int16, device=dev)
+    vc = torch.zeros((4, 8, 64, 16), dtype=torch.int16, device=dev)
+    bt = torch.zeros((2, 4), dtype=torch.int32, device=dev)
+    cl = torch.ones(2, dtype=torch.int32, device=dev)
+    ws = tv.new_workspace(2, 32, 64, 64, 32, dev)
+    with pytest.raises(tv.TvError) as e:          # partition not a multiple of the block size
+        tv.paged_attention_decode(*tv.new_workspace(2, 32, 64, 64, 24, dev), q, kc, vc, bt, cl,
+                                  64, 24, 0.125)
+    assert e.value.status == 2
+    with pytest.raises(tv.TvError) as e:          # max_context_len beyond the table
+        tv.paged_attention_decode(*tv.new_workspace(2, 32, 64, 65, 32, dev), q, kc, vc, bt, cl,
+                                  65, 32, 0.125)
+    assert e.value.status == 2
+    with pytest.raises(tv.TvError) as e:          # scale must be > 0
+        tv.paged_attention_decode(*ws, q, kc, vc, bt, cl, 64, 32, -1.0)
+    assert e.value.status == 2
+    q48 = torch.zeros((2, 32, 48), dtype=torch.int16, device=dev)
+    kc48 = torch.zeros((4, 8, 16, 48), dtype=torch.int16, device=dev)
+    vc48 = torch.zeros((4, 8, 48, 16), dtype=torch.int16, device=dev)
+    with pytest.raises(tv.TvError) as e:          # head_dim 48 is not implemented
+        tv.paged_attention_decode(*tv.new_workspace(2, 32, 48, 64, 32, dev), q48, kc48, vc48,
+                                  bt, cl, 64, 32, 0.125)
+    assert e.value.status == 3
+    torch.cuda.synchronize()
