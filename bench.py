@@ -10,11 +10,15 @@ default workload is batch 64 with ragged contexts drawn from U[512, 4096]
 partitions), built from a fixed seed.
 
 Timing: W untimed warm-up steps, then K timed steps.  Before every timed step
-an untimed 512 MiB write evicts the L2 and the 256 MB Infinity Cache, so the
-K/V bytes come from HBM ("cold" cache, the default); each step is bracketed by
-HIP events recorded on the stream the kernels run on, with one more event
-between each pair of kernels.  A back-to-back ("hot") figure is reported
-beside it.  Prints one JSON line.
+a kernel reads 512 MiB of other memory, which evicts the L2 and the 256 MB
+Infinity Cache, so the K/V bytes come from HBM ("cold" cache, the default).
+The eviction reads rather than writes: a write leaves dirty lines whose
+write-back would then be charged to the step.  The K (eviction, step) pairs run
+back to back between two HIP events on the kernels' stream, and the same loop
+with the eviction alone is timed and subtracted, so no event sits between the
+kernels of a step.  Per-kernel times are taken the same way (eviction + that
+kernel, minus eviction).  A back-to-back ("hot") figure and one with an event
+around every kernel ("isolated") are reported beside it.  Prints one JSON line.
 
 Throughput counts algorithmic bytes: K/V of every context token (2 x 8 heads x
 64 x 2 B = 2048 B per token), q (4 KiB per sequence), the block-table entries
@@ -86,6 +90,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-flush", action="store_true", help="skip the cold-cache flush")
+    ap.add_argument("--lib", default=None, help="load libtv from this path instead of the package")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -102,6 +107,9 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}), flush=True)
         return 1
+    if args.lib:
+        from paged_kv_cache_tv_amd import binding
+        binding._lib = binding.load_library(args.lib)
     tv.lib()                                   # loud failure if libtv.so is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -116,21 +124,56 @@ def main(argv=None):
           f"setup {setup_s:.1f}s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
-    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush_buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
 
     def flush(i):
         if not args.no_flush:
-            flush_buf.fill_(i & 0xFF)
+            flush_buf.sum()
 
     for i in range(args.warmup):
         flush(i)
         db.step(stream)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    def timed_loop(body, k):
+        """Mean ms per iteration of `body`, run k times back to back between two
+        events recorded on the kernels' stream."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(k):
+            body(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    K = args.steps
+    # The timed region: K steps, each preceded by the cache eviction.  The
+    # eviction's own time (measured alone, same loop shape) is subtracted.
     wall0 = time.perf_counter()
-    for i in range(args.steps):
+    t_flush_step = timed_loop(lambda i: (flush(i), db.step(stream)), K)
+    wall = time.perf_counter() - wall0
+    t_flush = timed_loop(flush, K)
+    t_flush_write = timed_loop(lambda i: (flush(i), db.write_step(stream)), K)
+    t_flush_decode = timed_loop(lambda i: (flush(i), db.decode(stream)), K)
+    t_flush_reduce = timed_loop(lambda i: (flush(i), db.reduce(stream)), K)
+    if args.no_flush:
+        t_flush = 0.0
+    step_ms_cold = t_flush_step - t_flush
+    decode_ms = t_flush_decode - t_flush
+    write_ms = t_flush_write - t_flush
+    reduce_ms = t_flush_reduce - t_flush
+
+    # Hot cache: the same steps back to back with no eviction in between.
+    hot_steps = max(10, K)
+    hot_ms = timed_loop(lambda i: db.step(stream), hot_steps)
+    hot_decode_ms = timed_loop(lambda i: db.decode(stream), hot_steps)
+
+    # Isolated launches: events around every kernel of every step (adds the
+    # event/dispatch latency of each boundary; reported for reference).
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
         flush(i)
         e = ev[i]
         e[0].record(stream)
@@ -141,28 +184,14 @@ def main(argv=None):
         db.reduce(stream)
         e[3].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
-    write_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    decode_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    reduce_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
-
-    # Hot cache: the same steps back to back, one event pair around all of them.
-    h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    hot_steps = max(10, args.steps)
-    torch.cuda.synchronize()
-    h0.record(stream)
-    for _ in range(hot_steps):
-        db.step(stream)
-    h1.record(stream)
-    torch.cuda.synchronize()
-    hot_ms = h0.elapsed_time(h1) / hot_steps
+    iso_step = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    iso_decode = np.array([e[1].elapsed_time(e[2]) for e in ev])
 
     out = db.out.cpu().numpy()
     dec_bytes, step_bytes = algorithmic_bytes(batch)
-    ms = float(step_ms.mean())
+    ms = float(step_ms_cold)
     value = step_bytes / (ms * 1e-3) / 1e9
-    dec_gbs = dec_bytes / (float(decode_ms.mean()) * 1e-3) / 1e9
+    dec_gbs = dec_bytes / (decode_ms * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -192,19 +221,21 @@ def main(argv=None):
         "seq_tokens_per_s": round(batch.total_tokens / (ms * 1e-3), 1),
         "decode_tokens_per_s": round(batch.num_seqs / (ms * 1e-3), 1),
         "step_bytes": step_bytes,
-        "kernels_us": {"cache_write": round(float(write_ms.mean()) * 1e3, 2),
-                       "paged_decode": round(float(decode_ms.mean()) * 1e3, 2),
-                       "paged_reduce": round(float(reduce_ms.mean()) * 1e3, 2)},
-        "step_us_min_median_max": [round(float(x) * 1e3, 2) for x in
-                                   (step_ms.min(), np.median(step_ms), step_ms.max())],
+        "kernels_us": {"cache_write": round(write_ms * 1e3, 2),
+                       "paged_decode": round(decode_ms * 1e3, 2),
+                       "paged_reduce": round(reduce_ms * 1e3, 2)},
+        "eviction_us": round(t_flush * 1e3, 2),
         "hot_cache": {"ms_per_step": round(hot_ms, 5),
-                      "GB_per_s": round(step_bytes / (hot_ms * 1e-3) / 1e9, 2)},
-        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+                      "GB_per_s": round(step_bytes / (hot_ms * 1e-3) / 1e9, 2),
+                      "paged_decode_us": round(hot_decode_ms * 1e3, 2)},
+        "isolated_launch_us": {"step_median": round(float(np.median(iso_step)) * 1e3, 2),
+                               "paged_decode_median": round(float(np.median(iso_decode)) * 1e3, 2)},
+        "wall_ms_per_step_incl_eviction": round(wall / args.steps * 1e3, 4),
         "roofline": {"bound": "hbm", "kernel": "paged_decode_kernel",
                      "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": dec_bytes,
-                     "avg_launch_us": round(float(decode_ms.mean()) * 1e3, 2)},
+                     "avg_launch_us": round(decode_ms * 1e3, 2)},
     }
 
     if not args.no_cpu_baseline:

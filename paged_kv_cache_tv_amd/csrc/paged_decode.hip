@@ -10,26 +10,29 @@
 // triple is written for the merge kernel.
 //
 // Mapping to CDNA4:
-//   * One workgroup of 4 wavefronts per (sequence, K/V head, partition).  The
-//     launch index runs K/V head fastest, so the workgroups reading one
-//     physical block land on the same XCD (dispatch is round-robin over the
-//     8 XCDs) when several sequences share it.
-//   * Each wavefront takes every 4th 16-token block of the partition.  One
-//     block of one K/V head is a 2 KiB K tile [16 tokens][64] plus a 2 KiB V
-//     tile [64][16 tokens]; each lane loads 32 B of K and 4 x 8 B of V
-//     straight from HBM into registers, already in MFMA operand layout.
+//   * One wavefront (a 64-thread workgroup) per (sequence, K/V head,
+//     partition).  The launch index runs K/V head fastest, so the workgroups
+//     reading one physical block land on the same XCD (dispatch is round-robin
+//     over the 8 XCDs) when several sequences share it.
+//   * One block of one K/V head is a 2 KiB K tile [16 tokens][64] plus a 2 KiB
+//     V tile [64][16 tokens]; each lane loads 32 B of K and 4 x 8 B of V
+//     straight from HBM into registers, already in MFMA operand layout, at
+//     fixed per-lane offsets from a uniform tile base.  A ring of four tile
+//     buffers keeps three tiles (12 KiB) in flight while one is consumed.
 //   * Scores S^T[16 tokens][16 heads] = K . Q^T come from two
 //     v_mfma_f32_16x16x32_bf16 (K is the A operand, the group's queries the B
-//     operand; columns past the group size are zero).  Lane (g = lane/16,
-//     r = lane%16) then holds the scores of tokens 4g..4g+3 for query head r,
-//     which is exactly the B-operand layout of a 16x16x16 MFMA contracting over
-//     those 4 tokens -- so the probabilities never leave the lane.
+//     operand; columns past the group size are zero), so the K tile is read
+//     once for all query heads of the group.  Lane (g = lane/16, r = lane%16)
+//     then holds the scores of tokens 4g..4g+3 for query head r, which is
+//     exactly the B-operand layout of a 16x16x16 MFMA contracting over those 4
+//     tokens -- so the probabilities never leave the lane.
 //   * O^T[64 dims][16 heads] += V^T . P^T uses v_mfma_f32_16x16x16_bf16 four
 //     times (16 dims each).  P is split into bf16 hi + lo parts (two MFMAs)
 //     so the products keep ~16 bits of P's mantissa instead of 8.
 //   * exp is computed as 2^x (v_exp_f32) with scale*log2(e) folded into the
-//     scores; the running maximum is kept in those base-2 units.
-//   * The wavefronts' (max, sum, output) are merged through LDS at the end.
+//     scores; the running maximum is kept in those base-2 units.  The only
+//     cross-lane traffic is the max over the 4 lane groups (2 shuffles per
+//     tile) and one final sum; no LDS, no barrier.
 #include "tv_internal.h"
 
 #include <math.h>
@@ -44,23 +47,26 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = kHeadDim;
 constexpr int BS = kBlockSize;
-constexpr int kTileElems = BS * D;   // one (block, K/V head) tile: 1024 bf16
-constexpr int kWaves = 4;
+constexpr int kTileBytes = BS * D * 2;   // one (block, K/V head) tile: 1024 bf16
+constexpr int kRing = 4;                 // tiles in flight per wavefront
 
 struct Tile {
     bf16x8 k0, k1;       // K[token r][16g .. 16g+8), K[token r][16g+8 .. 16g+16)
     i16x4 v[4];          // V^T[16j + r][4g .. 4g+4), j = 0..3
 };
 
-__device__ __forceinline__ void load_tile(Tile &t, const uint16_t *kt, const uint16_t *vt,
-                                          int r, int g)
+// kt, vt: tile bases (uniform); koff = (r*64 + 16g)*2 and voff = (r*16 + 4g)*2
+// bytes are this lane's offsets, the same for every tile.
+// kt, vt: tile bases (uniform); koff = (r*64 + 16g)*2 and voff = (r*16 + 4g)*2
+// bytes are this lane's offsets, the same for every tile.
+__device__ __forceinline__ void load_tile(Tile &t, const char *kt, const char *vt, uint32_t koff,
+                                          uint32_t voff)
 {
-    const uint4 *kp = reinterpret_cast<const uint4 *>(kt + r * D + g * 16);
-    t.k0 = __builtin_bit_cast(bf16x8, kp[0]);
-    t.k1 = __builtin_bit_cast(bf16x8, kp[1]);
+    t.k0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(kt + koff));
+    t.k1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(kt + koff + 16));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        t.v[j] = __builtin_bit_cast(i16x4, *reinterpret_cast<const uint2 *>(vt + (16 * j + r) * BS + 4 * g));
+        t.v[j] = __builtin_bit_cast(i16x4, *reinterpret_cast<const uint2 *>(vt + voff + 512 * j));
 }
 
 // Fold one 16-token tile into the running (m, l, o) of this lane's query head.
@@ -132,7 +138,7 @@ __device__ __forceinline__ void attend_tile(const Tile &t, bf16x8 qb0, bf16x8 qb
     o[3] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v3, plo, o[3], 0, 0, 0);
 }
 
-__global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(DecodeArgs a)
+__global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
 {
     const int kvh = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
     const int rest = (int)(blockIdx.x / (unsigned)a.num_kv_heads);
@@ -147,8 +153,7 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(DecodeArgs a)
     const int ptok = min(n - first_tok, a.part_tiles * BS);    // tokens in this partition
     const int ntiles = (ptok + BS - 1) / BS;
 
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x;
     const int r = lane & 15;
     const int g = lane >> 4;
     const float c = a.scale_log2;
@@ -170,50 +175,54 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(DecodeArgs a)
         o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int32_t *bt = a.block_tables + (int64_t)s * a.max_blocks + (int64_t)part * a.part_tiles;
-    const int64_t tile_stride = (int64_t)a.num_kv_heads * kTileElems;
-    const uint16_t *kbase = a.k_cache + (int64_t)kvh * kTileElems;
-    const uint16_t *vbase = a.v_cache + (int64_t)kvh * kTileElems;
-    const int ntw = w < ntiles ? (ntiles - w + kWaves - 1) / kWaves : 0;   // tiles of this wave
+    const char *kpool = reinterpret_cast<const char *>(a.k_cache) + (int64_t)kvh * kTileBytes;
+    const char *vpool = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * kTileBytes;
+    const int64_t tile_stride = (int64_t)a.num_kv_heads * kTileBytes;
+    const uint32_t koff = (uint32_t)(r * D + g * 16) * 2u;        // this lane's K bytes in a tile
+    const uint32_t voff = (uint32_t)(r * BS + g * 4) * 2u;        // this lane's V^T bytes (j = 0)
 
-    for (int c0 = 0; c0 < ntw; c0 += 64) {
-        const int cn = min(64, ntw - c0);
-        // This wave's table entries for the chunk, one per lane.
-        const int32_t phys_lane = lane < cn ? bt[w + kWaves * (c0 + lane)] : 0;
+    auto issue = [&](Tile &t, int32_t b) {
+        const int64_t bb = (b >= 0 && b < a.num_blocks) ? (int64_t)b : 0;
+        load_tile(t, kpool + bb * tile_stride, vpool + bb * tile_stride, koff, voff);
+    };
+    auto consume = [&](const Tile &t, int tile, int32_t b) {
+        if (b < 0 || b >= a.num_blocks)
+            return;                                     // entry outside the pool: skipped
+        if ((tile + 1) * BS <= ptok)
+            attend_tile<false>(t, qb0, qb1, 4, c, m_run, l_run, o);
+        else
+            attend_tile<true>(t, qb0, qb1, ptok - tile * BS - 4 * g, c, m_run, l_run, o);
+    };
 
-        auto tile_block = [&](int k) -> int64_t {
-            const int32_t b = __builtin_amdgcn_readlane(phys_lane, k);
-            return (b >= 0 && b < a.num_blocks) ? (int64_t)b : -1;
+    // Tiles are streamed through a ring of kRing register buffers: while tile k
+    // is consumed, tiles k+1 .. k+kRing-1 are in flight.  Every steady-state
+    // iteration issues the same loads, so each wait leaves exactly
+    // (kRing-1) tiles outstanding.  Past the last tile the ring re-loads the
+    // last tile (an L2 hit) instead of branching around the loads.
+    for (int c0 = 0; c0 < ntiles; c0 += 64) {
+        const int cn = min(64, ntiles - c0);
+        const int32_t phys_lane = lane < cn ? bt[c0 + lane] : 0;   // one table entry per lane
+        auto block_of = [&](int k) -> int32_t {
+            return __builtin_amdgcn_readlane(phys_lane, min(k, cn - 1));
         };
-        auto issue = [&](Tile &t, int64_t b) {
-            const int64_t bb = b < 0 ? 0 : b;
-            load_tile(t, kbase + bb * tile_stride, vbase + bb * tile_stride, r, g);
-        };
-        auto consume = [&](const Tile &t, int k, int64_t b) {
-            if (b < 0)
-                return;                                     // entry outside the pool: skipped
-            const int it = w + kWaves * (c0 + k);           // tile index inside the partition
-            if ((it + 1) * BS <= ptok)
-                attend_tile<false>(t, qb0, qb1, 4, c, m_run, l_run, o);
-            else
-                attend_tile<true>(t, qb0, qb1, ptok - it * BS - 4 * g, c, m_run, l_run, o);
-        };
-
-        Tile ta, tb;
-        int64_t ba = tile_block(0), bb2 = -1;
-        issue(ta, ba);
-        for (int k = 0; k < cn; k += 2) {
-            if (k + 1 < cn) {
-                bb2 = tile_block(k + 1);
-                issue(tb, bb2);
+        Tile ring[kRing];
+#pragma unroll
+        for (int u = 0; u < kRing; ++u)
+            issue(ring[u], block_of(u));
+        const int nit = (cn + kRing - 1) / kRing;
+        for (int it = 0; it + 1 < nit; ++it) {
+#pragma unroll
+            for (int u = 0; u < kRing; ++u) {
+                const int k = it * kRing + u;
+                consume(ring[u], c0 + k, block_of(k));
+                issue(ring[u], block_of(k + kRing));
             }
-            consume(ta, k, ba);
-            if (k + 1 >= cn)
-                break;
-            if (k + 2 < cn) {
-                ba = tile_block(k + 2);
-                issue(ta, ba);
-            }
-            consume(tb, k + 1, bb2);
+        }
+#pragma unroll
+        for (int u = 0; u < kRing; ++u) {
+            const int k = (nit - 1) * kRing + u;
+            if (k < cn)
+                consume(ring[u], c0 + k, block_of(k));
         }
     }
 
@@ -221,42 +230,17 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(DecodeArgs a)
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
 
-    __shared__ float sm_m[kWaves][16];
-    __shared__ float sm_l[kWaves][16];
-    __shared__ float sm_o[kWaves][16][D];
-    if (g == 0) {
-        sm_m[w][r] = m_run;
-        sm_l[w][r] = l_run;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            sm_o[w][r][16 * j + 4 * g + i] = o[j][i];
-    __syncthreads();
-
-    const int hq = a.num_kv_heads * G;
-    for (int e = threadIdx.x; e < G * D; e += 64 * kWaves) {
-        const int hr = e / D;
-        const int d = e % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int x = 0; x < kWaves; ++x)
-            M = fmaxf(M, sm_m[x][hr]);
-        float num = 0.f, den = 0.f;
-#pragma unroll
-        for (int x = 0; x < kWaves; ++x) {
-            const float mx = sm_m[x][hr];
-            const float f = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - M);
-            num = fmaf(f, sm_o[x][hr][d], num);
-            den = fmaf(f, sm_l[x][hr], den);
+    if (r < G) {
+        const int hq = a.num_kv_heads * G;
+        const int64_t row = ((int64_t)s * hq + (int64_t)kvh * G + r) * a.num_parts + part;
+        if (g == 0) {
+            a.part_max[row] = m_run;
+            a.part_sum[row] = l_run;
         }
-        const int64_t row = ((int64_t)s * hq + (int64_t)kvh * G + hr) * a.num_parts + part;
-        a.part_acc[row * D + d] = num;
-        if (d == 0) {
-            a.part_max[row] = M;
-            a.part_sum[row] = den;
-        }
+        float *acc = a.part_acc + row * D + 4 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4 *>(acc + 16 * j) = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
     }
 }
 
@@ -265,7 +249,7 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(DecodeArgs a)
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream)
 {
     const int64_t groups = (int64_t)a.num_kv_heads * a.num_seqs * a.num_parts;
-    hipLaunchKernelGGL(paged_decode_kernel, dim3((unsigned)groups), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL(paged_decode_kernel, dim3((unsigned)groups), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 
