@@ -20,21 +20,26 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void cache_write_kernel(CacheW
     if (tok >= a.num_tokens)
         return;
     const int lane = threadIdx.x & 63;
+    const int row = a.num_kv_heads * a.head_dim;
+    const int chunks = row >> 3;
+    const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.k + tok * row);
+    const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.v + tok * row);
+    // The first chunk of each lane is loaded together with the slot number, so
+    // the common case (num_kv_heads * head_dim <= 512) waits on memory once.
+    const bool have0 = lane < chunks;
+    const uint4 k0 = have0 ? ksrc[lane] : make_uint4(0, 0, 0, 0);
+    const uint4 v0 = have0 ? vsrc[lane] : make_uint4(0, 0, 0, 0);
     const int64_t slot = a.slot_mapping[tok];
     if (slot < 0 || slot >= a.num_slots)
         return;
     const int64_t blk = slot / a.block_size;
     const int off = (int)(slot - blk * a.block_size);
-    const int row = a.num_kv_heads * a.head_dim;
-    const int chunks = row >> 3;
-    const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.k + tok * row);
-    const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.v + tok * row);
     for (int c = lane; c < chunks; c += 64) {
+        const uint4 kk = c == lane ? k0 : ksrc[c];
+        const uint4 vv = c == lane ? v0 : vsrc[c];
         const int h = (c << 3) / a.head_dim;
         const int d = (c << 3) - h * a.head_dim;
         const int64_t tile = blk * a.num_kv_heads + h;
-        const uint4 kk = ksrc[c];
-        const uint4 vv = vsrc[c];
         *reinterpret_cast<uint4 *>(a.k_cache + (tile * a.block_size + off) * a.head_dim + d) = kk;
         uint16_t *vdst = a.v_cache + (tile * a.head_dim + d) * a.block_size + off;
         const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};

@@ -2,11 +2,18 @@
 // Attention": the running maximum / running sum rule, applied across the
 // context partitions of one sequence and query head).
 //
-// One 256-thread workgroup per (sequence, query head).  Pass 1 finds the
-// largest partition maximum M; pass 2 sums the weights 2^(m_p - M) * l_p;
-// pass 3 has 16 partition lanes x 16 four-wide column lanes accumulate the
-// weighted partial outputs, merged through LDS in a fixed order (so the result
-// is bitwise reproducible run to run).
+// Short contexts (at most kMerge partitions): one wavefront per (sequence,
+// query head), four per workgroup.  Such a merge is latency-bound (a few
+// hundred bytes per wavefront), so it waits on memory only twice: the context
+// length, then -- issued together -- the partition maxima and sums (lane p
+// holds partition p) and the partition rows (lane d holds dimension d).
+//
+// Longer contexts: one 256-thread workgroup per (sequence, query head);
+// thread (group q = tid/16, column c = tid%16) accumulates the float4 column
+// c of partitions q, q+16, q+32, ..., eight rows in flight at a time, and the
+// 16 groups are summed through shuffles and LDS.
+//
+// Summation orders are fixed, so results are bitwise reproducible run to run.
 #include "tv_internal.h"
 
 #include <math.h>
@@ -15,7 +22,8 @@ namespace tv {
 namespace {
 
 constexpr int D = kHeadDim;
-constexpr int kThreads = 256;
+constexpr int kWavesPerGroup = 4;
+constexpr int kMerge = 8;          // partitions whose rows are loaded up front
 
 __device__ __forceinline__ float wave_max(float x)
 {
@@ -33,10 +41,74 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
-__global__ __launch_bounds__(kThreads) void paged_reduce_kernel(ReduceArgs a)
+// Lane j's float, broadcast (the lane-read builtin moves 32-bit integers).
+__device__ __forceinline__ float lane_value(float x, int j)
 {
-    const int sh = blockIdx.x;                     // s * num_q_heads + h
-    const int s = sh / a.num_q_heads;
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), j));
+}
+
+__global__ __launch_bounds__(64 * kWavesPerGroup) void paged_reduce_kernel(ReduceArgs a)
+{
+    const int64_t sh = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);   // s * Hq + h
+    if (sh >= (int64_t)a.num_seqs * a.num_q_heads)
+        return;
+    const int lane = threadIdx.x & 63;
+    const int s = (int)(sh / a.num_q_heads);
+
+    int n = a.context_lens[s];
+    n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
+    const int np = (n + a.partition_size - 1) / a.partition_size;
+    float *out = a.out + sh * D;
+
+    const float *pm = a.part_max + sh * a.num_parts;
+    const float *pl = a.part_sum + sh * a.num_parts;
+    const float *pa = a.part_acc + sh * a.num_parts * D;
+
+    // Issue everything the common case needs before using any of it.
+    float rows[kMerge];
+#pragma unroll
+    for (int j = 0; j < kMerge; ++j)
+        rows[j] = j < np ? pa[(int64_t)j * D + lane] : 0.f;
+    const float m_lane = lane < np ? pm[lane] : -INFINITY;
+    const float l_lane = lane < np ? pl[lane] : 0.f;
+
+    // Maximum over all partitions (lane p covers p, p + 64, ...).
+    float m_all = m_lane;
+    for (int p = 64 + lane; p < np; p += 64)
+        m_all = fmaxf(m_all, pm[p]);
+    const float M = wave_max(m_all);
+    if (M == -INFINITY) {                          // no partition / no usable token
+        out[lane] = 0.f;
+        return;
+    }
+
+    const float w_lane = m_lane == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_lane - M);
+    float den_part = w_lane * l_lane;
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMerge; ++j)
+        if (j < np)
+            acc = fmaf(lane_value(w_lane, j), rows[j], acc);
+    for (int j = kMerge; j < min(np, 64); ++j)
+        acc = fmaf(lane_value(w_lane, j), pa[(int64_t)j * D + lane], acc);
+
+    // Partitions beyond the first 64 (contexts longer than 64 partitions).
+    for (int p0 = 64; p0 < np; p0 += 64) {
+        const float mp = p0 + lane < np ? pm[p0 + lane] : -INFINITY;
+        const float wp = mp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mp - M);
+        den_part = fmaf(wp, p0 + lane < np ? pl[p0 + lane] : 0.f, den_part);
+        const int cnt = min(64, np - p0);
+        for (int j = 0; j < cnt; ++j)
+            acc = fmaf(lane_value(wp, j), pa[(int64_t)(p0 + j) * D + lane], acc);
+    }
+    const float den = wave_sum(den_part);
+    out[lane] = acc / den;
+}
+
+__global__ __launch_bounds__(256) void paged_reduce_wide_kernel(ReduceArgs a)
+{
+    const int64_t sh = blockIdx.x;                 // s * Hq + h
+    const int s = (int)(sh / a.num_q_heads);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
@@ -44,18 +116,16 @@ __global__ __launch_bounds__(kThreads) void paged_reduce_kernel(ReduceArgs a)
     int n = a.context_lens[s];
     n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
     const int np = (n + a.partition_size - 1) / a.partition_size;
-    float *out = a.out + (int64_t)sh * D;
+    float *out = a.out + sh * D;
+    const float *pm = a.part_max + sh * a.num_parts;
+    const float *pl = a.part_sum + sh * a.num_parts;
+    const float4 *pa = reinterpret_cast<const float4 *>(a.part_acc + sh * a.num_parts * D);
 
-    const float *pm = a.part_max + (int64_t)sh * a.num_parts;
-    const float *pl = a.part_sum + (int64_t)sh * a.num_parts;
-    const float *pa = a.part_acc + (int64_t)sh * a.num_parts * D;
+    __shared__ float red[4];
+    __shared__ float4 part4[4][16];
 
-    __shared__ float red[kThreads / 64];
-    __shared__ float4 acc_sm[16][16];
-
-    // Pass 1: M = max_p m_p.
     float m = -INFINITY;
-    for (int p = tid; p < np; p += kThreads)
+    for (int p = tid; p < np; p += 256)
         m = fmaxf(m, pm[p]);
     m = wave_max(m);
     if (lane == 0)
@@ -63,49 +133,66 @@ __global__ __launch_bounds__(kThreads) void paged_reduce_kernel(ReduceArgs a)
     __syncthreads();
     const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
-
-    if (M == -INFINITY) {                          // no partition / no usable token
+    if (M == -INFINITY) {
         if (tid < D)
             out[tid] = 0.f;
         return;
     }
 
-    // Pass 2: denominator.
     float den = 0.f;
-    for (int p = tid; p < np; p += kThreads)
-        den = fmaf(__builtin_amdgcn_exp2f(pm[p] - M), pl[p], den);
+    for (int p = tid; p < np; p += 256) {
+        const float mp = pm[p];
+        if (mp != -INFINITY)
+            den = fmaf(__builtin_amdgcn_exp2f(mp - M), pl[p], den);
+    }
     den = wave_sum(den);
     if (lane == 0)
         red[wv] = den;
-    __syncthreads();
-    const float DEN = (red[0] + red[1]) + (red[2] + red[3]);
 
-    // Pass 3: numerator, dims 4c..4c+3 for partitions pg, pg+16, ...
-    const int pg = tid >> 4;
-    const int cidx = tid & 15;
+    const int q = tid >> 4;
+    const int c = tid & 15;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int p = pg; p < np; p += 16) {
-        const float wgt = __builtin_amdgcn_exp2f(pm[p] - M);
-        const float4 x = reinterpret_cast<const float4 *>(pa + (int64_t)p * D)[cidx];
-        acc.x = fmaf(wgt, x.x, acc.x);
-        acc.y = fmaf(wgt, x.y, acc.y);
-        acc.z = fmaf(wgt, x.z, acc.z);
-        acc.w = fmaf(wgt, x.w, acc.w);
+    for (int p0 = q; p0 < np; p0 += 16 * 8) {
+        float4 x[8];
+        float w[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int p = p0 + 16 * u;
+            const bool live = p < np;
+            x[u] = live ? pa[(int64_t)p * 16 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float mp = live ? pm[p] : -INFINITY;
+            w[u] = mp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mp - M);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            acc.x = fmaf(w[u], x[u].x, acc.x);
+            acc.y = fmaf(w[u], x[u].y, acc.y);
+            acc.z = fmaf(w[u], x[u].z, acc.z);
+            acc.w = fmaf(w[u], x[u].w, acc.w);
+        }
     }
-    acc_sm[pg][cidx] = acc;
+    // Sum the four partition groups of this wavefront (lanes c, c+16, c+32, c+48).
+#pragma unroll
+    for (int mk = 16; mk <= 32; mk <<= 1) {
+        acc.x += __shfl_xor(acc.x, mk);
+        acc.y += __shfl_xor(acc.y, mk);
+        acc.z += __shfl_xor(acc.z, mk);
+        acc.w += __shfl_xor(acc.w, mk);
+    }
+    if (lane < 16)
+        part4[wv][lane] = acc;
     __syncthreads();
     if (tid < 16) {
-        float4 t = acc_sm[0][tid];
+        const float DEN = (red[0] + red[1]) + (red[2] + red[3]);
+        float4 t = part4[0][tid];
 #pragma unroll
-        for (int q = 1; q < 16; ++q) {
-            const float4 y = acc_sm[q][tid];
-            t.x += y.x;
-            t.y += y.y;
-            t.z += y.z;
-            t.w += y.w;
+        for (int x = 1; x < 4; ++x) {
+            t.x += part4[x][tid].x;
+            t.y += part4[x][tid].y;
+            t.z += part4[x][tid].z;
+            t.w += part4[x][tid].w;
         }
-        const float inv = 1.f / DEN;
-        reinterpret_cast<float4 *>(out)[tid] = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+        reinterpret_cast<float4 *>(out)[tid] = make_float4(t.x / DEN, t.y / DEN, t.z / DEN, t.w / DEN);
     }
 }
 
@@ -113,8 +200,15 @@ __global__ __launch_bounds__(kThreads) void paged_reduce_kernel(ReduceArgs a)
 
 hipError_t launch_paged_reduce(const ReduceArgs &a, hipStream_t stream)
 {
-    const int64_t groups = (int64_t)a.num_seqs * a.num_q_heads;
-    hipLaunchKernelGGL(paged_reduce_kernel, dim3((unsigned)groups), dim3(kThreads), 0, stream, a);
+    if (a.num_parts > kMerge) {
+        const int64_t groups = (int64_t)a.num_seqs * a.num_q_heads;
+        hipLaunchKernelGGL(paged_reduce_wide_kernel, dim3((unsigned)groups), dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
+    const int64_t waves = (int64_t)a.num_seqs * a.num_q_heads;
+    const int64_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+    hipLaunchKernelGGL(paged_reduce_kernel, dim3((unsigned)groups), dim3(64 * kWavesPerGroup), 0,
+                       stream, a);
     return hipGetLastError();
 }
 

@@ -250,3 +250,24 @@ def test_errors_are_raised_before_launch(dev):
                                   bt, cl, 64, 32, 0.125)
     assert e.value.status == 3
     torch.cuda.synchronize()
+
+
+def test_many_sequences_use_the_per_partition_pass(dev, oracle_lib):
+    """More sequences than the balanced plan holds: the per-partition pass serves them."""
+    rng = np.random.default_rng(40)
+    lens = rng.integers(0, 700, size=1100)
+    batch = W.make_batch(lens, 40)
+    ref, _, _ = O.decode_step(oracle_lib, batch)
+    got, _ = _gpu_step(batch, dev)
+    _assert_close(got, ref, "1100 sequences")
+
+
+def test_short_sequences_many_segments_per_range(dev, oracle_lib):
+    """Many one- and two-block sequences: each wavefront's range spans many
+    (sequence, head) segments, so passes are cut at the segment limit."""
+    rng = np.random.default_rng(41)
+    lens = rng.integers(1, 40, size=300)
+    batch = W.make_batch(lens, 41)
+    ref, _, _ = O.decode_step(oracle_lib, batch)
+    got, _ = _gpu_step(batch, dev)
+    _assert_close(got, ref, "300 short sequences")
