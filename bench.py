@@ -44,6 +44,29 @@ if ROOT not in sys.path:
 METRIC = "paged GQA decode attention: achieved HBM GB/s (% of peak) and seq-tokens/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 FLUSH_BYTES = 512 << 20
+COPY_CALIBRATION_BYTES = 1 << 30
+DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_tv_amd", "csrc", "paged_decode.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "paged_decode_traffic.json")
+
+
+def source_digest(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per decode launch from the committed counter record, or None when
+    there is no record for this workload or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != source_digest(DECODE_SOURCE):
+        return None
+    w = rec.get("workloads", {}).get(workload_name)
+    return None if w is None else w.get("hbm_bytes_per_launch")
 
 
 def algorithmic_bytes(batch):
@@ -91,11 +114,13 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-flush", action="store_true", help="skip the cold-cache flush")
     ap.add_argument("--lib", default=None, help="load libtv from this path instead of the package")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 plain device-to-device copies of 1 GiB (counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the decode step is "
-                                   "measured on one GPU's share (see DESIGN.md for sharding)",
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the decode step is "
+                                   "measured on one GPU's share and nothing here spans GPUs",
                           "n_gpus": args.gpus}), flush=True)
         return 2
 
@@ -113,6 +138,15 @@ def main(argv=None):
     tv.lib()                                   # loud failure if libtv.so is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": COPY_CALIBRATION_BYTES, "copies": 5}), flush=True)
+        return 0
 
     t0 = time.perf_counter()
     batch = W.make_workload(args.workload)
@@ -233,7 +267,8 @@ def main(argv=None):
         "wall_ms_per_step_incl_eviction": round(wall / args.steps * 1e3, 4),
         "roofline": {"bound": "hbm", "kernel": "paged_decode_kernel",
                      "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(batch.name),
                      "algorithmic_bytes_per_launch": dec_bytes,
                      "avg_launch_us": round(decode_ms * 1e3, 2)},
     }

@@ -120,7 +120,7 @@ def test_edge_lengths(dev, oracle_lib):
     assert np.array_equal(got[one], expect), "a one-token context must return that V exactly"
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (12, 4), (32, 4), (32, 2), (64, 4)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (12, 4), (32, 4), (32, 2), (4, 1), (64, 4)])
 def test_group_sizes(dev, oracle_lib, hq, hkv):
     """Query heads per K/V head from 1 to 16."""
     batch = W.make_batch([37, 300, 1000], 34, num_q_heads=hq, num_kv_heads=hkv)
