@@ -40,12 +40,14 @@
  *     defined per call below and never reads or writes outside the buffers.
  *
  * Cache layout (a pool of num_blocks physical blocks; K and V pools separate):
- *   K pool: [num_blocks][num_kv_heads][block_size][head_dim]
+ *   K pool: [num_blocks][num_kv_heads][head_dim / 8][block_size][8]
  *   V pool: [num_blocks][num_kv_heads][head_dim][block_size]
- * i.e. one (block, K/V head) tile of K is block_size rows of head_dim values,
- * and the matching V tile holds the same values dimension-major.  Token
- * position t of a sequence lives in physical block block_table[t / block_size]
- * at offset t % block_size; its slot number is block * block_size + offset.
+ * i.e. one (block, K/V head) tile of K is head_dim / 8 chunks, chunk c holding
+ * dimensions 8c..8c+7 of every token of the block (16 bytes per token), and
+ * the matching V tile holds its values dimension-major.  Both tiles are
+ * contiguous (block_size * head_dim values each).  Token position t of a
+ * sequence lives in physical block block_table[t / block_size] at offset
+ * t % block_size; its slot number is block * block_size + offset.
  */
 #ifndef TV_H
 #define TV_H
@@ -81,8 +83,8 @@ int32_t tv_num_partitions(int32_t max_context_len, int32_t partition_size);
  * For every token i < num_tokens with 0 <= slot_mapping[i] < num_blocks *
  * block_size, with b = slot_mapping[i] / block_size, o = slot_mapping[i] %
  * block_size, for every K/V head h and dimension d:
- *     k_cache[b][h][o][d] = k[i][h][d]
- *     v_cache[b][h][d][o] = v[i][h][d]
+ *     k_cache[b][h][d / 8][o][d % 8] = k[i][h][d]
+ *     v_cache[b][h][d][o]            = v[i][h][d]
  * Other tokens (negative slots mark padding; slots past the pool) are
  * skipped.  Every other element of the pools keeps its bits.  The copy is
  * bit-exact.

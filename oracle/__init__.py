@@ -5,7 +5,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``oracle.c`` with plain gcc, no fast-math) through ctypes and never touches the
 GPU library.
 
-Cache layout indexed by the oracle: K pool ``[NB][Hkv][BS][D]``, V pool
+Cache layout indexed by the oracle: K pool ``[NB][Hkv][D/8][BS][8]``, V pool
 ``[NB][Hkv][D][BS]``, bf16 as raw uint16.  Results are float64.
 
 Parity status of each function (pins live in ``tests/test_oracle.py`` and
@@ -69,8 +69,10 @@ class Oracle:
     @staticmethod
     def new_pools(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
                   fill: int = 0x7FC0):
-        """Fresh K and V pools in the oracle's layout, every element set to ``fill`` bits."""
-        k = np.full((num_blocks, num_kv_heads, block_size, head_dim), fill, np.uint16)
+        """Fresh K and V pools in the oracle's layout, every element set to ``fill`` bits.
+        K: [NB, Hkv, D/8, BS, 8]; V: [NB, Hkv, D, BS]."""
+        assert head_dim % 8 == 0
+        k = np.full((num_blocks, num_kv_heads, head_dim // 8, block_size, 8), fill, np.uint16)
         v = np.full((num_blocks, num_kv_heads, head_dim, block_size), fill, np.uint16)
         return k, v
 
@@ -82,8 +84,9 @@ class Oracle:
         sm = np.ascontiguousarray(slot_mapping, np.int64)
         assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
         assert k_cache.dtype == np.uint16 and v_cache.dtype == np.uint16
-        nb, hkv, bs, d = k_cache.shape
-        assert v_cache.shape == (nb, hkv, d, bs)
+        nb, hkv, dc, bs, x = k_cache.shape
+        d = dc * x
+        assert x == 8 and v_cache.shape == (nb, hkv, d, bs)
         T = sm.shape[0]
         assert k.shape == (T, hkv, d) and v.shape == (T, hkv, d)
         r = self.lib.oracle_cache_write(_ptr(k, _u16p), _ptr(v, _u16p), _ptr(k_cache, _u16p),
@@ -102,8 +105,8 @@ class Oracle:
         bt = np.ascontiguousarray(block_tables, np.int32)
         cl = np.ascontiguousarray(context_lens, np.int32)
         S, hq, d = q.shape
-        nb, hkv, bs, d2 = k_cache.shape
-        assert d2 == d and v_cache.shape == (nb, hkv, d, bs)
+        nb, hkv, dc, bs, x = k_cache.shape
+        assert x == 8 and dc * x == d and v_cache.shape == (nb, hkv, d, bs)
         assert bt.ndim == 2 and bt.shape[0] == S and cl.shape == (S,)
         out = np.zeros((S, hq, d), np.float64)
         threads = cpu_count() if num_threads is None else int(num_threads)

@@ -30,9 +30,11 @@
  *   head 1, ...; so query head h reads K/V head h / (Hq / Hkv).
  *
  * Cache layout (part of the library's interface, indexed here on its own):
- *   K pool: [NB][Hkv][BS][D]   (one block and head = BS rows of D values)
- *   V pool: [NB][Hkv][D][BS]   (the same tile stored dimension-major)
- *   bf16 values are raw uint16 bit patterns.
+ *   K pool: [NB][Hkv][D/8][BS][8]  (one block and head = D/8 chunks; chunk c
+ *                                   holds dimensions 8c..8c+7 of the BS tokens,
+ *                                   8 consecutive values per token)
+ *   V pool: [NB][Hkv][D][BS]       (one block and head stored dimension-major)
+ *   bf16 values are raw uint16 bit patterns; head_dim is a multiple of 8.
  *
  * Arithmetic: double precision from the exact bf16 values; the two-pass
  * softmax of the definition (max, then exponentials, then their sum); no
@@ -48,6 +50,15 @@
 #ifdef _OPENMP
 #include <omp.h>
 #endif
+
+#define KCHUNK 8    /* K pool: dimensions stored together per token (16 bytes) */
+
+/* Element (block blk, K/V head h, token offset off, dimension d) of the K pool. */
+static long k_index(long blk, int h, long off, int d, int num_kv_heads, int head_dim, int block_size)
+{
+    long tile = (blk * num_kv_heads + h) * (long)head_dim * block_size;
+    return tile + ((long)(d / KCHUNK) * block_size + off) * KCHUNK + d % KCHUNK;
+}
 
 static double bf16_value(uint16_t bits)
 {
@@ -69,7 +80,8 @@ long oracle_cache_write(const uint16_t *k, const uint16_t *v,
                         int num_kv_heads, int head_dim, int block_size,
                         long num_blocks)
 {
-    if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+    if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 1 || head_dim % KCHUNK != 0 ||
+        block_size < 1 || num_blocks < 1)
         return -1;
     long num_slots = num_blocks * (long)block_size;
     unsigned char *taken = calloc((size_t)num_slots, 1);
@@ -97,7 +109,7 @@ long oracle_cache_write(const uint16_t *k, const uint16_t *v,
         for (int h = 0; h < num_kv_heads; ++h) {
             for (int d = 0; d < head_dim; ++d) {
                 long src = ((long)i * num_kv_heads + h) * head_dim + d;
-                long kdst = ((blk * num_kv_heads + h) * block_size + off) * head_dim + d;
+                long kdst = k_index(blk, h, off, d, num_kv_heads, head_dim, block_size);
                 long vdst = ((blk * num_kv_heads + h) * head_dim + d) * block_size + off;
                 k_cache[kdst] = k[src];
                 v_cache[vdst] = v[src];
@@ -123,7 +135,8 @@ int oracle_paged_attention(double *out, const uint16_t *q,
                            long num_blocks, double scale, int num_threads)
 {
     if (num_seqs < 0 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
-        head_dim < 1 || block_size < 1 || max_blocks < 1 || num_blocks < 1)
+        head_dim < 1 || head_dim % KCHUNK != 0 || block_size < 1 || max_blocks < 1 ||
+        num_blocks < 1)
         return -1;
     for (int s = 0; s < num_seqs; ++s) {
         int n = context_lens[s];
@@ -170,10 +183,10 @@ int oracle_paged_attention(double *out, const uint16_t *q,
         for (int t = 0; t < n; ++t) {
             long blk = block_tables[(long)s * max_blocks + t / block_size];
             long off = t % block_size;
-            const uint16_t *krow = k_cache + ((blk * num_kv_heads + g) * block_size + off) * head_dim;
             double dot = 0.0;
             for (int d = 0; d < head_dim; ++d)
-                dot += qv[d] * bf16_value(krow[d]);
+                dot += qv[d] * bf16_value(k_cache[k_index(blk, g, off, d, num_kv_heads, head_dim,
+                                                          block_size)]);
             score[t] = scale * dot;
         }
 

@@ -94,18 +94,40 @@ def num_partitions(max_context_len: int, partition_size: int) -> int:
     return int(lib().tv_num_partitions(int(max_context_len), int(partition_size)))
 
 
+def _pool_dims(k_cache, v_cache):
+    """(NB, Hkv, BS, D) of a K pool [NB, Hkv, D/8, BS, 8] and V pool [NB, Hkv, D, BS]."""
+    _need(k_cache, "k_cache", itemsize=2, ndim=5)
+    _need(v_cache, "v_cache", itemsize=2, ndim=4)
+    nb, hkv, dc, bs, x = k_cache.shape
+    if x != 8:
+        raise ValueError("k_cache must be [NB, Hkv, D/8, BS, 8]")
+    d = dc * x
+    if tuple(v_cache.shape) != (nb, hkv, d, bs):
+        raise ValueError("v_cache must be [NB, Hkv, D, BS] matching k_cache [NB, Hkv, D/8, BS, 8]")
+    return nb, hkv, bs, d
+
+
+def new_pools(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int, device,
+              fill: int = 0):
+    """Allocate K and V pools (int16 bit patterns) in the library's layout."""
+    import torch
+    if head_dim % 8:
+        raise ValueError("head_dim must be a multiple of 8")
+    k = torch.full((num_blocks, num_kv_heads, head_dim // 8, block_size, 8), fill,
+                   dtype=torch.int16, device=device)
+    v = torch.full((num_blocks, num_kv_heads, head_dim, block_size), fill, dtype=torch.int16,
+                   device=device)
+    return k, v
+
+
 def cache_write(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
-    """tv_cache_write.  k, v: [T, Hkv, D]; k_cache: [NB, Hkv, BS, D]; v_cache:
+    """tv_cache_write.  k, v: [T, Hkv, D]; k_cache: [NB, Hkv, D/8, BS, 8]; v_cache:
     [NB, Hkv, D, BS]; slot_mapping: int64 [T]."""
     import torch
     for t, n in ((k, "k"), (v, "v")):
         _need(t, n, itemsize=2, ndim=3)
-    _need(k_cache, "k_cache", itemsize=2, ndim=4)
-    _need(v_cache, "v_cache", itemsize=2, ndim=4)
     _need(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1)
-    nb, hkv, bs, d = k_cache.shape
-    if tuple(v_cache.shape) != (nb, hkv, d, bs):
-        raise ValueError("v_cache must be [NB, Hkv, D, BS] matching k_cache [NB, Hkv, BS, D]")
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     T = slot_mapping.shape[0]
     if tuple(k.shape) != (T, hkv, d) or tuple(v.shape) != (T, hkv, d):
         raise ValueError("k and v must be [T, Hkv, D] with T = len(slot_mapping)")
@@ -122,15 +144,13 @@ def paged_attention_decode(part_acc, part_max, part_sum, q, k_cache, v_cache, bl
     context_lens: int32 [S]; part_acc: float32 [S, Hq, P, D]; part_max/part_sum: [S, Hq, P]."""
     import torch
     _need(q, "q", itemsize=2, ndim=3)
-    _need(k_cache, "k_cache", itemsize=2, ndim=4)
-    _need(v_cache, "v_cache", itemsize=2, ndim=4)
     _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
     _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
     for t, n in ((part_acc, "part_acc"), (part_max, "part_max"), (part_sum, "part_sum")):
         _need(t, n, dtype=torch.float32)
     S, hq, d = q.shape
-    nb, hkv, bs, d2 = k_cache.shape
-    if d2 != d or tuple(v_cache.shape) != (nb, hkv, d, bs):
+    nb, hkv, bs, d2 = _pool_dims(k_cache, v_cache)
+    if d2 != d:
         raise ValueError("cache shapes do not match q")
     P = num_partitions(max_context_len, partition_size)
     if tuple(part_acc.shape) != (S, hq, P, d) or tuple(part_max.shape) != (S, hq, P) or \

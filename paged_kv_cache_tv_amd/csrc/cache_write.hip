@@ -4,9 +4,10 @@
 //
 // One wavefront per token.  A token's K (or V) is num_kv_heads * head_dim bf16
 // values, contiguous in the input; lanes take 16-byte chunks (8 values of one
-// head, since head_dim % 8 == 0).  K chunks land contiguously in the token's
-// row of the K tile; V values go to 8 consecutive rows of the dimension-major
-// V tile, one 2-byte store each.
+// head, since head_dim % 8 == 0).  The K tile of a (block, head) is stored as
+// head_dim / 8 chunks of [block_size tokens][8 dims], so each K chunk is one
+// 16-byte store at (chunk, token offset); V values go to 8 consecutive rows of
+// the dimension-major V tile, one 2-byte store each.
 #include "tv_internal.h"
 
 namespace tv {
@@ -40,7 +41,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void cache_write_kernel(CacheW
         const int h = (c << 3) / a.head_dim;
         const int d = (c << 3) - h * a.head_dim;
         const int64_t tile = blk * a.num_kv_heads + h;
-        *reinterpret_cast<uint4 *>(a.k_cache + (tile * a.block_size + off) * a.head_dim + d) = kk;
+        *reinterpret_cast<uint4 *>(a.k_cache + tile * a.head_dim * a.block_size +
+                                   ((int64_t)(d >> 3) * a.block_size + off) * 8) = kk;
         uint16_t *vdst = a.v_cache + (tile * a.head_dim + d) * a.block_size + off;
         const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll

@@ -14,15 +14,19 @@
 //     partition).  The launch index runs K/V head fastest, so the workgroups
 //     reading one physical block land on the same XCD (dispatch is round-robin
 //     over the 8 XCDs) when several sequences share it.
-//   * One block of one K/V head is a 2 KiB K tile [16 tokens][64] plus a 2 KiB
-//     V tile [64][16 tokens]; each lane loads 32 B of K and 4 x 8 B of V
-//     straight from HBM into registers, already in MFMA operand layout, at
-//     fixed per-lane offsets from a uniform tile base.  A ring of four tile
-//     buffers keeps three tiles (12 KiB) in flight while one is consumed.
+//   * One block of one K/V head is a 2 KiB K tile, stored as 8 chunks of
+//     [16 tokens][8 dims], plus a 2 KiB V tile [64 dims][16 tokens].  Each
+//     K load instruction reads 1 KiB contiguous (lane l: bytes 16l..16l+15 of
+//     chunks 0-3, then of chunks 4-7) and each V load instruction 512 B
+//     contiguous, so every 128-byte line is fetched by exactly one
+//     instruction; the data arrives already in MFMA operand layout.  The
+//     loads are non-temporal: K/V lines are used once and should not push the
+//     partition results out of L2.  A ring of four tile buffers keeps three
+//     tiles (12 KiB) in flight while one is consumed.
 //   * Scores S^T[16 tokens][16 heads] = K . Q^T come from two
-//     v_mfma_f32_16x16x32_bf16 (K is the A operand, the group's queries the B
-//     operand; columns past the group size are zero), so the K tile is read
-//     once for all query heads of the group.  Lane (g = lane/16, r = lane%16)
+//     v_mfma_f32_16x16x32_bf16 over dims 0-31 and 32-63 (K is the A operand,
+//     the group's queries the B operand; columns past the group size are
+//     zero), so the K tile is read once for all query heads of the group.  Lane (g = lane/16, r = lane%16)
 //     then holds the scores of tokens 4g..4g+3 for query head r, which is
 //     exactly the B-operand layout of a 16x16x16 MFMA contracting over those 4
 //     tokens -- so the probabilities never leave the lane.
@@ -44,6 +48,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = kHeadDim;
 constexpr int BS = kBlockSize;
@@ -51,22 +57,23 @@ constexpr int kTileBytes = BS * D * 2;   // one (block, K/V head) tile: 1024 bf1
 constexpr int kRing = 4;                 // tiles in flight per wavefront
 
 struct Tile {
-    bf16x8 k0, k1;       // K[token r][16g .. 16g+8), K[token r][16g+8 .. 16g+16)
+    bf16x8 k0, k1;       // K[token r][8g .. 8g+8), K[token r][32+8g .. 32+8g+8)
     i16x4 v[4];          // V^T[16j + r][4g .. 4g+4), j = 0..3
 };
 
-// kt, vt: tile bases (uniform); koff = (r*64 + 16g)*2 and voff = (r*16 + 4g)*2
-// bytes are this lane's offsets, the same for every tile.
-// kt, vt: tile bases (uniform); koff = (r*64 + 16g)*2 and voff = (r*16 + 4g)*2
-// bytes are this lane's offsets, the same for every tile.
+// kt, vt: tile bases (uniform); koff = 16*lane and voff = (r*16 + 4g)*2 bytes
+// are this lane's offsets, the same for every tile.
 __device__ __forceinline__ void load_tile(Tile &t, const char *kt, const char *vt, uint32_t koff,
                                           uint32_t voff)
 {
-    t.k0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(kt + koff));
-    t.k1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(kt + koff + 16));
+    t.k0 = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+                                          reinterpret_cast<const u32x4 *>(kt + koff)));
+    t.k1 = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+                                          reinterpret_cast<const u32x4 *>(kt + 1024 + koff)));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        t.v[j] = __builtin_bit_cast(i16x4, *reinterpret_cast<const uint2 *>(vt + voff + 512 * j));
+        t.v[j] = __builtin_bit_cast(i16x4, __builtin_nontemporal_load(
+                                               reinterpret_cast<const u32x2 *>(vt + voff + 512 * j)));
 }
 
 // Fold one 16-token tile into the running (m, l, o) of this lane's query head.
@@ -159,13 +166,13 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
     const float c = a.scale_log2;
     const int G = a.group;
 
-    // B operand of the score MFMA: column r = query head kvh*G + r.
+    // B operands of the score MFMAs: column r = query head kvh*G + r, rows =
+    // dims 8g..8g+7 (first MFMA) and 32+8g..32+8g+7 (second).
     bf16x8 qb0 = {}, qb1 = {};
     if (r < G) {
-        const uint4 *qp = reinterpret_cast<const uint4 *>(
-            a.q + ((int64_t)s * a.num_kv_heads * G + (int64_t)kvh * G + r) * D + g * 16);
-        qb0 = __builtin_bit_cast(bf16x8, qp[0]);
-        qb1 = __builtin_bit_cast(bf16x8, qp[1]);
+        const uint16_t *qp = a.q + ((int64_t)s * a.num_kv_heads * G + (int64_t)kvh * G + r) * D + g * 8;
+        qb0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp));
+        qb1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 32));
     }
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -178,7 +185,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
     const char *kpool = reinterpret_cast<const char *>(a.k_cache) + (int64_t)kvh * kTileBytes;
     const char *vpool = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * kTileBytes;
     const int64_t tile_stride = (int64_t)a.num_kv_heads * kTileBytes;
-    const uint32_t koff = (uint32_t)(r * D + g * 16) * 2u;        // this lane's K bytes in a tile
+    const uint32_t koff = (uint32_t)lane * 16u;                   // this lane's K bytes in a tile
     const uint32_t voff = (uint32_t)(r * BS + g * 4) * 2u;        // this lane's V^T bytes (j = 0)
 
     auto issue = [&](Tile &t, int32_t b) {

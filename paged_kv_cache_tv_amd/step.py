@@ -40,10 +40,8 @@ class DeviceBatch:
         sk, sv, ss = b.step_inputs()
         self.step_k, self.step_v = _dev(sk, self.device), _dev(sv, self.device)
         self.step_slots = _dev(ss.astype(np.int64), self.device)
-        self.k_cache = torch.full((b.num_blocks, b.num_kv_heads, b.block_size, b.head_dim),
-                                  BF16_NAN, dtype=torch.int16, device=self.device)
-        self.v_cache = torch.full((b.num_blocks, b.num_kv_heads, b.head_dim, b.block_size),
-                                  BF16_NAN, dtype=torch.int16, device=self.device)
+        self.k_cache, self.v_cache = tv.new_pools(b.num_blocks, b.num_kv_heads, b.head_dim,
+                                                  b.block_size, self.device, fill=BF16_NAN)
         self.out = torch.empty((b.num_seqs, b.num_q_heads, b.head_dim), dtype=torch.float32,
                                device=self.device)
         self.workspace = tv.new_workspace(b.num_seqs, b.num_q_heads, b.head_dim,

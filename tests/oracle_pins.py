@@ -275,7 +275,7 @@ def pin_paging_example(orc):
     # The 300th token (offset 11 of the 19th block) is read ...
     last_blk = b.block_tables[0, g["on_demand"]["blocks"] - 1]
     kc2 = kc.copy()
-    kc2[last_blk, :, (n - 1) % bs, :] = W.round_to_bf16_bits(np.array([4.0], np.float32))[0]
+    kc2[last_blk, :, :, (n - 1) % bs, :] = W.round_to_bf16_bits(np.array([4.0], np.float32))[0]
     out2 = orc.paged_attention(b.q, kc2, vc, b.block_tables, b.context_lens, b.scale, 2)
     assert not np.array_equal(out, out2), "the last token was not read"
     # ... and table entries past the 19th are not.
@@ -296,8 +296,8 @@ def pin_cache_layout_literal(orc):
     slots = np.array([t["slot"] for t in g["tokens"]], np.int64)
     written = orc.cache_write(k, v, kc, vc, slots)
     assert written == g["written"]
-    assert kc.ravel().tolist() == g["expected_k_pool"], "K pool layout"
-    assert vc.ravel().tolist() == g["expected_v_pool"], "V pool layout"
+    assert kc.tolist() == g["expected_k_pool"], "K pool layout"
+    assert vc.tolist() == g["expected_v_pool"], "V pool layout"
 
 
 def pin_cache_write_untouched(orc):

@@ -118,6 +118,6 @@ def test_binding_refuses_host_tensors():
     import paged_kv_cache_tv_amd as tv
     x = torch.zeros((1, 8, 64), dtype=torch.int16)
     with pytest.raises(ValueError):
-        tv.cache_write(x, x, torch.zeros((2, 8, 16, 64), dtype=torch.int16),
+        tv.cache_write(x, x, torch.zeros((2, 8, 8, 16, 8), dtype=torch.int16),
                        torch.zeros((2, 8, 64, 16), dtype=torch.int16),
                        torch.zeros(1, dtype=torch.int64))

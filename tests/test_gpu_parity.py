@@ -213,8 +213,7 @@ def test_cache_write_skips_padding_and_out_of_pool(dev, oracle_lib):
     slots[7] = batch.num_blocks * 16 + 12345
     kc_ref, vc_ref = O.Oracle.new_pools(batch.num_blocks, 8, 64, 16)
     oracle_lib.cache_write(k, v, kc_ref, vc_ref, slots)
-    kc = torch.full((batch.num_blocks, 8, 16, 64), W.BF16_NAN, dtype=torch.int16, device=dev)
-    vc = torch.full((batch.num_blocks, 8, 64, 16), W.BF16_NAN, dtype=torch.int16, device=dev)
+    kc, vc = tv.new_pools(batch.num_blocks, 8, 64, 16, dev, fill=W.BF16_NAN)
     kt = torch.from_numpy(k.view(np.int16)).to(dev)
     vt = torch.from_numpy(v.view(np.int16)).to(dev)
     tv.cache_write(kt, vt, kc, vc, torch.from_numpy(slots).to(dev))
@@ -226,8 +225,7 @@ def test_errors_are_raised_before_launch(dev):
     import torch
     import paged_kv_cache_tv_amd as tv
     q = torch.zeros((2, 32, 64), dtype=torch.int16, device=dev)
-    kc = torch.zeros((4, 8, 16, 64), dtype=torch.int16, device=dev)
-    vc = torch.zeros((4, 8, 64, 16), dtype=torch.int16, device=dev)
+    kc, vc = tv.new_pools(4, 8, 64, 16, dev)
     bt = torch.zeros((2, 4), dtype=torch.int32, device=dev)
     cl = torch.ones(2, dtype=torch.int32, device=dev)
     ws = tv.new_workspace(2, 32, 64, 64, 32, dev)
@@ -243,8 +241,7 @@ def test_errors_are_raised_before_launch(dev):
         tv.paged_attention_decode(*ws, q, kc, vc, bt, cl, 64, 32, -1.0)
     assert e.value.status == 2
     q48 = torch.zeros((2, 32, 48), dtype=torch.int16, device=dev)
-    kc48 = torch.zeros((4, 8, 16, 48), dtype=torch.int16, device=dev)
-    vc48 = torch.zeros((4, 8, 48, 16), dtype=torch.int16, device=dev)
+    kc48, vc48 = tv.new_pools(4, 8, 48, 16, dev)
     with pytest.raises(tv.TvError) as e:          # head_dim 48 is not implemented
         tv.paged_attention_decode(*tv.new_workspace(2, 32, 48, 64, 32, dev), q48, kc48, vc48,
                                   bt, cl, 64, 32, 0.125)
@@ -252,8 +249,9 @@ def test_errors_are_raised_before_launch(dev):
     torch.cuda.synchronize()
 
 
-def test_many_sequences_use_the_per_partition_pass(dev, oracle_lib):
-    """More sequences than the balanced plan holds: the per-partition pass serves them."""
+def test_many_sequences(dev, oracle_lib):
+    """1100 sequences of 0..700 tokens: a grid far larger than the chip, with
+    empty contexts and many empty partitions mixed in."""
     rng = np.random.default_rng(40)
     lens = rng.integers(0, 700, size=1100)
     batch = W.make_batch(lens, 40)
@@ -262,9 +260,9 @@ def test_many_sequences_use_the_per_partition_pass(dev, oracle_lib):
     _assert_close(got, ref, "1100 sequences")
 
 
-def test_short_sequences_many_segments_per_range(dev, oracle_lib):
-    """Many one- and two-block sequences: each wavefront's range spans many
-    (sequence, head) segments, so passes are cut at the segment limit."""
+def test_short_sequences(dev, oracle_lib):
+    """300 sequences of 1..40 tokens: one to three blocks each, nearly every
+    tile a partial one."""
     rng = np.random.default_rng(41)
     lens = rng.integers(1, 40, size=300)
     batch = W.make_batch(lens, 41)

@@ -28,9 +28,13 @@ MUTANTS = [
     ("context-one-long", "const int n = context_lens[s];",
      "const int n = context_lens[s] + (context_lens[s] % 16 != 0);"),
     ("v-read-row-major", "vtile[(long)d * block_size + off]", "vtile[off * head_dim + d]"),
-    ("k-offset-dropped",
-     "const uint16_t *krow = k_cache + ((blk * num_kv_heads + g) * block_size + off) * head_dim;",
-     "const uint16_t *krow = k_cache + ((blk * num_kv_heads + g) * block_size) * head_dim;"),
+    ("k-offset-dropped", "((long)(d / KCHUNK) * block_size + off) * KCHUNK",
+     "((long)(d / KCHUNK) * block_size) * KCHUNK"),
+    ("k-token-major-layout", "((long)(d / KCHUNK) * block_size + off) * KCHUNK + d % KCHUNK",
+     "(off * (head_dim / KCHUNK) + d / KCHUNK) * KCHUNK + d % KCHUNK"),
+    ("k-chunk-dims-reversed", "* KCHUNK + d % KCHUNK;", "* KCHUNK + (KCHUNK - 1 - d % KCHUNK);"),
+    ("k-read-head-of-query", "dot += qv[d] * bf16_value(k_cache[k_index(blk, g, off, d,",
+     "dot += qv[d] * bf16_value(k_cache[k_index(blk, h % num_kv_heads, off, d,"),
     ("softmax-sign", "score[t] = exp(score[t] - m);", "score[t] = exp(m - score[t]);"),
     ("max-not-subtracted", "score[t] = exp(score[t] - m);", "score[t] = exp(score[t]);"),
     ("not-normalised", "double p = score[t] / l;", "double p = score[t];"),
@@ -49,8 +53,8 @@ MUTANTS = [
      "long vdst = ((blk * num_kv_heads + h) * block_size + off) * head_dim + d;"),
     ("write-offset-zero", "long off = (long)(slot % block_size);", "long off = 0;"),
     ("write-head-swap",
-     "long kdst = ((blk * num_kv_heads + h) * block_size + off) * head_dim + d;",
-     "long kdst = ((blk * num_kv_heads + (num_kv_heads - 1 - h)) * block_size + off) * head_dim + d;"),
+     "long kdst = k_index(blk, h, off, d, num_kv_heads, head_dim, block_size);",
+     "long kdst = k_index(blk, num_kv_heads - 1 - h, off, d, num_kv_heads, head_dim, block_size);"),
     ("write-keeps-padding", "if (slot < 0 || slot >= num_slots)\n            continue;\n        long blk",
      "if (slot >= num_slots)\n            continue;\n        if (slot < 0) slot = 0;\n        long blk"),
     ("pv-uses-first-token", "o[d] += p * bf16_value(vtile[(long)d * block_size + off]);",
