@@ -3,8 +3,11 @@
     python bench.py [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
 
 One step = the whole path for one attention layer of a decode step: cache
-write of the batch's new tokens (tv_cache_write), partition pass
-(tv_paged_attention_decode) and merge (tv_paged_attention_reduce).  The
+write of the batch's new tokens, partition pass and merge.  By default the
+step is two launches -- tv_paged_attention_decode_append (cache write folded
+into the partition pass) and tv_paged_attention_reduce; ``--step separate``
+times the three-launch form (tv_cache_write, tv_paged_attention_decode,
+tv_paged_attention_reduce), which is also reported alongside.  The
 default workload is batch 64 with ragged contexts drawn from U[512, 4096]
 (32 query heads, 8 K/V heads, head_dim 64, bf16, 16-token blocks, 512-token
 partitions), built from a fixed seed.
@@ -55,9 +58,10 @@ def source_digest(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload_name: str):
-    """HBM bytes per decode launch from the committed counter record, or None when
-    there is no record for this workload or the kernel source changed since."""
+def measured_traffic(workload_name: str, kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed counter record, or
+    None when there is no record for this kernel and workload or the kernel
+    source changed since."""
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
@@ -65,12 +69,15 @@ def measured_traffic(workload_name: str):
         return None
     if rec.get("kernel_source_sha256") != source_digest(DECODE_SOURCE):
         return None
+    if rec.get("kernel") != kernel:
+        return None
     w = rec.get("workloads", {}).get(workload_name)
     return None if w is None else w.get("hbm_bytes_per_launch")
 
 
 def algorithmic_bytes(batch):
-    """(decode kernel bytes, whole-step bytes) for one step of ``batch``."""
+    """(partition-pass bytes, whole-step bytes, new-token write bytes) for one
+    step of ``batch``."""
     S = batch.num_seqs
     lens = batch.context_lens.astype(np.int64)
     kv_row = 2 * batch.num_kv_heads * batch.head_dim * 2           # K+V bytes per token
@@ -80,7 +87,7 @@ def algorithmic_bytes(batch):
     reduce_out = S * batch.num_q_heads * batch.head_dim * 4
     live = int((batch.new_slots >= 0).sum())
     write = live * (2 * kv_row) + S * 8
-    return decode, decode + reduce_out + write
+    return decode, decode + reduce_out + write, write
 
 
 def cpu_baseline(batch, target_seconds: float):
@@ -110,6 +117,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--step", choices=["fused", "separate"], default="fused",
+                    help="two launches (write folded into the partition pass) or three")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-flush", action="store_true", help="skip the cold-cache flush")
@@ -164,9 +173,13 @@ def main(argv=None):
         if not args.no_flush:
             flush_buf.sum()
 
+    fused = args.step == "fused"
+    run_step = (lambda: db.fused_step(stream)) if fused else (lambda: db.step(stream))
+    other_step = (lambda: db.step(stream)) if fused else (lambda: db.fused_step(stream))
     for i in range(args.warmup):
         flush(i)
-        db.step(stream)
+        run_step()
+        other_step()
     torch.cuda.synchronize()
 
     def timed_loop(body, k):
@@ -185,47 +198,60 @@ def main(argv=None):
     # The timed region: K steps, each preceded by the cache eviction.  The
     # eviction's own time (measured alone, same loop shape) is subtracted.
     wall0 = time.perf_counter()
-    t_flush_step = timed_loop(lambda i: (flush(i), db.step(stream)), K)
+    t_flush_step = timed_loop(lambda i: (flush(i), run_step()), K)
     wall = time.perf_counter() - wall0
     t_flush = timed_loop(flush, K)
+    t_flush_other = timed_loop(lambda i: (flush(i), other_step()), K)
     t_flush_write = timed_loop(lambda i: (flush(i), db.write_step(stream)), K)
     t_flush_decode = timed_loop(lambda i: (flush(i), db.decode(stream)), K)
+    t_flush_append = timed_loop(lambda i: (flush(i), db.decode_append(stream)), K)
     t_flush_reduce = timed_loop(lambda i: (flush(i), db.reduce(stream)), K)
     if args.no_flush:
         t_flush = 0.0
     step_ms_cold = t_flush_step - t_flush
+    other_ms = t_flush_other - t_flush
     decode_ms = t_flush_decode - t_flush
+    append_ms = t_flush_append - t_flush
     write_ms = t_flush_write - t_flush
     reduce_ms = t_flush_reduce - t_flush
 
     # Hot cache: the same steps back to back with no eviction in between.
     hot_steps = max(10, K)
-    hot_ms = timed_loop(lambda i: db.step(stream), hot_steps)
-    hot_decode_ms = timed_loop(lambda i: db.decode(stream), hot_steps)
+    hot_ms = timed_loop(lambda i: run_step(), hot_steps)
+    hot_decode_ms = timed_loop(lambda i: (db.decode_append(stream) if fused else db.decode(stream)),
+                               hot_steps)
 
     # Isolated launches: events around every kernel of every step (adds the
     # event/dispatch latency of each boundary; reported for reference).
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    kernels = ([db.decode_append, db.reduce] if fused
+               else [db.write_step, db.decode, db.reduce])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
+          for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
         flush(i)
         e = ev[i]
         e[0].record(stream)
-        db.write_step(stream)
-        e[1].record(stream)
-        db.decode(stream)
-        e[2].record(stream)
-        db.reduce(stream)
-        e[3].record(stream)
+        for j, kern in enumerate(kernels):
+            kern(stream)
+            e[j + 1].record(stream)
     torch.cuda.synchronize()
-    iso_step = np.array([e[0].elapsed_time(e[3]) for e in ev])
-    iso_decode = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    main = 0 if fused else 1                      # the partition pass among the launches
+    iso_step = np.array([e[0].elapsed_time(e[-1]) for e in ev])
+    iso_decode = np.array([e[main].elapsed_time(e[main + 1]) for e in ev])
 
+    # The output of a final step in the timed form, checked against the oracle below.
+    run_step()
+    torch.cuda.synchronize()
     out = db.out.cpu().numpy()
-    dec_bytes, step_bytes = algorithmic_bytes(batch)
+    dec_bytes, step_bytes, write_bytes = algorithmic_bytes(batch)
     ms = float(step_ms_cold)
     value = step_bytes / (ms * 1e-3) / 1e9
-    dec_gbs = dec_bytes / (decode_ms * 1e-3) / 1e9
+    if fused:
+        roof_kernel, roof_bytes, roof_ms = "paged_decode_kernel<append>", dec_bytes + write_bytes, append_ms
+    else:
+        roof_kernel, roof_bytes, roof_ms = "paged_decode_kernel", dec_bytes, decode_ms
+    roof_gbs = roof_bytes / (roof_ms * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -255,8 +281,12 @@ def main(argv=None):
         "seq_tokens_per_s": round(batch.total_tokens / (ms * 1e-3), 1),
         "decode_tokens_per_s": round(batch.num_seqs / (ms * 1e-3), 1),
         "step_bytes": step_bytes,
+        "step": "two launches: decode_append + reduce" if fused else
+                "three launches: cache_write + decode + reduce",
+        "other_step_us": round(other_ms * 1e3, 2),
         "kernels_us": {"cache_write": round(write_ms * 1e3, 2),
                        "paged_decode": round(decode_ms * 1e3, 2),
+                       "paged_decode_append": round(append_ms * 1e3, 2),
                        "paged_reduce": round(reduce_ms * 1e3, 2)},
         "eviction_us": round(t_flush * 1e3, 2),
         "hot_cache": {"ms_per_step": round(hot_ms, 5),
@@ -265,12 +295,12 @@ def main(argv=None):
         "isolated_launch_us": {"step_median": round(float(np.median(iso_step)) * 1e3, 2),
                                "paged_decode_median": round(float(np.median(iso_decode)) * 1e3, 2)},
         "wall_ms_per_step_incl_eviction": round(wall / args.steps * 1e3, 4),
-        "roofline": {"bound": "hbm", "kernel": "paged_decode_kernel",
-                     "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(batch.name),
-                     "algorithmic_bytes_per_launch": dec_bytes,
-                     "avg_launch_us": round(decode_ms * 1e3, 2)},
+        "roofline": {"bound": "hbm", "kernel": roof_kernel,
+                     "achieved": round(roof_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(roof_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(batch.name, roof_kernel),
+                     "algorithmic_bytes_per_launch": roof_bytes,
+                     "avg_launch_us": round(roof_ms * 1e3, 2)},
     }
 
     if not args.no_cpu_baseline:

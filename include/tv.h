@@ -9,6 +9,8 @@
  *                                   newest query over its whole cached context,
  *                                   one partial result per context partition;
  *   3. tv_paged_attention_reduce -- merge the partial results into the output.
+ * tv_paged_attention_decode_append does steps 1 and 2 in one launch when each
+ * sequence brings one new token.
  *
  * Sources (the pages this library is built from):
  *   - "vLLM" (blog.rlaisqls.com), section "가상 메모리 방식의 해결": the KV
@@ -156,6 +158,44 @@ tv_status tv_paged_attention_decode(float *part_acc, float *part_max, float *par
                                     int32_t max_blocks_per_seq, int64_t num_blocks,
                                     int32_t max_context_len, int32_t partition_size,
                                     float scale, void *stream);
+
+/*
+ * Partition pass with the cache write folded in (the same two steps as
+ * tv_cache_write of one new token per sequence followed by
+ * tv_paged_attention_decode, in one launch).
+ *
+ * For every sequence s with n = context_lens[s] >= 1 (n counts the new token)
+ * and 0 <= slot_mapping[s] < num_blocks * block_size, the new token's K and V
+ * (k_new[s], v_new[s]: [num_kv_heads][head_dim] bf16) are written into that
+ * slot exactly as tv_cache_write writes token s; slot_mapping[s] < 0 (or
+ * n == 0) appends nothing for s.  The partials are then those of
+ * tv_paged_attention_decode over the pools after the writes.
+ *
+ * Precondition (the usual one for a decode step): slot_mapping[s] is negative
+ * or is the slot the block table gives for position n - 1 of sequence s, and
+ * no other sequence of the call reads that slot.  Then the result equals the
+ * two-call sequence bit for bit.  A slot elsewhere is still written, but
+ * position n - 1 is read from the pool, and a slot that another sequence of
+ * the same call reads gives unspecified values for that sequence.
+ *
+ *   k_new         bf16 [num_seqs][num_kv_heads][head_dim], 16-byte aligned
+ *   v_new         bf16 [num_seqs][num_kv_heads][head_dim], 2-byte aligned
+ *   slot_mapping  int64 [num_seqs], 8-byte aligned
+ *   other arguments as for tv_paged_attention_decode (the pools writable).
+ * Supported shapes and errors: as for tv_paged_attention_decode, plus
+ * TV_ERR_NULL for a NULL k_new, v_new or slot_mapping.
+ */
+tv_status tv_paged_attention_decode_append(float *part_acc, float *part_max, float *part_sum,
+                                           const uint16_t *q, const uint16_t *k_new,
+                                           const uint16_t *v_new, const int64_t *slot_mapping,
+                                           uint16_t *k_cache, uint16_t *v_cache,
+                                           const int32_t *block_tables,
+                                           const int32_t *context_lens,
+                                           int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t block_size, int32_t max_blocks_per_seq,
+                                           int64_t num_blocks, int32_t max_context_len,
+                                           int32_t partition_size, float scale, void *stream);
 
 /*
  * Log-sum-exp merge of the partitions ("vLLM" page, Flash Attention: the

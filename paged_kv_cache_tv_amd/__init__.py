@@ -7,8 +7,8 @@ marshals torch tensors into the C calls declared in ``include/tv.h``.
 
 from .binding import (LIB_PATH, TvError, cache_write, lib, load_library, new_pools,
                       new_workspace, num_partitions, paged_attention, paged_attention_decode,
-                      paged_attention_reduce)
+                      paged_attention_decode_append, paged_attention_reduce)
 
 __all__ = ["LIB_PATH", "TvError", "cache_write", "lib", "load_library", "new_pools",
            "new_workspace", "num_partitions", "paged_attention", "paged_attention_decode",
-           "paged_attention_reduce"]
+           "paged_attention_decode_append", "paged_attention_reduce"]

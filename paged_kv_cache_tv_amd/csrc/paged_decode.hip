@@ -145,6 +145,12 @@ __device__ __forceinline__ void attend_tile(const Tile &t, bf16x8 qb0, bf16x8 qb
     o[3] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v3, plo, o[3], 0, 0, 0);
 }
 
+// APPEND: sequence s also brings a new token (k_new, v_new) for slot
+// slot_mapping[s].  The workgroup holding the sequence's last partition writes
+// the token's K/V of its head into the pools, and -- when that slot is the one
+// the block table gives for position n-1 -- attends to the new values straight
+// from registers, so no other workgroup and no earlier kernel is involved.
+template <bool APPEND>
 __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
 {
     const int kvh = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
@@ -175,6 +181,21 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
         qb1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 32));
     }
 
+    // Append: the partition holding position n-1 stages the new token's K/V
+    // row of this head in LDS (after its first tile loads are out, so the
+    // stream is not delayed), replaces position n-1 with the staged row when
+    // the slot is that position's (the pool copy of that slot is never read
+    // back in this launch), and writes the row into the pools after its loop.
+    __shared__ uint16_t s_new[2 * D];     // K row then V row of the new token
+    const bool append_here = APPEND && first_tok + ptok == n;
+    int64_t wslot = -1;                   // slot to write (-1: none)
+    int32_t tblk = -1;                    // table entry of position n-1
+    if (append_here) {
+        wslot = a.slot_mapping[s];
+        tblk = a.block_tables[(int64_t)s * a.max_blocks + (n - 1) / BS];
+    }
+    int sub_off = -1;                     // token of the last tile replaced (-1: none)
+
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 o[4];
 #pragma unroll
@@ -195,6 +216,23 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
     auto consume = [&](const Tile &t, int tile, int32_t b) {
         if (b < 0 || b >= a.num_blocks)
             return;                                     // entry outside the pool: skipped
+        if (APPEND && sub_off >= 0 && tile == ntiles - 1) {
+            Tile u = t;                                 // position n-1 takes the new token
+            if (r == sub_off) {
+                u.k0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(s_new + 8 * g));
+                u.k1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(s_new + 32 + 8 * g));
+            }
+            if (g == (sub_off >> 2)) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (i == (sub_off & 3))
+                            u.v[j][i] = (short)s_new[D + 16 * j + r];
+            }
+            attend_tile<true>(u, qb0, qb1, ptok - tile * BS - 4 * g, c, m_run, l_run, o);
+            return;
+        }
         if ((tile + 1) * BS <= ptok)
             attend_tile<false>(t, qb0, qb1, 4, c, m_run, l_run, o);
         else
@@ -216,6 +254,20 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
 #pragma unroll
         for (int u = 0; u < kRing; ++u)
             issue(ring[u], block_of(u));
+        if (APPEND && c0 == 0 && append_here) {
+            if (wslot >= 0 && wslot < a.num_blocks * BS) {
+                // Lane l stages 4 bytes: K dims 2l, 2l+1 (l < 32) or V dims 2(l-32), 2(l-32)+1.
+                const uint16_t *row = (lane < 32 ? a.k_new : a.v_new) +
+                                      ((int64_t)s * a.num_kv_heads + kvh) * D + 2 * (lane & 31);
+                reinterpret_cast<uint32_t *>(s_new)[lane] = *reinterpret_cast<const uint32_t *>(row);
+                if ((int64_t)tblk * BS + (n - 1) % BS == wslot)
+                    sub_off = (n - 1) % BS;
+            } else {
+                wslot = -1;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);           // LDS stores done (lgkmcnt 0)
+            __builtin_amdgcn_wave_barrier();
+        }
         const int nit = (cn + kRing - 1) / kRing;
         for (int it = 0; it + 1 < nit; ++it) {
 #pragma unroll
@@ -231,6 +283,17 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
             if (k < cn)
                 consume(ring[u], c0 + k, block_of(k));
         }
+    }
+
+    if (APPEND && wslot >= 0) {           // the cache write of the new token, this head
+        const int64_t wblk = wslot / BS;
+        const int woff = (int)(wslot - wblk * BS);
+        uint16_t *kt = a.k_cache_w + (wblk * a.num_kv_heads + kvh) * (int64_t)(BS * D);
+        uint16_t *vt = a.v_cache_w + (wblk * a.num_kv_heads + kvh) * (int64_t)(BS * D);
+        if (lane < D / 8)                 // K: chunk `lane` (16 bytes)
+            *reinterpret_cast<uint4 *>(kt + (lane * BS + woff) * 8) =
+                *reinterpret_cast<const uint4 *>(s_new + 8 * lane);
+        vt[lane * BS + woff] = s_new[D + lane];   // V: dimension `lane`
     }
 
     // Sum the lane groups' partial l (same query head, different tokens).
@@ -256,7 +319,10 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream)
 {
     const int64_t groups = (int64_t)a.num_kv_heads * a.num_seqs * a.num_parts;
-    hipLaunchKernelGGL(paged_decode_kernel, dim3((unsigned)groups), dim3(64), 0, stream, a);
+    if (a.k_new)
+        hipLaunchKernelGGL(paged_decode_kernel<true>, dim3((unsigned)groups), dim3(64), 0, stream, a);
+    else
+        hipLaunchKernelGGL(paged_decode_kernel<false>, dim3((unsigned)groups), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -67,14 +67,17 @@ tv_status tv_cache_write(const uint16_t *k, const uint16_t *v, uint16_t *k_cache
     return from_hip(tv::launch_cache_write(a, static_cast<hipStream_t>(stream)));
 }
 
-tv_status tv_paged_attention_decode(float *part_acc, float *part_max, float *part_sum,
-                                    const uint16_t *q, const uint16_t *k_cache,
-                                    const uint16_t *v_cache, const int32_t *block_tables,
-                                    const int32_t *context_lens, int32_t num_seqs,
-                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                    int32_t block_size, int32_t max_blocks_per_seq,
-                                    int64_t num_blocks, int32_t max_context_len,
-                                    int32_t partition_size, float scale, void *stream)
+namespace {
+
+// Checks shared by both decode entry points; fills `a` on success.  Returns
+// TV_OK with a.num_parts == 0 when there is nothing to launch.
+tv_status check_decode(tv::DecodeArgs &a, float *part_acc, float *part_max, float *part_sum,
+                       const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                       const int32_t *block_tables, const int32_t *context_lens,
+                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                       int64_t num_blocks, int32_t max_context_len, int32_t partition_size,
+                       float scale)
 {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 ||
@@ -89,6 +92,7 @@ tv_status tv_paged_attention_decode(float *part_acc, float *part_max, float *par
     if (head_dim != tv::kHeadDim || block_size != tv::kBlockSize ||
         num_q_heads / num_kv_heads > tv::kMaxGroup)
         return TV_ERR_UNSUPPORTED;
+    a = tv::DecodeArgs{};
     if (num_seqs == 0 || max_context_len == 0)
         return TV_OK;
     if (!part_acc || !part_max || !part_sum || !q || !k_cache || !v_cache || !block_tables ||
@@ -101,7 +105,6 @@ tv_status tv_paged_attention_decode(float *part_acc, float *part_max, float *par
         !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(part_acc, 4) ||
         !aligned(part_max, 4) || !aligned(part_sum, 4))
         return TV_ERR_ALIGNMENT;
-    tv::DecodeArgs a{};
     a.part_acc = part_acc;
     a.part_max = part_max;
     a.part_sum = part_sum;
@@ -119,6 +122,60 @@ tv_status tv_paged_attention_decode(float *part_acc, float *part_max, float *par
     a.max_context_len = max_context_len;
     a.num_blocks = num_blocks;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);   // log2(e)
+    return TV_OK;
+}
+
+}  // namespace
+
+tv_status tv_paged_attention_decode(float *part_acc, float *part_max, float *part_sum,
+                                    const uint16_t *q, const uint16_t *k_cache,
+                                    const uint16_t *v_cache, const int32_t *block_tables,
+                                    const int32_t *context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t max_blocks_per_seq,
+                                    int64_t num_blocks, int32_t max_context_len,
+                                    int32_t partition_size, float scale, void *stream)
+{
+    tv::DecodeArgs a;
+    const tv_status st = check_decode(a, part_acc, part_max, part_sum, q, k_cache, v_cache,
+                                      block_tables, context_lens, num_seqs, num_q_heads,
+                                      num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                      num_blocks, max_context_len, partition_size, scale);
+    if (st != TV_OK || a.num_parts == 0)
+        return st;
+    return from_hip(tv::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+tv_status tv_paged_attention_decode_append(float *part_acc, float *part_max, float *part_sum,
+                                           const uint16_t *q, const uint16_t *k_new,
+                                           const uint16_t *v_new, const int64_t *slot_mapping,
+                                           uint16_t *k_cache, uint16_t *v_cache,
+                                           const int32_t *block_tables,
+                                           const int32_t *context_lens, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t max_blocks_per_seq, int64_t num_blocks,
+                                           int32_t max_context_len, int32_t partition_size,
+                                           float scale, void *stream)
+{
+    tv::DecodeArgs a;
+    const tv_status st = check_decode(a, part_acc, part_max, part_sum, q, k_cache, v_cache,
+                                      block_tables, context_lens, num_seqs, num_q_heads,
+                                      num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                      num_blocks, max_context_len, partition_size, scale);
+    if (st != TV_OK || a.num_parts == 0)
+        return st;
+    if (!k_new || !v_new || !slot_mapping)
+        return TV_ERR_NULL;
+    if (!aligned(k_new, 16) || !aligned(v_new, 2) || !aligned(slot_mapping, 8))
+        return TV_ERR_ALIGNMENT;
+    if (num_blocks > INT64_MAX / block_size)
+        return TV_ERR_SHAPE;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.slot_mapping = slot_mapping;
+    a.k_cache_w = k_cache;
+    a.v_cache_w = v_cache;
     return from_hip(tv::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -44,6 +44,13 @@ struct DecodeArgs {
     int32_t max_context_len;
     int64_t num_blocks;
     float scale_log2;           // scale * log2(e)
+    // Append (tv_paged_attention_decode_append): one new token per sequence,
+    // written into the pools before it is attended to.  k_new == nullptr: none.
+    const uint16_t *k_new;      // [num_seqs][num_kv_heads][head_dim]
+    const uint16_t *v_new;
+    const int64_t *slot_mapping;   // [num_seqs]
+    uint16_t *k_cache_w;        // the pools again, writable
+    uint16_t *v_cache_w;
 };
 
 struct ReduceArgs {

@@ -74,10 +74,26 @@ class DeviceBatch:
         tv.paged_attention_reduce(self.out, pa, pm, ps, self.context_lens, self.max_context_len,
                                   self.partition_size, stream)
 
+    def decode_append(self, stream=None) -> None:
+        """Cache write of the new tokens and partition pass in one launch."""
+        pa, pm, ps = self.workspace
+        tv.paged_attention_decode_append(pa, pm, ps, self.q, self.step_k, self.step_v,
+                                         self.step_slots, self.k_cache, self.v_cache,
+                                         self.block_tables, self.context_lens,
+                                         self.max_context_len, self.partition_size,
+                                         self.batch.scale, stream)
+
     def step(self, stream=None):
-        """Cache write of the new tokens, partition pass, merge.  Returns ``out``."""
+        """Cache write of the new tokens, partition pass, merge (three launches).
+        Returns ``out``."""
         self.write_step(stream)
         self.decode(stream)
+        self.reduce(stream)
+        return self.out
+
+    def fused_step(self, stream=None):
+        """The same step in two launches: write + partition pass, then merge."""
+        self.decode_append(stream)
         self.reduce(stream)
         return self.out
 

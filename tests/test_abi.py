@@ -35,7 +35,8 @@ def _declared():
 
 def test_header_declares_the_three_calls():
     names = _declared()
-    for n in ("tv_cache_write", "tv_paged_attention_decode", "tv_paged_attention_reduce"):
+    for n in ("tv_cache_write", "tv_paged_attention_decode", "tv_paged_attention_reduce",
+              "tv_paged_attention_decode_append"):
         assert n in names
 
 
@@ -96,6 +97,39 @@ def test_decode_validation(lib):
     assert _dec(lib, mctx=0) == TV_OK
     assert _dec(lib, ptrs=(BAD,) * 7 + (None,)) == TV_ERR_NULL
     assert _dec(lib) == TV_ERR_ALIGNMENT
+
+
+ALIGNED = 0x1000     # a non-NULL, aligned fake address: only ever paired with an argument
+                     # that fails validation, so nothing is launched
+
+
+def _app(lib, S=2, hq=32, hkv=8, d=64, bs=16, mb=4, nb=8, mctx=64, part=32, scale=0.125,
+         ptrs=(BAD,) * 11):
+    return lib.tv_paged_attention_decode_append(*ptrs, S, hq, hkv, d, bs, mb, nb, mctx, part,
+                                                scale, None)
+
+
+def test_decode_append_validation(lib):
+    assert _app(lib, S=-1) == TV_ERR_SHAPE
+    assert _app(lib, hq=30) == TV_ERR_SHAPE
+    assert _app(lib, part=24) == TV_ERR_SHAPE
+    assert _app(lib, mctx=65) == TV_ERR_SHAPE
+    assert _app(lib, scale=-1.0) == TV_ERR_SHAPE
+    assert _app(lib, d=128) == TV_ERR_UNSUPPORTED
+    assert _app(lib, S=0) == TV_OK
+    assert _app(lib, mctx=0) == TV_OK
+    assert _app(lib) == TV_ERR_ALIGNMENT
+    # The partition-pass arguments pass their checks; the append ones do not.
+    for i in (4, 5, 6):                                   # k_new, v_new, slot_mapping
+        ptrs = [ALIGNED] * 11
+        ptrs[i] = None
+        assert _app(lib, ptrs=tuple(ptrs)) == TV_ERR_NULL
+    ptrs = [ALIGNED] * 11
+    ptrs[4] = BAD                                         # k_new misaligned
+    assert _app(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
+    ptrs = [ALIGNED] * 11
+    ptrs[6] = 0x1004                                      # slot_mapping not 8-byte aligned
+    assert _app(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
 
 
 def _red(lib, S=2, hq=32, d=64, mctx=64, part=32, ptrs=(BAD,) * 5):

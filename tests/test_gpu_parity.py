@@ -29,12 +29,14 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _gpu_step(batch, dev, partition_size=None, max_context_len=None):
+def _gpu_step(batch, dev, partition_size=None, max_context_len=None, fused=False):
+    """One step through the C interface: three launches, or with ``fused`` the
+    write folded into the partition pass (tv_paged_attention_decode_append)."""
     import torch
     from paged_kv_cache_tv_amd.step import DeviceBatch
     db = DeviceBatch(batch, dev, partition_size=partition_size, max_context_len=max_context_len)
     db.fill()
-    out = db.step().clone()
+    out = (db.fused_step() if fused else db.step()).clone()
     torch.cuda.synchronize()
     return out.cpu().numpy(), db
 
@@ -269,3 +271,104 @@ def test_short_sequences(dev, oracle_lib):
     ref, _, _ = O.decode_step(oracle_lib, batch)
     got, _ = _gpu_step(batch, dev)
     _assert_close(got, ref, "300 short sequences")
+
+
+# ---------------------------------------------------------------------------
+# tv_paged_attention_decode_append: the cache write folded into the partition
+# pass.  Under its precondition it must equal the three-call step bit for bit.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
+def test_append_workload_parity(dev, oracle_lib, index):
+    """Full-size workloads through the two-launch step: pools bit-exact against
+    the oracle, output within the bars and bitwise equal to the three-launch step."""
+    batch = W.make_workload(index)
+    ref, kc_ref, vc_ref = _oracle_step(oracle_lib, ("workload", index), batch)
+    got, db = _gpu_step(batch, dev, fused=True)
+    kc, vc = db.pools_numpy()
+    assert np.array_equal(kc, kc_ref), "K pool differs from the oracle's cache write"
+    assert np.array_equal(vc, vc_ref), "V pool differs from the oracle's cache write"
+    _assert_close(got, ref, f"append workload {index}")
+    sep, _ = _gpu_step(batch, dev)
+    assert np.array_equal(got, sep), "fused step differs from the three-launch step"
+
+
+def test_append_edge_positions(dev, oracle_lib):
+    """The new token at every kind of position: first of a block, last of a block,
+    alone in a partition, the whole context (n = 1 returns V_new exactly)."""
+    lens = [1, 2, 16, 17, 32, 33, 512, 513, 1024, 1025, 1, 0]
+    batch = W.make_batch(lens, 42)
+    ref, kc_ref, vc_ref = O.decode_step(oracle_lib, batch)
+    got, db = _gpu_step(batch, dev, fused=True)
+    kc, vc = db.pools_numpy()
+    assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+    _assert_close(got, ref, "append edge positions")
+    sep, _ = _gpu_step(batch, dev)
+    assert np.array_equal(got, sep)
+    k_new, v_new, _ = batch.step_inputs()
+    vnew = W.bf16_bits_to_float32(v_new)[:, np.repeat(np.arange(8), 4)]
+    for s, n in enumerate(lens):
+        if n == 1:
+            assert np.array_equal(got[s], vnew[s]), "a one-token context must return V_new exactly"
+        if n == 0:
+            assert (got[s] == 0).all()
+
+
+def test_append_skips_and_slots_elsewhere(dev, oracle_lib):
+    """slot -1 and slots past the pool append nothing; a slot in a block no
+    sequence reads is written there while position n-1 is read from the pool."""
+    import torch
+    import paged_kv_cache_tv_amd as tv
+    from paged_kv_cache_tv_amd.step import DeviceBatch
+    batch = W.make_batch([40, 70, 300, 5], 43)
+    k_new, v_new, step_slots = batch.step_inputs()
+    rng = np.random.default_rng(43)
+    k_old = W.round_to_bf16_bits(rng.standard_normal(k_new.shape).astype(np.float32))
+    v_old = W.round_to_bf16_bits(rng.standard_normal(v_new.shape).astype(np.float32))
+    used = set(batch.block_tables.ravel().tolist())
+    spare = next(b for b in range(batch.num_blocks) if b not in used and b != batch.poison_block)
+    slots = step_slots.copy()
+    slots[0] = -1                                   # no new token for sequence 0
+    slots[1] = batch.num_blocks * 16 + 3            # past the pool: skipped
+    slots[2] = spare * 16 + 7                       # written elsewhere; not read by anyone
+    # Reference: position n-1 first holds (k_old, v_old); then the oracle's cache
+    # write of the new tokens at `slots`; then attention.
+    kc_ref, vc_ref = O.build_pools(oracle_lib, batch, include_step=False)
+    oracle_lib.cache_write(k_old, v_old, kc_ref, vc_ref, step_slots)
+    oracle_lib.cache_write(k_new, v_new, kc_ref, vc_ref, slots)
+    ref = oracle_lib.paged_attention(batch.q, kc_ref, vc_ref, batch.block_tables,
+                                     batch.context_lens, batch.scale)
+    db = DeviceBatch(batch, dev)
+    db.fill()
+    tv.cache_write(torch.from_numpy(k_old.view(np.int16)).to(dev),
+                   torch.from_numpy(v_old.view(np.int16)).to(dev), db.k_cache, db.v_cache,
+                   db.step_slots)
+    db.step_slots = torch.from_numpy(slots).to(dev)
+    out = db.fused_step().clone()
+    torch.cuda.synchronize()
+    kc, vc = db.pools_numpy()
+    assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+    _assert_close(out.cpu().numpy(), ref, "append skips")
+
+
+def test_append_errors(dev):
+    import torch
+    import paged_kv_cache_tv_amd as tv
+    q = torch.zeros((2, 32, 64), dtype=torch.int16, device=dev)
+    kc, vc = tv.new_pools(4, 8, 64, 16, dev)
+    kn = torch.zeros((2, 8, 64), dtype=torch.int16, device=dev)
+    bt = torch.zeros((2, 4), dtype=torch.int32, device=dev)
+    cl = torch.ones(2, dtype=torch.int32, device=dev)
+    ws = tv.new_workspace(2, 32, 64, 64, 32, dev)
+    sm = torch.zeros(2, dtype=torch.int64, device=dev)
+    with pytest.raises(ValueError):                   # k_new of the wrong shape
+        tv.paged_attention_decode_append(*ws, q, kn[:1], kn, sm, kc, vc, bt, cl, 64, 32, 0.125)
+    lib = tv.lib()
+    pa, pm, ps = ws
+    st = lib.tv_paged_attention_decode_append(pa.data_ptr(), pm.data_ptr(), ps.data_ptr(),
+                                              q.data_ptr(), None, kn.data_ptr(), sm.data_ptr(),
+                                              kc.data_ptr(), vc.data_ptr(), bt.data_ptr(),
+                                              cl.data_ptr(), 2, 32, 8, 64, 16, 4, 4, 64, 32,
+                                              0.125, None)
+    assert st == 1                                    # TV_ERR_NULL, nothing launched
+    torch.cuda.synchronize()
