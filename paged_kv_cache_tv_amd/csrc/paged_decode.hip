@@ -181,18 +181,22 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
         qb1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 32));
     }
 
-    // Append: the partition holding position n-1 stages the new token's K/V
-    // row of this head in LDS (after its first tile loads are out, so the
-    // stream is not delayed), replaces position n-1 with the staged row when
-    // the slot is that position's (the pool copy of that slot is never read
-    // back in this launch), and writes the row into the pools after its loop.
+    // Append: the partition holding position n-1 loads the new token's K/V row
+    // of this head with its first loads, stages it in LDS once its first tile
+    // loads are out, replaces position n-1 with the staged row when the slot
+    // is that position's (the pool copy of that slot is never read back in
+    // this launch), and writes the row into the pools after its loop.
     __shared__ uint16_t s_new[2 * D];     // K row then V row of the new token
     const bool append_here = APPEND && first_tok + ptok == n;
     int64_t wslot = -1;                   // slot to write (-1: none)
     int32_t tblk = -1;                    // table entry of position n-1
+    uint32_t new_pair = 0;                // lane l: K dims 2l, 2l+1 (l < 32) or V dims 2(l-32), +1
     if (append_here) {
         wslot = a.slot_mapping[s];
         tblk = a.block_tables[(int64_t)s * a.max_blocks + (n - 1) / BS];
+        new_pair = *reinterpret_cast<const uint32_t *>((lane < 32 ? a.k_new : a.v_new) +
+                                                       ((int64_t)s * a.num_kv_heads + kvh) * D +
+                                                       2 * (lane & 31));
     }
     int sub_off = -1;                     // token of the last tile replaced (-1: none)
 
@@ -256,10 +260,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
             issue(ring[u], block_of(u));
         if (APPEND && c0 == 0 && append_here) {
             if (wslot >= 0 && wslot < a.num_blocks * BS) {
-                // Lane l stages 4 bytes: K dims 2l, 2l+1 (l < 32) or V dims 2(l-32), 2(l-32)+1.
-                const uint16_t *row = (lane < 32 ? a.k_new : a.v_new) +
-                                      ((int64_t)s * a.num_kv_heads + kvh) * D + 2 * (lane & 31);
-                reinterpret_cast<uint32_t *>(s_new)[lane] = *reinterpret_cast<const uint32_t *>(row);
+                reinterpret_cast<uint32_t *>(s_new)[lane] = new_pair;   // stage the row in LDS
                 if ((int64_t)tblk * BS + (n - 1) % BS == wslot)
                     sub_off = (n - 1) % BS;
             } else {
