@@ -53,9 +53,16 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "paged_decode_traffic.json")
 
 
 def source_digest(path: str) -> str:
+    """sha256 of a kernel source with comments and blank space removed, so that
+    only a change of code (not of its comments) retires a measurement."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode("utf-8")).hexdigest()
 
 
 def measured_traffic(workload_name: str, kernel: str):

@@ -26,17 +26,19 @@
 //   * Scores S^T[16 tokens][16 heads] = K . Q^T come from two
 //     v_mfma_f32_16x16x32_bf16 over dims 0-31 and 32-63 (K is the A operand,
 //     the group's queries the B operand; columns past the group size are
-//     zero), so the K tile is read once for all query heads of the group.  Lane (g = lane/16, r = lane%16)
-//     then holds the scores of tokens 4g..4g+3 for query head r, which is
-//     exactly the B-operand layout of a 16x16x16 MFMA contracting over those 4
-//     tokens -- so the probabilities never leave the lane.
+//     zero), so the K tile is read once for all query heads of the group.
+//     Lane (g = lane/16, r = lane%16) then holds the scores of tokens
+//     4g..4g+3 for query head r, which is exactly the B-operand layout of a
+//     16x16x16 MFMA contracting over those 4 tokens -- so the probabilities
+//     never leave the lane.
 //   * O^T[64 dims][16 heads] += V^T . P^T uses v_mfma_f32_16x16x16_bf16 four
 //     times (16 dims each).  P is split into bf16 hi + lo parts (two MFMAs)
 //     so the products keep ~16 bits of P's mantissa instead of 8.
 //   * exp is computed as 2^x (v_exp_f32) with scale*log2(e) folded into the
 //     scores; the running maximum is kept in those base-2 units.  The only
 //     cross-lane traffic is the max over the 4 lane groups (2 shuffles per
-//     tile) and one final sum; no LDS, no barrier.
+//     tile) and one final sum; no barrier.  (LDS holds only the appended
+//     token's row in the append variant.)
 #include "tv_internal.h"
 
 #include <math.h>
