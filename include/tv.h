@@ -66,7 +66,8 @@ typedef enum tv_status {
     TV_ERR_SHAPE = 2,        /* sizes are negative, zero where they must not be, or inconsistent */
     TV_ERR_UNSUPPORTED = 3,  /* valid shape that this build does not implement */
     TV_ERR_HIP = 4,          /* the HIP runtime reported an error when launching */
-    TV_ERR_ALIGNMENT = 5     /* a pointer is not aligned as required */
+    TV_ERR_ALIGNMENT = 5,    /* a pointer is not aligned as required */
+    TV_ERR_NO_BLOCKS = 6     /* block manager: no free block left (or host memory exhausted) */
 } tv_status;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -225,6 +226,94 @@ tv_status tv_paged_attention_reduce(float *out, const float *part_acc,
                                     int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                     int32_t max_context_len, int32_t partition_size,
                                     void *stream);
+
+/*
+ * Copy-on-write support ("vLLM" page, section "가상 메모리 방식의 해결":
+ * requests sharing a prompt share its blocks; a block is copied when a branch
+ * writes into it).
+ *
+ * For every pair i < num_pairs, with src = block_pairs[2i] and dst =
+ * block_pairs[2i + 1]: every element of block dst (all K/V heads, both pools)
+ * becomes a copy of the same element of block src.  Pairs with src or dst
+ * outside [0, num_blocks), or src == dst, are skipped.  The copy is bit-exact.
+ *
+ *   k_cache, v_cache  pools (layout above), 16-byte aligned
+ *   block_pairs   int64 [num_pairs][2] (device), 8-byte aligned
+ *   num_kv_heads * head_dim * block_size must be a multiple of 8
+ *
+ * The destinations must be distinct and no destination may also be a source
+ * of the same call; otherwise the result is unspecified.  num_pairs == 0 is a
+ * no-op.  Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED,
+ * TV_ERR_ALIGNMENT, TV_ERR_HIP.
+ */
+tv_status tv_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int64_t *block_pairs,
+                         int64_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, void *stream);
+
+/*
+ * Block manager: host-side bookkeeping of the physical blocks ("vLLM" page,
+ * section "가상 메모리 방식의 해결": blocks handed out one at a time as tokens
+ * arrive -- 300 tokens take 19 blocks of 16 --, a per-sequence table from
+ * logical to physical blocks that need not be contiguous, and blocks shared
+ * between requests of one prompt with copy-on-write at the branch).
+ *
+ * A manager owns num_blocks physical block numbers and up to max_seqs
+ * sequences, identified by the caller's numbers 0 .. max_seqs-1.  It keeps a
+ * reference count per block: a block returns to the free list when no
+ * sequence refers to it.  The first blocks handed out are 0, 1, 2, ...; freed
+ * blocks are reused first.  All calls are host-only, do no GPU work and are
+ * not thread-safe for one manager (different managers are independent).
+ * The caller moves K/V data: tv_cache_write (or
+ * tv_paged_attention_decode_append) for the slots the manager returns, and
+ * tv_copy_blocks for the copy-on-write pairs it returns.
+ */
+typedef struct tv_block_manager tv_block_manager;
+
+/* New manager in *out (NULL on failure).  TV_ERR_SHAPE for non-positive sizes,
+ * TV_ERR_NO_BLOCKS if host memory runs out. */
+tv_status tv_bm_create(int32_t num_blocks, int32_t block_size, int32_t max_seqs,
+                       int32_t max_blocks_per_seq, tv_block_manager **out);
+void tv_bm_destroy(tv_block_manager *bm);              /* NULL is a no-op */
+
+/* Free blocks; reference count of a block; token count of a sequence (-1 for
+ * an unused sequence number or a bad argument). */
+int32_t tv_bm_num_free(const tv_block_manager *bm);
+int32_t tv_bm_refcount(const tv_block_manager *bm, int32_t block);
+int32_t tv_bm_length(const tv_block_manager *bm, int32_t seq);
+
+/* Start sequence `seq` (unused) with num_tokens positions and ceil(num_tokens /
+ * block_size) fresh blocks.  TV_ERR_NO_BLOCKS (nothing changed) if too few
+ * blocks are free; TV_ERR_SHAPE for a sequence in use or more than
+ * max_blocks_per_seq blocks. */
+tv_status tv_bm_add_sequence(tv_block_manager *bm, int32_t seq, int32_t num_tokens);
+
+/* Sequence `child` (unused) starts as a copy of `parent`: same length, same
+ * blocks, each block's reference count + 1.  No data moves. */
+tv_status tv_bm_fork(tv_block_manager *bm, int32_t parent, int32_t child);
+
+/* Reserve the next position n (= the current length) of `seq` and return its
+ * slot (block * block_size + offset); the length becomes n + 1.
+ *   - n % block_size == 0: a fresh block is appended to the table;
+ *   - otherwise, if the block holding n is shared (reference count > 1), it is
+ *     replaced in this table by a fresh block and *copy_src / *copy_dst name
+ *     the pair the caller must copy (tv_copy_blocks) before writing the slot;
+ *     else *copy_src = *copy_dst = -1.
+ * TV_ERR_NO_BLOCKS (nothing changed) if a block is needed and none is free. */
+tv_status tv_bm_append_slot(tv_block_manager *bm, int32_t seq, int64_t *slot,
+                            int64_t *copy_src, int64_t *copy_dst);
+
+/* Drop sequence `seq`: every block's reference count - 1, blocks reaching 0
+ * return to the free list. */
+tv_status tv_bm_free_sequence(tv_block_manager *bm, int32_t seq);
+
+/* The block table of `seq` into row[0 .. *num_blocks) (host memory);
+ * TV_ERR_SHAPE if it has more than `width` blocks. */
+tv_status tv_bm_block_table(const tv_block_manager *bm, int32_t seq, int32_t *row,
+                            int32_t width, int32_t *num_blocks);
+
+/* Slots of positions start .. start+count-1 of `seq` (host memory). */
+tv_status tv_bm_slots(const tv_block_manager *bm, int32_t seq, int32_t start, int32_t count,
+                      int64_t *slots);
 
 #ifdef __cplusplus
 }

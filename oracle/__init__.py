@@ -15,6 +15,8 @@ Parity status of each function (pins live in ``tests/test_oracle.py`` and
   * ``paged_attention`` -- pinned (contiguous brute force, torch SDPA,
                            closed forms, invariances, the 300-token paging
                            example).
+  * ``copy_blocks``     -- pinned (hand-derived literal pools; skip rules;
+                           refused conflicting pairs).
 """
 
 from __future__ import annotations
@@ -62,6 +64,9 @@ class Oracle:
                                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_long, ctypes.c_double, ctypes.c_int]
+        lib.oracle_copy_blocks.restype = ctypes.c_long
+        lib.oracle_copy_blocks.argtypes = [_u16p, _u16p, _i64p, ctypes.c_long, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_long]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         self.lib = lib
@@ -95,6 +100,22 @@ class Oracle:
             raise ValueError("duplicate slot in slot_mapping")
         if r < 0:
             raise ValueError("oracle_cache_write rejected its arguments")
+        return int(r)
+
+    def copy_blocks(self, k_cache: np.ndarray, v_cache: np.ndarray, pairs) -> int:
+        """Copy block src to block dst (both pools, all heads) for each (src, dst)
+        in ``pairs``, in place.  Returns the number of blocks copied."""
+        assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+        nb, hkv, dc, bs, x = k_cache.shape
+        d = dc * x
+        assert x == 8 and v_cache.shape == (nb, hkv, d, bs)
+        pr = np.ascontiguousarray(np.asarray(pairs, np.int64).reshape(-1, 2))
+        r = self.lib.oracle_copy_blocks(_ptr(k_cache, _u16p), _ptr(v_cache, _u16p),
+                                        _ptr(pr, _i64p), pr.shape[0], hkv, d, bs, nb)
+        if r == -2:
+            raise ValueError("a destination block repeats or is also a source")
+        if r < 0:
+            raise ValueError("oracle_copy_blocks rejected its arguments")
         return int(r)
 
     def paged_attention(self, q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,

@@ -121,6 +121,47 @@ long oracle_cache_write(const uint16_t *k, const uint16_t *v,
 }
 
 /*
+ * Copy-on-write of whole blocks ("vLLM" page, "가상 메모리 방식의 해결":
+ * requests of one prompt share its blocks; a branch writing into a shared
+ * block gets its own copy).  For each pair (src, dst) = (pairs[2i],
+ * pairs[2i+1]), every element of block dst in both pools becomes a copy of
+ * block src.  Pairs with a block outside the pool or src == dst are skipped.
+ * Returns the number of blocks copied, -1 on a bad argument, -2 if a
+ * destination repeats or is also a source (no pool is touched then).
+ */
+long oracle_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int64_t *pairs,
+                        long num_pairs, int num_kv_heads, int head_dim, int block_size,
+                        long num_blocks)
+{
+    if (num_pairs < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+        return -1;
+    for (long i = 0; i < num_pairs; ++i) {
+        int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst)
+            continue;
+        for (long j = 0; j < num_pairs; ++j) {
+            int64_t s2 = pairs[2 * j], d2 = pairs[2 * j + 1];
+            int valid2 = s2 >= 0 && s2 < num_blocks && d2 >= 0 && d2 < num_blocks && s2 != d2;
+            if (valid2 && j != i && (d2 == dst || s2 == dst))
+                return -2;
+        }
+    }
+    long block_elems = (long)num_kv_heads * head_dim * block_size;
+    long copied = 0;
+    for (long i = 0; i < num_pairs; ++i) {
+        int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst)
+            continue;
+        for (long e = 0; e < block_elems; ++e) {
+            k_cache[dst * block_elems + e] = k_cache[src * block_elems + e];
+            v_cache[dst * block_elems + e] = v_cache[src * block_elems + e];
+        }
+        ++copied;
+    }
+    return copied;
+}
+
+/*
  * out[s][h][d] (double, [S][Hq][D]) = softmax over t < n of
  * scale * q[s][h] . K_t, applied to V_t, with K_t, V_t read from the pools
  * through block_tables (int32 [S][max_blocks]) and n = context_lens[s].

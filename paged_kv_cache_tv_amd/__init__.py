@@ -5,10 +5,12 @@ log-sum-exp merge -- run in the HIP kernels of ``libtv.so``; this package only
 marshals torch tensors into the C calls declared in ``include/tv.h``.
 """
 
-from .binding import (LIB_PATH, TvError, cache_write, lib, load_library, new_pools,
+from .binding import (LIB_PATH, BlockManager, TvError, cache_write, copy_blocks, lib,
+                      load_library, new_pools,
                       new_workspace, num_partitions, paged_attention, paged_attention_decode,
                       paged_attention_decode_append, paged_attention_reduce)
 
-__all__ = ["LIB_PATH", "TvError", "cache_write", "lib", "load_library", "new_pools",
+__all__ = ["LIB_PATH", "BlockManager", "TvError", "cache_write", "copy_blocks", "lib",
+           "load_library", "new_pools",
            "new_workspace", "num_partitions", "paged_attention", "paged_attention_decode",
            "paged_attention_decode_append", "paged_attention_reduce"]

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtv.so")
 
 TV_OK = 0
 STATUS_NAMES = {0: "TV_OK", 1: "TV_ERR_NULL", 2: "TV_ERR_SHAPE", 3: "TV_ERR_UNSUPPORTED",
-                4: "TV_ERR_HIP", 5: "TV_ERR_ALIGNMENT"}
+                4: "TV_ERR_HIP", 5: "TV_ERR_ALIGNMENT", 6: "TV_ERR_NO_BLOCKS"}
 
 
 class TvError(RuntimeError):
@@ -53,6 +53,31 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                      f32, vp]
     lib.tv_paged_attention_reduce.restype = ctypes.c_int
     lib.tv_paged_attention_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.tv_copy_blocks.restype = ctypes.c_int
+    lib.tv_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, vp]
+    i32p, i64p = ctypes.POINTER(i32), ctypes.POINTER(i64)
+    lib.tv_bm_create.restype = ctypes.c_int
+    lib.tv_bm_create.argtypes = [i32, i32, i32, i32, ctypes.POINTER(vp)]
+    lib.tv_bm_destroy.restype = None
+    lib.tv_bm_destroy.argtypes = [vp]
+    for name in ("tv_bm_num_free",):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = [vp]
+    for name in ("tv_bm_refcount", "tv_bm_length"):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = [vp, i32]
+    lib.tv_bm_add_sequence.restype = ctypes.c_int
+    lib.tv_bm_add_sequence.argtypes = [vp, i32, i32]
+    lib.tv_bm_fork.restype = ctypes.c_int
+    lib.tv_bm_fork.argtypes = [vp, i32, i32]
+    lib.tv_bm_append_slot.restype = ctypes.c_int
+    lib.tv_bm_append_slot.argtypes = [vp, i32, i64p, i64p, i64p]
+    lib.tv_bm_free_sequence.restype = ctypes.c_int
+    lib.tv_bm_free_sequence.argtypes = [vp, i32]
+    lib.tv_bm_block_table.restype = ctypes.c_int
+    lib.tv_bm_block_table.argtypes = [vp, i32, i32p, i32, i32p]
+    lib.tv_bm_slots.restype = ctypes.c_int
+    lib.tv_bm_slots.argtypes = [vp, i32, i32, i32, i64p]
     return lib
 
 
@@ -255,3 +280,86 @@ def paged_attention(q, k_cache, v_cache, block_tables, context_lens, max_context
                            max_context_len, partition_size, scale, stream)
     paged_attention_reduce(out, pa, pm, ps, context_lens, max_context_len, partition_size, stream)
     return out
+
+
+def copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:
+    """tv_copy_blocks.  block_pairs: int64 [num_pairs, 2] (source, destination) on
+    the device; pools as for cache_write."""
+    import torch
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    _need(block_pairs, "block_pairs", dtype=torch.int64, ndim=2)
+    if block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [num_pairs, 2]")
+    st = lib().tv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_pairs.data_ptr(),
+                              block_pairs.shape[0], hkv, d, bs, nb,
+                              _stream_handle(stream, k_cache.device))
+    _check("tv_copy_blocks", st)
+
+
+class BlockManager:
+    """The library's block manager (tv_bm_*): free list, per-sequence block
+    tables, reference counts and copy-on-write.  Host-only bookkeeping; the
+    caller moves the K/V data (cache_write / decode_append for slots,
+    copy_blocks for copy-on-write pairs)."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_seqs: int, max_blocks_per_seq: int):
+        self._lib = lib()
+        h = ctypes.c_void_p()
+        _check("tv_bm_create", self._lib.tv_bm_create(num_blocks, block_size, max_seqs,
+                                                      max_blocks_per_seq, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.max_seqs, self.max_blocks_per_seq = max_seqs, max_blocks_per_seq
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.tv_bm_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def num_free(self) -> int:
+        return int(self._lib.tv_bm_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.tv_bm_refcount(self._h, block))
+
+    def length(self, seq: int) -> int:
+        return int(self._lib.tv_bm_length(self._h, seq))
+
+    def add_sequence(self, seq: int, num_tokens: int) -> None:
+        _check("tv_bm_add_sequence", self._lib.tv_bm_add_sequence(self._h, seq, num_tokens))
+
+    def fork(self, parent: int, child: int) -> None:
+        _check("tv_bm_fork", self._lib.tv_bm_fork(self._h, parent, child))
+
+    def append_slot(self, seq: int):
+        """(slot, copy_src, copy_dst) for the next position of ``seq``; copy_src /
+        copy_dst are -1 unless a shared block had to be copied."""
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check("tv_bm_append_slot", self._lib.tv_bm_append_slot(
+            self._h, seq, ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst)))
+        return slot.value, src.value, dst.value
+
+    def free_sequence(self, seq: int) -> None:
+        _check("tv_bm_free_sequence", self._lib.tv_bm_free_sequence(self._h, seq))
+
+    def block_table(self, seq: int):
+        import numpy as np
+        row = np.zeros(self.max_blocks_per_seq, np.int32)
+        nb = ctypes.c_int32()
+        _check("tv_bm_block_table", self._lib.tv_bm_block_table(
+            self._h, seq, row.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), row.shape[0],
+            ctypes.byref(nb)))
+        return row[:nb.value].copy()
+
+    def slots(self, seq: int, start: int, count: int):
+        import numpy as np
+        out = np.zeros(count, np.int64)
+        _check("tv_bm_slots", self._lib.tv_bm_slots(
+            self._h, seq, start, count, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+        return out

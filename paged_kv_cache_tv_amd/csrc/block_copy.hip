@@ -1,0 +1,56 @@
+// Block copy for copy-on-write ("vLLM" page, section "가상 메모리 방식의 해결":
+// requests sharing a prompt share its blocks, and a block is copied only when a
+// branch writes into it).  Copies every K/V head of block src to block dst in
+// both pools: a bit copy of two contiguous runs of
+// num_kv_heads * block_size * head_dim values.
+//
+// One 256-thread workgroup per (pair, pool); each thread moves 16-byte
+// chunks, so the 16 KiB runs of the decode shape take four loads and four
+// stores per thread, all issued before the first store.
+#include "tv_internal.h"
+
+namespace tv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+__global__ __launch_bounds__(kThreads) void block_copy_kernel(BlockCopyArgs a)
+{
+    const int64_t pair = blockIdx.x >> 1;
+    const int pool = blockIdx.x & 1;
+    const int64_t src = a.pairs[2 * pair];
+    const int64_t dst = a.pairs[2 * pair + 1];
+    if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks || src == dst)
+        return;
+    uint16_t *base = pool ? a.v_cache : a.k_cache;
+    const uint4 *from = reinterpret_cast<const uint4 *>(base + src * a.block_elems);
+    uint4 *to = reinterpret_cast<uint4 *>(base + dst * a.block_elems);
+    const int64_t chunks = a.block_elems / 8;
+    for (int64_t c0 = 0; c0 < chunks; c0 += kThreads * kUnroll) {
+        uint4 x[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t c = c0 + u * kThreads + threadIdx.x;
+            if (c < chunks)
+                x[u] = from[c];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t c = c0 + u * kThreads + threadIdx.x;
+            if (c < chunks)
+                to[c] = x[u];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t stream)
+{
+    hipLaunchKernelGGL(block_copy_kernel, dim3((unsigned)(2 * a.num_pairs)), dim3(kThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace tv

@@ -27,6 +27,7 @@ const char *tv_status_string(tv_status status)
     case TV_ERR_UNSUPPORTED: return "TV_ERR_UNSUPPORTED: shape not implemented";
     case TV_ERR_HIP: return "TV_ERR_HIP: HIP runtime error";
     case TV_ERR_ALIGNMENT: return "TV_ERR_ALIGNMENT: misaligned pointer";
+    case TV_ERR_NO_BLOCKS: return "TV_ERR_NO_BLOCKS: no free block (or no host memory)";
     }
     return "unknown tv_status";
 }
@@ -205,3 +206,27 @@ tv_status tv_paged_attention_reduce(float *out, const float *part_acc, const flo
 }
 
 }  // extern "C"
+
+tv_status tv_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int64_t *block_pairs,
+                         int64_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, void *stream)
+{
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks <= 0)
+        return TV_ERR_SHAPE;
+    const int64_t block_elems = (int64_t)num_kv_heads * head_dim * block_size;
+    if (block_elems % 8 != 0)
+        return TV_ERR_UNSUPPORTED;
+    if (num_pairs == 0)
+        return TV_OK;
+    if (!k_cache || !v_cache || !block_pairs)
+        return TV_ERR_NULL;
+    if (2 * num_pairs > 0x7fffffff)
+        return TV_ERR_UNSUPPORTED;
+    if (num_blocks > INT64_MAX / block_elems)
+        return TV_ERR_SHAPE;
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 8))
+        return TV_ERR_ALIGNMENT;
+    tv::BlockCopyArgs a{k_cache, v_cache, block_pairs, num_pairs, num_blocks, block_elems};
+    return from_hip(tv::launch_block_copy(a, static_cast<hipStream_t>(stream)));
+}

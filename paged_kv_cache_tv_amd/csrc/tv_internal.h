@@ -66,7 +66,17 @@ struct ReduceArgs {
     int32_t max_context_len;
 };
 
+struct BlockCopyArgs {
+    uint16_t *k_cache;
+    uint16_t *v_cache;
+    const int64_t *pairs;       // [num_pairs][2]: source block, destination block
+    int64_t num_pairs;
+    int64_t num_blocks;
+    int64_t block_elems;        // num_kv_heads * block_size * head_dim (a multiple of 8)
+};
+
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream);
+hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_paged_reduce(const ReduceArgs &a, hipStream_t stream);
 

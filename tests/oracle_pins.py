@@ -12,7 +12,8 @@ the oracle disagrees with:
     thread count;
   * the pages' worked paging example (300 tokens -> 19 blocks) and the GQA
     grouping figure, stored under tests/golden/ with their citations;
-  * a hand-derived literal cache layout (tests/golden/cache_layout_tiny.json).
+  * a hand-derived literal cache layout (tests/golden/cache_layout_tiny.json)
+    and a hand-derived literal block copy (tests/golden/block_copy_tiny.json).
 
 Run as a script (``python tests/oracle_pins.py LIB``) it executes every pin
 against the oracle library LIB and prints one line per pin: the mutation test
@@ -346,11 +347,34 @@ def pin_thread_invariance(orc):
     assert np.array_equal(a, c)
 
 
+def pin_block_copy_literal(orc):
+    """Copy-on-write copies land exactly where the hand-derived literal pools say;
+    pairs naming one block twice or a block past the pool are skipped; a pair
+    list whose destination repeats is refused without touching the pools."""
+    g = _golden("block_copy_tiny.json")
+    nb, hkv, bs, d = g["num_blocks"], g["num_kv_heads"], g["block_size"], g["head_dim"]
+    kc = np.array(g["k_pool_before"], np.uint16).reshape(nb, hkv, d // 8, bs, 8)
+    vc = np.array(g["v_pool_before"], np.uint16).reshape(nb, hkv, d, bs)
+    copied = orc.copy_blocks(kc, vc, g["pairs"])
+    assert copied == g["copied"]
+    assert kc.reshape(nb, -1).tolist() == g["expected_k_pool"], "K pool after the copy"
+    assert vc.reshape(nb, -1).tolist() == g["expected_v_pool"], "V pool after the copy"
+    kc2, vc2 = kc.copy(), vc.copy()
+    for bad in ([[0, 1], [2, 1]], [[0, 1], [1, 2]]):       # repeated destination; dst also a source
+        try:
+            orc.copy_blocks(kc2, vc2, bad)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError(f"conflicting pairs {bad} accepted")
+    assert np.array_equal(kc2, kc) and np.array_equal(vc2, vc), "refused copy touched the pools"
+
+
 ALL_PINS = [
     pin_contiguous_bruteforce, pin_torch_sdpa, pin_block_permutation, pin_single_token,
     pin_constant_v, pin_zero_query_mean, pin_gqa_figure, pin_one_dominant_key,
     pin_two_token_logistic, pin_score_shift, pin_paging_example, pin_cache_layout_literal,
-    pin_cache_write_untouched, pin_empty, pin_thread_invariance,
+    pin_cache_write_untouched, pin_empty, pin_thread_invariance, pin_block_copy_literal,
 ]
 
 

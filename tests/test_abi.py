@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         assert lib.tv_status_string(code)
     assert b"unknown" in lib.tv_status_string(99)
 
@@ -130,6 +130,20 @@ def test_decode_append_validation(lib):
     ptrs = [ALIGNED] * 11
     ptrs[6] = 0x1004                                      # slot_mapping not 8-byte aligned
     assert _app(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
+
+
+def _copy(lib, n=3, hkv=8, d=64, bs=16, nb=8, ptrs=(BAD,) * 3):
+    return lib.tv_copy_blocks(*ptrs, n, hkv, d, bs, nb, None)
+
+
+def test_copy_blocks_validation(lib):
+    assert _copy(lib, n=-1) == TV_ERR_SHAPE
+    assert _copy(lib, hkv=0) == TV_ERR_SHAPE
+    assert _copy(lib, nb=0) == TV_ERR_SHAPE
+    assert _copy(lib, hkv=1, d=3, bs=1) == TV_ERR_UNSUPPORTED    # 3 values per block
+    assert _copy(lib, n=0, ptrs=(None,) * 3) == TV_OK           # no-op
+    assert _copy(lib, ptrs=(BAD, BAD, None)) == TV_ERR_NULL
+    assert _copy(lib) == TV_ERR_ALIGNMENT
 
 
 def _red(lib, S=2, hq=32, d=64, mctx=64, part=32, ptrs=(BAD,) * 5):

@@ -57,6 +57,12 @@ MUTANTS = [
      "long kdst = k_index(blk, num_kv_heads - 1 - h, off, d, num_kv_heads, head_dim, block_size);"),
     ("write-keeps-padding", "if (slot < 0 || slot >= num_slots)\n            continue;\n        long blk",
      "if (slot >= num_slots)\n            continue;\n        if (slot < 0) slot = 0;\n        long blk"),
+    ("copy-k-only", "v_cache[dst * block_elems + e] = v_cache[src * block_elems + e];", ";"),
+    ("copy-direction-swapped", "k_cache[dst * block_elems + e] = k_cache[src * block_elems + e];",
+     "k_cache[src * block_elems + e] = k_cache[dst * block_elems + e];"),
+    ("copy-skips-nothing", "|| src == dst)\n            continue;\n        for (long e",
+     ")\n            continue;\n        for (long e"),
+    ("copy-half-block", "for (long e = 0; e < block_elems; ++e)", "for (long e = 0; e < block_elems / 2; ++e)"),
     ("pv-uses-first-token", "o[d] += p * bf16_value(vtile[(long)d * block_size + off]);",
      "o[d] += p * bf16_value(v_cache[(long)d * block_size]);"),
 ]
