@@ -97,6 +97,63 @@ def algorithmic_bytes(batch):
     return decode, decode + reduce_out + write, write
 
 
+def block_copy_rate(tv, dev, stream, flush, steps, pairs=2048):
+    """Copy-on-write copies on a pool of their own: `pairs` blocks (all 8 K/V
+    heads of 16 tokens x 64 dims in both pools, 32 KiB per block) copied to
+    fresh blocks.  Each launch follows a cache eviction and is bracketed by its
+    own pair of events on the kernel's stream; the figure is the mean over
+    `steps` launches.  Bytes counted: each block read once and written once."""
+    import torch
+    kc, vc = tv.new_pools(2 * pairs, 8, 64, 16, dev, fill=0)
+    pr = torch.stack([torch.arange(pairs), pairs + torch.arange(pairs)], 1).to(torch.int64).to(dev)
+    tv.copy_blocks(kc, vc, pr, stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        flush(i)
+        a.record(stream)
+        tv.copy_blocks(kc, vc, pr, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    moved = pairs * 2 * (2 * 8 * 16 * 64 * 2)           # read + write, K and V pools
+    gbs = moved / (ms * 1e-3) / 1e9
+    del kc, vc
+    return {"kernel": "block_copy_kernel", "pairs": pairs, "bytes_per_launch": moved,
+            "us_per_launch": round(ms * 1e3, 2), "GB_per_s": round(gbs, 2),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def block_manager_rate(tv, steps, prompts=64, samples=4, prefix=1024, seed=7):
+    """Host cost of one decode step's bookkeeping: tv_bm_prepare_decode for a
+    live batch shaped like the shared-prefix workload (64 prompts of 1024
+    tokens, each forked into 4 samples with U{0..1024} private tokens).  Mean
+    wall-clock microseconds per call over `steps` calls, each call growing all
+    256 sequences by one token."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    bs, width = 16, 192
+    S = prompts * samples
+    bm = tv.BlockManager(prompts * prefix // bs + S * (1024 + steps + 16) // bs + 64, bs, S, width)
+    for p in range(prompts):
+        bm.add_sequence(samples * p, prefix)
+        for j in range(1, samples):
+            bm.fork(samples * p, samples * p + j)
+    for s, r in enumerate(rng.integers(0, 1025, S)):
+        for _ in range(int(r)):
+            bm.append_slot(s)
+    seqs = list(range(S))
+    bm.prepare_decode(seqs, width)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        bm.prepare_decode(seqs, width)
+    us = (time.perf_counter() - t0) / steps * 1e6
+    bm.close()
+    return {"call": "tv_bm_prepare_decode", "seqs": S, "width": width,
+            "host_us_per_step": round(us, 2)}
+
+
 def cpu_baseline(batch, target_seconds: float):
     """Time the CPU oracle doing the same step (cache write + attention) on this host."""
     import oracle as O
@@ -127,6 +184,8 @@ def main(argv=None):
     ap.add_argument("--step", choices=["fused", "separate"], default="fused",
                     help="two launches (write folded into the partition pass) or three")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block-copy", action="store_true",
+                    help="skip the copy-on-write block copy measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-flush", action="store_true", help="skip the cold-cache flush")
     ap.add_argument("--lib", default=None, help="load libtv from this path instead of the package")
@@ -309,6 +368,10 @@ def main(argv=None):
                      "algorithmic_bytes_per_launch": roof_bytes,
                      "avg_launch_us": round(roof_ms * 1e3, 2)},
     }
+
+    if not args.no_block_copy:
+        result["block_copy"] = block_copy_rate(tv, dev, stream, flush, K)
+        result["block_manager"] = block_manager_rate(tv, K)
 
     if not args.no_cpu_baseline:
         ref, times, threads = cpu_baseline(batch, args.cpu_seconds)

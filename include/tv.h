@@ -302,6 +302,30 @@ tv_status tv_bm_fork(tv_block_manager *bm, int32_t parent, int32_t child);
 tv_status tv_bm_append_slot(tv_block_manager *bm, int32_t seq, int64_t *slot,
                             int64_t *copy_src, int64_t *copy_dst);
 
+/* One decode step's host-side inputs for the sequences seqs[0 .. num_seqs):
+ * for r = 0, 1, ... in order, the next position of seqs[r] is reserved as by
+ * tv_bm_append_slot, and then
+ *   slot_mapping[r]             its slot,
+ *   context_lens[r]             the new length (the new token included),
+ *   block_tables[r*width + j]   block j of its table, 0 past its last block,
+ *   copy_pairs[2c], [2c + 1]    the c-th copy-on-write pair (src, dst), in
+ *                               order of r, c < *num_copies <= num_seqs.
+ * All outputs are host memory: block_tables int32 [num_seqs][width],
+ * context_lens int32 [num_seqs], slot_mapping int64 [num_seqs], copy_pairs
+ * int64 [num_seqs][2].  These are the inputs of tv_copy_blocks (run first),
+ * then tv_paged_attention_decode_append: every slot lies in a block that only
+ * its own sequence's table holds, so the append precondition holds; the copy
+ * destinations are fresh blocks, distinct and never a source of the call.
+ * The seqs must be distinct live sequences whose new block count fits width
+ * and max_blocks_per_seq, else TV_ERR_SHAPE before anything changes.
+ * All-or-nothing: on TV_ERR_NO_BLOCKS (a block is needed and none is free)
+ * every reservation already made is taken back, leaving the manager, its free
+ * list order included, as before the call; the outputs are then unspecified.
+ * num_seqs == 0 sets *num_copies = 0. */
+tv_status tv_bm_prepare_decode(tv_block_manager *bm, const int32_t *seqs, int32_t num_seqs,
+                               int32_t width, int32_t *block_tables, int32_t *context_lens,
+                               int64_t *slot_mapping, int64_t *copy_pairs, int32_t *num_copies);
+
 /* Drop sequence `seq`: every block's reference count - 1, blocks reaching 0
  * return to the free list. */
 tv_status tv_bm_free_sequence(tv_block_manager *bm, int32_t seq);

@@ -78,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_bm_block_table.argtypes = [vp, i32, i32p, i32, i32p]
     lib.tv_bm_slots.restype = ctypes.c_int
     lib.tv_bm_slots.argtypes = [vp, i32, i32, i32, i64p]
+    lib.tv_bm_prepare_decode.restype = ctypes.c_int
+    lib.tv_bm_prepare_decode.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, i32p]
     return lib
 
 
@@ -363,3 +365,21 @@ class BlockManager:
         _check("tv_bm_slots", self._lib.tv_bm_slots(
             self._h, seq, start, count, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
         return out
+
+    def prepare_decode(self, seqs, width: int):
+        """Reserve one position for each of ``seqs`` (in order) and return the
+        host arrays of that decode step: (block_tables int32 [S][width],
+        context_lens int32 [S], slot_mapping int64 [S], copy_pairs int64 [C][2]).
+        All-or-nothing: on error nothing has changed."""
+        import numpy as np
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        S = seqs.shape[0]
+        tables = np.empty((S, width), np.int32)
+        lens = np.empty(S, np.int32)
+        slots = np.empty(S, np.int64)
+        pairs = np.empty((S, 2), np.int64)
+        nc = ctypes.c_int32()
+        _check("tv_bm_prepare_decode", self._lib.tv_bm_prepare_decode(
+            self._h, seqs.ctypes.data, S, width, tables.ctypes.data, lens.ctypes.data,
+            slots.ctypes.data, pairs.ctypes.data, ctypes.byref(nc)))
+        return tables, lens, slots, pairs[:nc.value].copy()

@@ -4,16 +4,19 @@
 // both pools: a bit copy of two contiguous runs of
 // num_kv_heads * block_size * head_dim values.
 //
-// One 256-thread workgroup per (pair, pool); each thread moves 16-byte
-// chunks, so the 16 KiB runs of the decode shape take four loads and four
-// stores per thread, all issued before the first store.
+// One 128-thread workgroup per (pair, pool); each thread moves eight 16-byte
+// chunks per pass, so a 16 KiB run of the decode shape is one pass: eight
+// loads, then eight stores.  Both are non-temporal: the source is read once
+// and the destination is next read by a later launch.
 #include "tv_internal.h"
 
 namespace tv {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kThreads = 128;
+constexpr int kUnroll = 8;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void block_copy_kernel(BlockCopyArgs a)
 {
@@ -24,22 +27,22 @@ __global__ __launch_bounds__(kThreads) void block_copy_kernel(BlockCopyArgs a)
     if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks || src == dst)
         return;
     uint16_t *base = pool ? a.v_cache : a.k_cache;
-    const uint4 *from = reinterpret_cast<const uint4 *>(base + src * a.block_elems);
-    uint4 *to = reinterpret_cast<uint4 *>(base + dst * a.block_elems);
+    const u32x4 *from = reinterpret_cast<const u32x4 *>(base + src * a.block_elems);
+    u32x4 *to = reinterpret_cast<u32x4 *>(base + dst * a.block_elems);
     const int64_t chunks = a.block_elems / 8;
     for (int64_t c0 = 0; c0 < chunks; c0 += kThreads * kUnroll) {
-        uint4 x[kUnroll];
+        u32x4 x[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t c = c0 + u * kThreads + threadIdx.x;
             if (c < chunks)
-                x[u] = from[c];
+                x[u] = __builtin_nontemporal_load(from + c);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t c = c0 + u * kThreads + threadIdx.x;
             if (c < chunks)
-                to[c] = x[u];
+                __builtin_nontemporal_store(x[u], to + c);
         }
     }
 }

@@ -10,6 +10,7 @@
 // plain host memory owned by the manager object; nothing touches the GPU.
 #include "../../include/tv.h"
 
+#include <algorithm>
 #include <cstdint>
 #include <new>
 #include <vector>
@@ -21,6 +22,7 @@ struct tv_block_manager {
     std::vector<int32_t> refcount;            // per physical block
     std::vector<int32_t> length;              // per sequence; -1 = not in use
     std::vector<std::vector<int32_t>> table;  // per sequence
+    std::vector<uint8_t> seen;                // prepare_decode scratch, per sequence
 };
 
 namespace {
@@ -54,6 +56,71 @@ void release_block(tv_block_manager *bm, int32_t b)
         bm->free_stack.push_back(b);
 }
 
+// One reserved position, with what it did to the books so that it can be
+// taken back.
+struct Append {
+    enum Kind { kInPlace, kNewBlock, kCopy } kind = kInPlace;
+    int32_t seq = -1;
+    int32_t index = 0;        // table index of the block holding the position
+    int32_t old_block = -1;   // kCopy: the shared block it replaced
+    int32_t new_block = -1;   // kNewBlock / kCopy: the block taken from the free list
+    int64_t slot = -1;
+};
+
+// Reserve position n = length[seq] of a live sequence (see tv_bm_append_slot).
+// On TV_ERR_SHAPE / TV_ERR_NO_BLOCKS nothing has changed.
+tv_status append(tv_block_manager *bm, int32_t seq, Append *out)
+{
+    std::vector<int32_t> &t = bm->table[seq];
+    const int32_t n = bm->length[seq];
+    const int32_t off = n % bm->block_size;
+    Append a;
+    a.seq = seq;
+    a.index = n / bm->block_size;
+    if (off == 0) {                               // the position opens a new block
+        if ((int32_t)t.size() + 1 > bm->max_blocks_per_seq)
+            return TV_ERR_SHAPE;
+        if (bm->free_stack.empty())
+            return TV_ERR_NO_BLOCKS;
+        try {
+            t.reserve(t.size() + 1);
+        } catch (...) {
+            return TV_ERR_NO_BLOCKS;
+        }
+        a.kind = Append::kNewBlock;
+        a.new_block = take_block(bm);
+        t.push_back(a.new_block);
+    } else if (bm->refcount[t[a.index]] > 1) {    // shared: copy on write
+        if (bm->free_stack.empty())
+            return TV_ERR_NO_BLOCKS;
+        a.kind = Append::kCopy;
+        a.old_block = t[a.index];
+        a.new_block = take_block(bm);
+        --bm->refcount[a.old_block];
+        t[a.index] = a.new_block;
+    }
+    a.slot = (int64_t)t[a.index] * bm->block_size + off;
+    bm->length[seq] = n + 1;
+    *out = a;
+    return TV_OK;
+}
+
+// Take back the most recent append still standing.  Undoing appends in the
+// reverse of their order restores the free list's order too.
+void undo(tv_block_manager *bm, const Append &a)
+{
+    std::vector<int32_t> &t = bm->table[a.seq];
+    --bm->length[a.seq];
+    if (a.kind == Append::kNewBlock) {
+        t.pop_back();
+        release_block(bm, a.new_block);
+    } else if (a.kind == Append::kCopy) {
+        t[a.index] = a.old_block;
+        ++bm->refcount[a.old_block];
+        release_block(bm, a.new_block);
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -78,6 +145,7 @@ tv_status tv_bm_create(int32_t num_blocks, int32_t block_size, int32_t max_seqs,
         bm->refcount.assign(num_blocks, 0);
         bm->length.assign(max_seqs, -1);
         bm->table.resize(max_seqs);
+        bm->seen.assign(max_seqs, 0);
     } catch (...) {
         delete bm;
         return TV_ERR_NO_BLOCKS;
@@ -121,6 +189,11 @@ tv_status tv_bm_add_sequence(tv_block_manager *bm, int32_t seq, int32_t num_toke
         return TV_ERR_NO_BLOCKS;
     std::vector<int32_t> &t = bm->table[seq];
     t.clear();
+    try {
+        t.reserve((size_t)need);
+    } catch (...) {
+        return TV_ERR_NO_BLOCKS;
+    }
     for (int32_t i = 0; i < need; ++i)
         t.push_back(take_block(bm));
     bm->length[seq] = num_tokens;
@@ -133,7 +206,11 @@ tv_status tv_bm_fork(tv_block_manager *bm, int32_t parent, int32_t child)
         return TV_ERR_NULL;
     if (!live_seq(bm, parent) || !valid_seq(bm, child) || bm->length[child] >= 0)
         return TV_ERR_SHAPE;
-    bm->table[child] = bm->table[parent];
+    try {
+        bm->table[child] = bm->table[parent];
+    } catch (...) {
+        return TV_ERR_NO_BLOCKS;
+    }
     for (int32_t b : bm->table[child])
         ++bm->refcount[b];
     bm->length[child] = bm->length[parent];
@@ -147,31 +224,81 @@ tv_status tv_bm_append_slot(tv_block_manager *bm, int32_t seq, int64_t *slot,
         return TV_ERR_NULL;
     if (!live_seq(bm, seq))
         return TV_ERR_SHAPE;
-    std::vector<int32_t> &t = bm->table[seq];
-    const int32_t n = bm->length[seq];
-    const int32_t off = n % bm->block_size;
-    *copy_src = -1;
-    *copy_dst = -1;
-    if (off == 0) {                               // the position opens a new block
-        if ((int32_t)t.size() + 1 > bm->max_blocks_per_seq)
-            return TV_ERR_SHAPE;
-        if (bm->free_stack.empty())
-            return TV_ERR_NO_BLOCKS;
-        t.push_back(take_block(bm));
-    } else {
-        int32_t &last = t[n / bm->block_size];
-        if (bm->refcount[last] > 1) {             // shared: copy on write
-            if (bm->free_stack.empty())
-                return TV_ERR_NO_BLOCKS;
-            const int32_t fresh = take_block(bm);
-            *copy_src = last;
-            *copy_dst = fresh;
-            --bm->refcount[last];
-            last = fresh;
+    Append r;
+    const tv_status st = append(bm, seq, &r);
+    if (st != TV_OK)
+        return st;
+    *slot = r.slot;
+    *copy_src = r.kind == Append::kCopy ? r.old_block : -1;
+    *copy_dst = r.kind == Append::kCopy ? r.new_block : -1;
+    return TV_OK;
+}
+
+tv_status tv_bm_prepare_decode(tv_block_manager *bm, const int32_t *seqs, int32_t num_seqs,
+                               int32_t width, int32_t *block_tables, int32_t *context_lens,
+                               int64_t *slot_mapping, int64_t *copy_pairs, int32_t *num_copies)
+{
+    if (!bm || !num_copies)
+        return TV_ERR_NULL;
+    if (num_seqs < 0 || width < 0)
+        return TV_ERR_SHAPE;
+    if (num_seqs > 0 && (!seqs || !block_tables || !context_lens || !slot_mapping || !copy_pairs))
+        return TV_ERR_NULL;
+    // Every check that does not depend on the free list comes first, so that
+    // only a shortage of blocks can stop the loop below.
+    std::vector<Append> done;
+    try {
+        done.reserve((size_t)num_seqs);
+    } catch (...) {
+        return TV_ERR_NO_BLOCKS;
+    }
+    std::vector<uint8_t> &seen = bm->seen;    // all zero between calls
+    tv_status bad = TV_OK;
+    int32_t checked = 0;
+    for (; checked < num_seqs; ++checked) {
+        const int32_t seq = seqs[checked];
+        if (!live_seq(bm, seq) || seen[seq]) {
+            bad = TV_ERR_SHAPE;
+            break;
+        }
+        seen[seq] = 1;
+        const int32_t need = blocks_for(bm, (int64_t)bm->length[seq] + 1);
+        if (need > width || need > bm->max_blocks_per_seq) {
+            ++checked;
+            bad = TV_ERR_SHAPE;
+            break;
         }
     }
-    *slot = (int64_t)t[n / bm->block_size] * bm->block_size + off;
-    bm->length[seq] = n + 1;
+    for (int32_t r = 0; r < checked; ++r)
+        seen[seqs[r]] = 0;
+    if (bad != TV_OK)
+        return bad;
+    for (int32_t r = 0; r < num_seqs; ++r) {
+        Append a;
+        const tv_status st = append(bm, seqs[r], &a);
+        if (st != TV_OK) {
+            for (auto it = done.rbegin(); it != done.rend(); ++it)
+                undo(bm, *it);
+            return st;
+        }
+        done.push_back(a);
+    }
+    int32_t copies = 0;
+    for (int32_t r = 0; r < num_seqs; ++r) {
+        const int32_t seq = seqs[r];
+        const std::vector<int32_t> &t = bm->table[seq];
+        int32_t *row = block_tables + (int64_t)r * width;
+        std::copy(t.begin(), t.end(), row);
+        std::fill(row + t.size(), row + width, 0);
+        context_lens[r] = bm->length[seq];
+        slot_mapping[r] = done[r].slot;
+        if (done[r].kind == Append::kCopy) {
+            copy_pairs[2 * copies] = done[r].old_block;
+            copy_pairs[2 * copies + 1] = done[r].new_block;
+            ++copies;
+        }
+    }
+    *num_copies = copies;
     return TV_OK;
 }
 

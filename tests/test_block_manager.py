@@ -174,3 +174,108 @@ def test_random_operations_keep_the_books(seed):
             bm.free_sequence(s)
             del live[s]
         _check_invariants(bm, live, NB)
+
+
+def _state(bm, seqs, num_blocks):
+    """Everything observable about a manager: lengths, tables, reference counts,
+    and the order in which free blocks would be handed out."""
+    live = {s: (bm.length(s), bm.block_table(s).tolist()) for s in seqs if bm.length(s) >= 0}
+    refs = [bm.refcount(b) for b in range(num_blocks)]
+    return live, refs, bm.num_free()
+
+
+def _free_order(bm, num_blocks, probe_seq):
+    """The free list from the top down, read by taking every free block with one
+    add_sequence on an unused sequence number (then giving them back)."""
+    n = bm.num_free()
+    if n == 0:
+        return []
+    bm.add_sequence(probe_seq, n * BS)
+    order = bm.block_table(probe_seq).tolist()
+    bm.free_sequence(probe_seq)
+    return order
+
+
+def _scenario(seed, NB=96, SEQS=24, width=24):
+    rng = np.random.default_rng(seed)
+    bm = tv.BlockManager(NB, BS, SEQS + 1, width)
+    live = []
+    for i in range(6):
+        bm.add_sequence(3 * i, int(rng.integers(1, 100)))
+        live.append(3 * i)
+        for j in (1, 2):
+            if rng.random() < 0.7:
+                bm.fork(3 * i, 3 * i + j)
+                live.append(3 * i + j)
+    return bm, live, rng
+
+
+@pytest.mark.parametrize("seed", [3, 4, 5])
+def test_prepare_decode_equals_per_sequence_appends(seed):
+    """A batch call gives the same slots, tables, lengths and copy pairs as
+    append_slot / block_table / length called per sequence in the same order on
+    an identical manager, over several steps with forks sharing blocks."""
+    a, live, rng = _scenario(seed)
+    b, _, _ = _scenario(seed)
+    width = 24
+    for step in range(20):
+        order = [int(s) for s in rng.permutation(live)]
+        tables, lens, slots, pairs = a.prepare_decode(order, width)
+        exp_pairs = []
+        for r, s in enumerate(order):
+            slot, src, dst = b.append_slot(s)
+            assert slots[r] == slot and lens[r] == b.length(s)
+            t = b.block_table(s)
+            assert (tables[r, :len(t)] == t).all() and (tables[r, len(t):] == 0).all()
+            if src >= 0:
+                exp_pairs.append((src, dst))
+        assert pairs.tolist() == [list(p) for p in exp_pairs]
+        # The outputs meet tv_copy_blocks' and the fused append's preconditions.
+        dsts = pairs[:, 1].tolist()
+        assert len(set(dsts)) == len(dsts) and not set(dsts) & set(pairs[:, 0].tolist())
+        for r, s in enumerate(order):
+            assert a.refcount(int(slots[r] // BS)) == 1
+            assert slots[r] == tables[r, (lens[r] - 1) // BS] * BS + (lens[r] - 1) % BS
+        assert _state(a, range(25), 96) == _state(b, range(25), 96)
+
+
+def test_prepare_decode_rolls_back_when_blocks_run_out():
+    bm = tv.BlockManager(10, BS, 8, 8)
+    bm.add_sequence(0, 20)            # blocks 0, 1 (4 tokens in block 1)
+    bm.fork(0, 1)
+    bm.fork(0, 2)
+    bm.add_sequence(3, 32)            # blocks 2, 3: position 32 opens a block
+    bm.add_sequence(4, 80)            # blocks 4..8: one block left free
+    before = _state(bm, range(8), 10)
+    order_before = _free_order(bm, 10, 7)
+    # Needs: seq 1 copy, seq 2 copy, seq 3 new block, seq 0 in place -> 3 blocks, 1 free.
+    free = bm.num_free()
+    assert free < 3
+    for order in ([1, 2, 3, 0], [3, 1, 2]):      # undo a copy / a new block
+        with pytest.raises(tv.TvError) as e:
+            bm.prepare_decode(order, 8)
+        assert e.value.status == 6
+        assert _state(bm, range(8), 10) == before
+        assert _free_order(bm, 10, 7) == order_before
+    # The same step succeeds once blocks are returned.
+    bm.free_sequence(4)
+    tables, lens, slots, pairs = bm.prepare_decode([1, 2, 3, 0], 8)
+    assert len(pairs) == 2 and lens.tolist() == [21, 21, 33, 21]
+
+
+def test_prepare_decode_argument_errors_change_nothing():
+    bm = tv.BlockManager(16, BS, 4, 3)
+    bm.add_sequence(0, 16)
+    bm.add_sequence(1, 48)            # 3 blocks: its next position needs a 4th
+    before = _state(bm, range(4), 16)
+    for seqs, width in (([0, 0], 3),      # repeated sequence
+                        ([0, 2], 3),      # unused sequence
+                        ([0, 9], 3),      # out of range
+                        ([0], 1),         # 2 blocks after the append > width 1
+                        ([1], 8)):        # 4 blocks > max_blocks_per_seq 3
+        with pytest.raises(tv.TvError) as e:
+            bm.prepare_decode(seqs, width)
+        assert e.value.status == 2, (seqs, width)
+        assert _state(bm, range(4), 16) == before
+    tables, lens, slots, pairs = bm.prepare_decode([], 3)
+    assert tables.shape == (0, 3) and len(pairs) == 0

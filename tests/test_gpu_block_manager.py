@@ -2,8 +2,9 @@
 
 * tv_copy_blocks against the oracle's block copy: whole pools bit-exact.
 * Prompts are prefilled, each forked into four samples that share the prompt's
-  blocks, then several decode steps run. Each step asks the manager for slots,
-  copies shared blocks on write (tv_copy_blocks), and runs the two-launch step.
+  blocks, then several decode steps run. Each step asks the manager for slots
+  (per sequence, or with one tv_bm_prepare_decode call), copies shared blocks
+  on write (tv_copy_blocks), and runs the two-launch step.
   After every step:
   - each live sequence's K/V, gathered from the GPU pools through its own
     block table, equals that sequence's token history bit for bit;
@@ -71,7 +72,8 @@ def _gather(kc, vc, slots):
     return k, v
 
 
-def test_parallel_sampling_live(dev, oracle_lib):
+@pytest.mark.parametrize("batch_call", [False, True], ids=["per-sequence", "prepare_decode"])
+def test_parallel_sampling_live(dev, oracle_lib, batch_call):
     import torch
     import paged_kv_cache_tv_amd as tv
     rng = np.random.default_rng(51)
@@ -97,23 +99,28 @@ def test_parallel_sampling_live(dev, oracle_lib):
                 del hist[4 * i + 3]
         live = sorted(hist)
         S = len(live)
-        slots, pairs = [], []
         k_new, v_new = _bf16(rng, (S, HKV, D)), _bf16(rng, (S, HKV, D))
+        if batch_call:
+            tables, lens, slots, pairs = bm.prepare_decode(live, WIDTH)
+            pairs = [tuple(p) for p in pairs.tolist()]
+        else:
+            slots, pairs = [], []
+            for seq in live:
+                slot, src, dst = bm.append_slot(seq)
+                slots.append(slot)
+                if src >= 0:
+                    pairs.append((src, dst))
+            lens = np.array([bm.length(s) for s in live], np.int32)
+            tables = np.zeros((S, WIDTH), np.int32)
+            for r, seq in enumerate(live):
+                t = bm.block_table(seq)
+                tables[r, :len(t)] = t
         for r, seq in enumerate(live):
-            slot, src, dst = bm.append_slot(seq)
-            slots.append(slot)
-            if src >= 0:
-                pairs.append((src, dst))
             k, v = hist[seq]
             hist[seq] = (np.concatenate([k, k_new[r:r + 1]]), np.concatenate([v, v_new[r:r + 1]]))
         copies_seen += len(pairs)
         if pairs:
             tv.copy_blocks(kc, vc, _to_dev(np.array(pairs, np.int64), dev))
-        lens = np.array([bm.length(s) for s in live], np.int32)
-        tables = np.zeros((S, WIDTH), np.int32)
-        for r, seq in enumerate(live):
-            t = bm.block_table(seq)
-            tables[r, :len(t)] = t
         q = _bf16(rng, (S, HQ, D))
         max_ctx = int(lens.max())
         ws = tv.new_workspace(S, HQ, D, max_ctx, 512, dev)
