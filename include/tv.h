@@ -228,6 +228,48 @@ tv_status tv_paged_attention_reduce(float *out, const float *part_acc,
                                     void *stream);
 
 /*
+ * Prefill and chunked prefill ("tiny-vLLM으로 처음부터 고성능 LLM 추론 엔진
+ * 구축하기" page, section "고급 추론 개념": prefill runs the whole prompt,
+ * decode only the newest token; "tiny-vllm 씹뜯맛즐 - (1)" page, section 1:
+ * causal decoder; "vLLM" page: paged K/V and Flash Attention's online softmax).
+ *
+ * Sequence s brings m = query_start[s+1] - query_start[s] query rows, q rows
+ * query_start[s] .. query_start[s+1]-1, which are the last m positions of its
+ * n = context_lens[s] cached positions (the chunk's own K/V already written,
+ * e.g. by tv_cache_write).  Row query_start[s] + i sits at position
+ * p = n - m + i and, for every query head h (K/V head h / (num_q_heads /
+ * num_kv_heads)):
+ *     out[row][h][:] = softmax over t <= p of (scale * q[row][h] . K_t) applied to V_t.
+ * A full prefill is m = n; m = 1 is a decode step.  Rows with p < 0 (a chunk
+ * longer than the context) are 0.
+ *
+ *   out           float [rows][num_q_heads][head_dim], 16-byte aligned
+ *   q             bf16  [rows][num_q_heads][head_dim], 16-byte aligned
+ *   query_start   int32 [num_seqs + 1], non-decreasing (device)
+ *   k_cache, v_cache, block_tables, context_lens   as for the decode call
+ *   max_query_len    host-side upper bound of the m; rows i >= max_query_len
+ *                    of a sequence are not written
+ *   max_context_len  host-side upper bound of context_lens, <= max_blocks_per_seq * block_size
+ *
+ * Supported shapes: head_dim == 64, block_size == 16, num_q_heads /
+ * num_kv_heads in {1, 2, 4, 8, 16}.  Arithmetic: bf16 products accumulated
+ * in fp32, softmax weights rounded to bf16 for the product with V.
+ * Odd device data as for the decode call: context lengths are clamped to
+ * [0, max_context_len], table entries outside [0, num_blocks) drop their
+ * tokens (a row left with no token is 0), positions >= n are never read.
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED, TV_ERR_ALIGNMENT,
+ * TV_ERR_HIP.  num_seqs == 0 or max_query_len == 0 is a no-op.
+ */
+tv_status tv_paged_attention_prefill(float *out, const uint16_t *q, const int32_t *query_start,
+                                     const uint16_t *k_cache, const uint16_t *v_cache,
+                                     const int32_t *block_tables, const int32_t *context_lens,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size,
+                                     int32_t max_blocks_per_seq, int64_t num_blocks,
+                                     int32_t max_query_len, int32_t max_context_len, float scale,
+                                     void *stream);
+
+/*
  * Copy-on-write support ("vLLM" page, section "가상 메모리 방식의 해결":
  * requests sharing a prompt share its blocks; a block is copied when a branch
  * writes into it).

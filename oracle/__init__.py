@@ -1,4 +1,4 @@
-"""CPU oracle for the paged GQA decode step -- TEST INFRASTRUCTURE.
+"""CPU oracle for paged GQA attention (decode, prefill, block copy) -- TEST INFRASTRUCTURE.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` import this package.  It wraps ``liboracle.so`` (built from
@@ -17,6 +17,10 @@ Parity status of each function (pins live in ``tests/test_oracle.py`` and
                            example).
   * ``copy_blocks``     -- pinned (hand-derived literal pools; skip rules;
                            refused conflicting pairs).
+  * ``paged_prefill``   -- pinned (torch SDPA with a causal mask on full
+                           prompts, chunking invariance, one row per sequence
+                           equals decode, first position equals V_0, block
+                           permutation, rows past the context).
 """
 
 from __future__ import annotations
@@ -64,6 +68,11 @@ class Oracle:
                                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_long, ctypes.c_double, ctypes.c_int]
+        lib.oracle_paged_prefill.restype = ctypes.c_int
+        lib.oracle_paged_prefill.argtypes = [_f64p, _u16p, _i32p, _u16p, _u16p, _i32p, _i32p,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_long, ctypes.c_double, ctypes.c_int]
         lib.oracle_copy_blocks.restype = ctypes.c_long
         lib.oracle_copy_blocks.argtypes = [_u16p, _u16p, _i64p, ctypes.c_long, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_long]
@@ -137,6 +146,31 @@ class Oracle:
                                             bt.shape[1], nb, float(scale), threads)
         if r != 0:
             raise ValueError("oracle_paged_attention rejected its arguments")
+        return out
+
+    def paged_prefill(self, q: np.ndarray, query_start: np.ndarray, k_cache: np.ndarray,
+                      v_cache: np.ndarray, block_tables: np.ndarray, context_lens: np.ndarray,
+                      scale: float, num_threads: Optional[int] = None) -> np.ndarray:
+        """Causal attention of the query rows of every sequence (rows
+        query_start[s] .. query_start[s+1]-1, the last positions of its context)
+        over its cached context; float64 [rows, Hq, D]."""
+        q = np.ascontiguousarray(q, np.uint16)
+        qs = np.ascontiguousarray(query_start, np.int32)
+        bt = np.ascontiguousarray(block_tables, np.int32)
+        cl = np.ascontiguousarray(context_lens, np.int32)
+        T, hq, d = q.shape
+        S = cl.shape[0]
+        nb, hkv, dc, bs, x = k_cache.shape
+        assert x == 8 and dc * x == d and v_cache.shape == (nb, hkv, d, bs)
+        assert qs.shape == (S + 1,) and qs[S] <= T and bt.ndim == 2 and bt.shape[0] == S
+        out = np.zeros((T, hq, d), np.float64)
+        threads = cpu_count() if num_threads is None else int(num_threads)
+        r = self.lib.oracle_paged_prefill(_ptr(out, _f64p), _ptr(q, _u16p), _ptr(qs, _i32p),
+                                          _ptr(k_cache, _u16p), _ptr(v_cache, _u16p),
+                                          _ptr(bt, _i32p), _ptr(cl, _i32p), S, hq, hkv, d, bs,
+                                          max(bt.shape[1], 1), nb, float(scale), threads)
+        if r != 0:
+            raise ValueError("oracle_paged_prefill rejected its arguments")
         return out
 
     def max_threads(self) -> int:

@@ -1,5 +1,6 @@
 /*
- * oracle.c -- plain, slow CPU reference for one paged GQA decode step.
+ * oracle.c -- plain, slow CPU reference for paged GQA attention (decode step,
+ * prefill / chunked prefill, block copy).
  *
  * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg load this library.  The GPU library never
@@ -162,6 +163,68 @@ long oracle_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int64_t *pai
 }
 
 /*
+ * o[d] = softmax over t < count of scale * qv . K_t, applied to V_t, for K/V
+ * head g of sequence s, with K_t and V_t read from the pools through the
+ * sequence's table row.  count = 0 gives a zero row.  Returns 0, or 1 if host
+ * memory ran out.
+ */
+static int attend(double *o, const double *qv, const uint16_t *k_cache, const uint16_t *v_cache,
+                  const int32_t *table_row, int g, int count, int num_kv_heads, int head_dim,
+                  int block_size, double scale)
+{
+    for (int d = 0; d < head_dim; ++d)
+        o[d] = 0.0;
+    if (count == 0)
+        return 0;
+    double *score = malloc(sizeof(double) * (size_t)count);
+    if (!score)
+        return 1;
+
+    /* S = scale * q K^T over the positions, gathered through the table. */
+    for (int t = 0; t < count; ++t) {
+        long blk = table_row[t / block_size];
+        long off = t % block_size;
+        double dot = 0.0;
+        for (int d = 0; d < head_dim; ++d)
+            dot += qv[d] * bf16_value(k_cache[k_index(blk, g, off, d, num_kv_heads, head_dim,
+                                                      block_size)]);
+        score[t] = scale * dot;
+    }
+
+    /* P = softmax(S): subtract the maximum, exponentiate, normalise. */
+    double m = score[0];
+    for (int t = 1; t < count; ++t)
+        if (score[t] > m)
+            m = score[t];
+    double l = 0.0;
+    for (int t = 0; t < count; ++t) {
+        score[t] = exp(score[t] - m);
+        l += score[t];
+    }
+
+    /* O = P V. */
+    for (int t = 0; t < count; ++t) {
+        long blk = table_row[t / block_size];
+        long off = t % block_size;
+        const uint16_t *vtile = v_cache + (blk * num_kv_heads + g) * (long)head_dim * block_size;
+        double p = score[t] / l;
+        for (int d = 0; d < head_dim; ++d)
+            o[d] += p * bf16_value(vtile[(long)d * block_size + off]);
+    }
+    free(score);
+    return 0;
+}
+
+/* Every table entry a context of n tokens uses lies in the pool. */
+static int table_ok(const int32_t *table_row, int n, int block_size, long num_blocks)
+{
+    for (int b = 0; b < (n + block_size - 1) / block_size; ++b)
+        if (table_row[b] < 0 || table_row[b] >= num_blocks)
+            return 0;
+    return 1;
+}
+
+/*
  * out[s][h][d] (double, [S][Hq][D]) = softmax over t < n of
  * scale * q[s][h] . K_t, applied to V_t, with K_t, V_t read from the pools
  * through block_tables (int32 [S][max_blocks]) and n = context_lens[s].
@@ -181,13 +244,9 @@ int oracle_paged_attention(double *out, const uint16_t *q,
         return -1;
     for (int s = 0; s < num_seqs; ++s) {
         int n = context_lens[s];
-        if (n < 0 || n > max_blocks * block_size)
+        if (n < 0 || n > max_blocks * block_size ||
+            !table_ok(block_tables + (long)s * max_blocks, n, block_size, num_blocks))
             return -1;
-        for (int b = 0; b < (n + block_size - 1) / block_size; ++b) {
-            int32_t phys = block_tables[(long)s * max_blocks + b];
-            if (phys < 0 || phys >= num_blocks)
-                return -1;
-        }
     }
     const int group = num_q_heads / num_kv_heads;
     const long pairs = (long)num_seqs * num_q_heads;
@@ -202,58 +261,89 @@ int oracle_paged_attention(double *out, const uint16_t *q,
         const int s = (int)(pair / num_q_heads);
         const int h = (int)(pair % num_q_heads);
         const int g = h / group;                      /* the K/V head this query head reads */
-        const int n = context_lens[s];
-        double *o = out + pair * head_dim;
-        for (int d = 0; d < head_dim; ++d)
-            o[d] = 0.0;
-        if (n == 0)
-            continue;
-
-        double *score = malloc(sizeof(double) * (size_t)n);
         double *qv = malloc(sizeof(double) * (size_t)head_dim);
-        if (!score || !qv) {
-            free(score);
-            free(qv);
+        if (!qv) {
             bad = 1;
             continue;
         }
         for (int d = 0; d < head_dim; ++d)
             qv[d] = bf16_value(q[pair * head_dim + d]);
-
-        /* S = scale * q K^T over the n cached positions, gathered through the table. */
-        for (int t = 0; t < n; ++t) {
-            long blk = block_tables[(long)s * max_blocks + t / block_size];
-            long off = t % block_size;
-            double dot = 0.0;
-            for (int d = 0; d < head_dim; ++d)
-                dot += qv[d] * bf16_value(k_cache[k_index(blk, g, off, d, num_kv_heads, head_dim,
-                                                          block_size)]);
-            score[t] = scale * dot;
-        }
-
-        /* P = softmax(S): subtract the maximum, exponentiate, normalise. */
-        double m = score[0];
-        for (int t = 1; t < n; ++t)
-            if (score[t] > m)
-                m = score[t];
-        double l = 0.0;
-        for (int t = 0; t < n; ++t) {
-            score[t] = exp(score[t] - m);
-            l += score[t];
-        }
-
-        /* O = P V. */
-        for (int t = 0; t < n; ++t) {
-            long blk = block_tables[(long)s * max_blocks + t / block_size];
-            long off = t % block_size;
-            const uint16_t *vtile = v_cache + (blk * num_kv_heads + g) * (long)head_dim * block_size;
-            double p = score[t] / l;
-            for (int d = 0; d < head_dim; ++d)
-                o[d] += p * bf16_value(vtile[(long)d * block_size + off]);
-        }
-        free(score);
+        bad |= attend(out + pair * head_dim, qv, k_cache, v_cache,
+                      block_tables + (long)s * max_blocks, g, context_lens[s], num_kv_heads,
+                      head_dim, block_size, scale);
         free(qv);
     }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Prefill and chunked prefill ("tiny-vLLM으로 처음부터 고성능 LLM 추론 엔진
+ * 구축하기" page, section "고급 추론 개념": prefill runs the whole prompt,
+ * decode only the newest token; "tiny-vllm 씹뜯맛즐 - (1)" page, section 1:
+ * each position attends to itself and the positions before it).
+ *
+ * Sequence s owns query rows query_start[s] .. query_start[s+1]-1 (m rows of
+ * q, [rows][Hq][D]).  Its context holds n = context_lens[s] positions, the
+ * chunk's own tokens being the last m of them (already in the pools).  Row
+ * query_start[s] + i sits at position p = n - m + i and attends to positions
+ * 0..p:
+ *     out[row][h][:] = softmax over t <= p of scale * q[row][h] . K_t, applied to V_t.
+ * A row with p < 0 (a chunk longer than the context) is zero.  A full prefill
+ * is m = n; a decode step is m = 1.
+ * Returns 0, or -1 on a bad argument (query_start decreasing or negative, a
+ * context longer than the table, a table entry outside the pool).
+ */
+int oracle_paged_prefill(double *out, const uint16_t *q, const int32_t *query_start,
+                         const uint16_t *k_cache, const uint16_t *v_cache,
+                         const int32_t *block_tables, const int32_t *context_lens,
+                         int num_seqs, int num_q_heads, int num_kv_heads,
+                         int head_dim, int block_size, int max_blocks,
+                         long num_blocks, double scale, int num_threads)
+{
+    if (num_seqs < 0 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
+        head_dim < 1 || head_dim % KCHUNK != 0 || block_size < 1 || max_blocks < 1 ||
+        num_blocks < 1 || query_start[0] < 0)
+        return -1;
+    for (int s = 0; s < num_seqs; ++s) {
+        int n = context_lens[s];
+        if (query_start[s + 1] < query_start[s] || n < 0 || n > max_blocks * block_size ||
+            !table_ok(block_tables + (long)s * max_blocks, n, block_size, num_blocks))
+            return -1;
+    }
+    const long rows = query_start[num_seqs];
+    int *seq_of_row = malloc(sizeof(int) * (size_t)(rows > 0 ? rows : 1));
+    if (!seq_of_row)
+        return -1;
+    for (int s = 0; s < num_seqs; ++s)
+        for (long r = query_start[s]; r < query_start[s + 1]; ++r)
+            seq_of_row[r] = s;
+    const int group = num_q_heads / num_kv_heads;
+    int bad = 0;
+
+#ifdef _OPENMP
+    if (num_threads < 1)
+        num_threads = 1;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(num_threads) reduction(| : bad)
+#endif
+    for (long pair = (long)query_start[0] * num_q_heads; pair < rows * num_q_heads; ++pair) {
+        const long row = pair / num_q_heads;
+        const int h = (int)(pair % num_q_heads);
+        const int s = seq_of_row[row];
+        const int m = query_start[s + 1] - query_start[s];
+        const int p = context_lens[s] - m + (int)(row - query_start[s]);
+        double *qv = malloc(sizeof(double) * (size_t)head_dim);
+        if (!qv) {
+            bad = 1;
+            continue;
+        }
+        for (int d = 0; d < head_dim; ++d)
+            qv[d] = bf16_value(q[pair * head_dim + d]);
+        bad |= attend(out + pair * head_dim, qv, k_cache, v_cache,
+                      block_tables + (long)s * max_blocks, h / group, p >= 0 ? p + 1 : 0,
+                      num_kv_heads, head_dim, block_size, scale);
+        free(qv);
+    }
+    free(seq_of_row);
     return bad ? -1 : 0;
 }
 

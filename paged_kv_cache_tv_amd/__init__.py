@@ -1,16 +1,18 @@
-"""MI355X-native paged GQA decode attention: libtv (HIP, gfx950) and its Python binding.
+"""MI355X-native paged GQA attention: libtv (HIP, gfx950) and its Python binding.
 
 The three steps of one decode step -- cache write, partitioned paged attention,
-log-sum-exp merge -- run in the HIP kernels of ``libtv.so``; this package only
+log-sum-exp merge --, prefill / chunked-prefill attention, copy-on-write block
+copies and the host block manager run in ``libtv.so``; this package only
 marshals torch tensors into the C calls declared in ``include/tv.h``.
 """
 
 from .binding import (LIB_PATH, BlockManager, TvError, cache_write, copy_blocks, lib,
                       load_library, new_pools,
                       new_workspace, num_partitions, paged_attention, paged_attention_decode,
-                      paged_attention_decode_append, paged_attention_reduce)
+                      paged_attention_decode_append, paged_attention_prefill,
+                      paged_attention_reduce)
 
 __all__ = ["LIB_PATH", "BlockManager", "TvError", "cache_write", "copy_blocks", "lib",
            "load_library", "new_pools",
            "new_workspace", "num_partitions", "paged_attention", "paged_attention_decode",
-           "paged_attention_decode_append", "paged_attention_reduce"]
+           "paged_attention_decode_append", "paged_attention_prefill", "paged_attention_reduce"]

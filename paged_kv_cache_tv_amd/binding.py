@@ -53,6 +53,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                      f32, vp]
     lib.tv_paged_attention_reduce.restype = ctypes.c_int
     lib.tv_paged_attention_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.tv_paged_attention_prefill.restype = ctypes.c_int
+    lib.tv_paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                               i32, i32, i64, i32, i32, ctypes.c_float, vp]
     lib.tv_copy_blocks.restype = ctypes.c_int
     lib.tv_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, vp]
     i32p, i64p = ctypes.POINTER(i32), ctypes.POINTER(i64)
@@ -195,6 +198,33 @@ def paged_attention_decode(part_acc, part_max, part_sum, q, k_cache, v_cache, bl
         S, hq, hkv, d, bs, block_tables.shape[1], nb, int(max_context_len), int(partition_size),
         float(scale), _stream_handle(stream, q.device))
     _check("tv_paged_attention_decode", st)
+
+
+def paged_attention_prefill(out, q, query_start, k_cache, v_cache, block_tables, context_lens,
+                            max_query_len: int, max_context_len: int, scale: float,
+                            stream=None) -> None:
+    """tv_paged_attention_prefill.  q, out: [rows, Hq, D] (bf16 / float32);
+    query_start: int32 [S + 1]; block_tables: int32 [S, max_blocks];
+    context_lens: int32 [S]."""
+    import torch
+    _need(q, "q", itemsize=2, ndim=3)
+    _need(out, "out", dtype=torch.float32, ndim=3)
+    _need(query_start, "query_start", dtype=torch.int32, ndim=1)
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    rows, hq, d = q.shape
+    nb, hkv, bs, d2 = _pool_dims(k_cache, v_cache)
+    if d2 != d or tuple(out.shape) != (rows, hq, d):
+        raise ValueError("out, q and the cache must agree on [rows, Hq, D]")
+    S = context_lens.shape[0]
+    if query_start.shape[0] != S + 1 or block_tables.shape[0] != S:
+        raise ValueError("query_start must have S + 1 entries and block_tables S rows")
+    st = lib().tv_paged_attention_prefill(
+        out.data_ptr(), q.data_ptr(), query_start.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, hq, hkv, d, bs,
+        block_tables.shape[1], nb, int(max_query_len), int(max_context_len), float(scale),
+        _stream_handle(stream, q.device))
+    _check("tv_paged_attention_prefill", st)
 
 
 def paged_attention_decode_append(part_acc, part_max, part_sum, q, k_new, v_new, slot_mapping,

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtv.so")
 
-SOURCES = ["cache_write.hip", "paged_decode.hip", "paged_reduce.hip", "block_copy.hip", "tv_api.cpp",
+SOURCES = ["cache_write.hip", "paged_decode.hip", "paged_reduce.hip", "block_copy.hip",
+           "paged_prefill.hip", "tv_api.cpp",
            "block_manager.cpp"]
 ARCH = "gfx950"
 # Packed-FP32 VALU forms are switched off for all device code.

@@ -180,6 +180,59 @@ tv_status tv_paged_attention_decode_append(float *part_acc, float *part_max, flo
     return from_hip(tv::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+tv_status tv_paged_attention_prefill(float *out, const uint16_t *q, const int32_t *query_start,
+                                     const uint16_t *k_cache, const uint16_t *v_cache,
+                                     const int32_t *block_tables, const int32_t *context_lens,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size,
+                                     int32_t max_blocks_per_seq, int64_t num_blocks,
+                                     int32_t max_query_len, int32_t max_context_len, float scale,
+                                     void *stream)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_query_len < 0 ||
+        max_context_len < 0)
+        return TV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0)
+        return TV_ERR_SHAPE;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+        return TV_ERR_SHAPE;
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return TV_ERR_SHAPE;
+    const int32_t group = num_q_heads / num_kv_heads;
+    if (head_dim != tv::kHeadDim || block_size != tv::kBlockSize ||
+        (group != 1 && group != 2 && group != 4 && group != 8 && group != 16))
+        return TV_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || max_query_len == 0)
+        return TV_OK;
+    if (!out || !q || !query_start || !k_cache || !v_cache || !block_tables || !context_lens)
+        return TV_ERR_NULL;
+    const int64_t rows_per_wg = 256 / group;
+    if ((int64_t)num_kv_heads * num_seqs * ceil_div(max_query_len, rows_per_wg) > 0x7fffffff)
+        return TV_ERR_UNSUPPORTED;
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(query_start, 4) ||
+        !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_tables, 4) ||
+        !aligned(context_lens, 4))
+        return TV_ERR_ALIGNMENT;
+    tv::PrefillArgs a{};
+    a.out = out;
+    a.q = q;
+    a.query_start = query_start;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.group = group;
+    a.max_blocks = max_blocks_per_seq;
+    a.max_query_len = max_query_len;
+    a.max_context_len = max_context_len;
+    a.num_blocks = num_blocks;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);   // log2(e)
+    return from_hip(tv::launch_paged_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
 tv_status tv_paged_attention_reduce(float *out, const float *part_acc, const float *part_max,
                                     const float *part_sum, const int32_t *context_lens,
                                     int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,

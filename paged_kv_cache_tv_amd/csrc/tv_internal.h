@@ -66,6 +66,24 @@ struct ReduceArgs {
     int32_t max_context_len;
 };
 
+struct PrefillArgs {
+    float *out;                 // [rows][num_q_heads][head_dim]
+    const uint16_t *q;          // [rows][num_q_heads][head_dim]
+    const int32_t *query_start; // [num_seqs + 1]
+    const uint16_t *k_cache;
+    const uint16_t *v_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    int32_t num_seqs;
+    int32_t num_kv_heads;
+    int32_t group;              // query heads per K/V head: 1, 2, 4, 8 or 16
+    int32_t max_blocks;         // row stride of block_tables
+    int32_t max_query_len;
+    int32_t max_context_len;
+    int64_t num_blocks;
+    float scale_log2;           // scale * log2(e)
+};
+
 struct BlockCopyArgs {
     uint16_t *k_cache;
     uint16_t *v_cache;
@@ -77,6 +95,7 @@ struct BlockCopyArgs {
 
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream);
 hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t stream);
+hipError_t launch_paged_prefill(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_paged_reduce(const ReduceArgs &a, hipStream_t stream);
 

@@ -378,3 +378,114 @@ def make_workload(index: int) -> DecodeBatch:
         return _independent(_rng(1005), 1005, lens, name="decode-b4-ctx32k-128k",
                             k_outlier_period=97, k_outlier_factor=8.0)
     raise ValueError("workload index must be 1..5")
+
+
+# --------------------------------------------------------------------------- prefill
+
+
+@dataclass
+class PrefillBatch:
+    """One prefill (or chunked-prefill) step.
+
+    Sequence ``s`` has ``prior_lens[s]`` positions already cached and a chunk of
+    ``query_lens[s]`` new tokens at the positions after them, so its context
+    holds ``context_lens[s] = prior + chunk`` positions once the step has
+    written the chunk.  ``q`` holds one row ``[Hq, D]`` per chunk token,
+    sequence by sequence (rows ``query_start[s] .. query_start[s+1]-1``).
+    Pools, tables and the K/V rows of every position come from ``base``.
+    """
+
+    name: str
+    base: DecodeBatch
+    prior_lens: np.ndarray            # int32 [S]
+    query_lens: np.ndarray            # int32 [S]
+    query_start: np.ndarray           # int32 [S + 1]
+    q: np.ndarray                     # uint16 [T, Hq, D]
+
+    @property
+    def num_seqs(self) -> int:
+        return self.base.num_seqs
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def context_lens(self) -> np.ndarray:
+        return self.base.context_lens
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max()) if self.num_seqs else 0
+
+    def _positions(self, chunk: bool):
+        k, v, slots = [], [], []
+        b = self.base
+        for s in range(self.num_seqs):
+            lo, hi = (int(self.prior_lens[s]), int(b.context_lens[s])) if chunk else \
+                (0, int(self.prior_lens[s]))
+            pos = np.arange(lo, hi)
+            rows = b.token_rows[s][pos]
+            k.append(b.kv_k[rows])
+            v.append(b.kv_v[rows])
+            slots.append(_slots_for(b.block_tables[s], pos, b.block_size))
+        return (np.concatenate(k), np.concatenate(v), np.concatenate(slots).astype(np.int64))
+
+    def prior_inputs(self):
+        """(k, v, slot_mapping) of the positions cached before the step."""
+        return self._positions(chunk=False)
+
+    def chunk_inputs(self):
+        """(k, v, slot_mapping) of the chunk's tokens, in q row order (the step writes these)."""
+        return self._positions(chunk=True)
+
+    def causal_flops(self) -> int:
+        """Multiply-adds x 2 of QK^T and PV over the (query, key) pairs the causal
+        mask keeps: row i of sequence s at position p = n - m + i sees p + 1 keys."""
+        pairs = 0
+        for s in range(self.num_seqs):
+            n, m = int(self.context_lens[s]), int(self.query_lens[s])
+            p = np.arange(n - m, n, dtype=np.int64)
+            pairs += int(np.maximum(p + 1, 0).sum())
+        b = self.base
+        return pairs * b.num_q_heads * 4 * b.head_dim
+
+
+def make_prefill_batch(prior_lens: Sequence[int], query_lens: Sequence[int], seed: int, *,
+                       name: str = "prefill-custom", q_sigma: float = 1.0,
+                       **kw) -> PrefillBatch:
+    """Independent sequences of ``prior + chunk`` positions (K/V, tables and pool
+    drawn as by ``make_batch``), then the chunk's query rows [T, Hq, D] from the
+    same generator."""
+    prior = np.asarray(prior_lens, np.int64)
+    ql = np.asarray(query_lens, np.int64)
+    if prior.shape != ql.shape or (prior < 0).any() or (ql < 0).any():
+        raise ValueError("prior_lens and query_lens: same length, non-negative")
+    rng = _rng(seed)
+    base = _independent(rng, seed, prior + ql, **kw)
+    qs = np.zeros(len(ql) + 1, np.int32)
+    qs[1:] = np.cumsum(ql)
+    q = _draw_bf16(rng, (int(qs[-1]), base.num_q_heads, base.head_dim), q_sigma)
+    return PrefillBatch(name=name, base=base, prior_lens=prior.astype(np.int32),
+                        query_lens=ql.astype(np.int32), query_start=qs, q=q)
+
+
+PREFILL_WORKLOADS = {
+    1: "3 prompts of 37, 100 and 300 tokens, full prefill",
+    2: "8 sequences: chunk U[1,512] on top of U[0,2048] cached positions",
+    3: "8 prompts of 2048 tokens, full prefill",
+}
+
+
+def make_prefill_workload(index: int) -> PrefillBatch:
+    """Build one of the seeded prefill workloads (1-based index)."""
+    if index == 1:
+        return make_prefill_batch([0, 0, 0], [37, 100, 300], 2001, name="prefill-b3-37-100-300")
+    if index == 2:
+        rng = _rng(2002)
+        prior = rng.integers(0, 2048, size=8, endpoint=True)
+        chunk = rng.integers(1, 512, size=8, endpoint=True)
+        return make_prefill_batch(prior, chunk, 2002, name="prefill-b8-chunk1-512-ctx0-2048")
+    if index == 3:
+        return make_prefill_batch([0] * 8, [2048] * 8, 2003, name="prefill-b8-prompt2048")
+    raise ValueError("prefill workload index must be 1..3")

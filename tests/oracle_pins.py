@@ -13,7 +13,11 @@ the oracle disagrees with:
   * the pages' worked paging example (300 tokens -> 19 blocks) and the GQA
     grouping figure, stored under tests/golden/ with their citations;
   * a hand-derived literal cache layout (tests/golden/cache_layout_tiny.json)
-    and a hand-derived literal block copy (tests/golden/block_copy_tiny.json).
+    and a hand-derived literal block copy (tests/golden/block_copy_tiny.json);
+  * for prefill: torch SDPA with its own causal mask on full prompts and with
+    a bottom-right mask on chunks, chunking invariance, single rows equal to
+    the decode oracle, position 0 equal to V_0, rows before the context,
+    block permutation.
 
 Run as a script (``python tests/oracle_pins.py LIB``) it executes every pin
 against the oracle library LIB and prints one line per pin: the mutation test
@@ -370,11 +374,146 @@ def pin_block_copy_literal(orc):
     assert np.array_equal(kc2, kc) and np.array_equal(vc2, vc), "refused copy touched the pools"
 
 
+# ------------------------------------------------------------------ prefill pins
+
+
+def _prefill(orc, pb, num_threads=2):
+    """Pools holding every position of the prefill batch (prior and chunk, written
+    by the oracle's own cache write) and the oracle's prefill output."""
+    kc, vc = O.Oracle.new_pools(pb.base.num_blocks, pb.base.num_kv_heads, pb.base.head_dim,
+                                pb.base.block_size)
+    for k, v, sl in (pb.prior_inputs(), pb.chunk_inputs()):
+        orc.cache_write(k, v, kc, vc, sl)
+    out = orc.paged_prefill(pb.q, pb.query_start, kc, vc, pb.base.block_tables,
+                            pb.context_lens, pb.base.scale, num_threads)
+    return out, kc, vc
+
+
+def _sdpa_prefill_reference(pb):
+    """torch SDPA (float64, grouped K/V heads) per sequence on the unpaged data,
+    with a boolean mask: chunk row i (position n - m + i) may see key t iff
+    t <= n - m + i."""
+    import torch
+    import torch.nn.functional as F
+    b = pb.base
+    out = np.zeros((pb.num_rows, b.num_q_heads, b.head_dim))
+    for s in range(pb.num_seqs):
+        n, m, r0 = int(b.context_lens[s]), int(pb.query_lens[s]), int(pb.query_start[s])
+        if m == 0:
+            continue
+        k, v = b.logical_kv(s)
+        qt = torch.from_numpy(_f64(pb.q[r0:r0 + m])).permute(1, 0, 2)[None].contiguous()
+        kt = torch.from_numpy(_f64(k)).permute(1, 0, 2)[None].contiguous()
+        vt = torch.from_numpy(_f64(v)).permute(1, 0, 2)[None].contiguous()
+        mask = torch.arange(n)[None, :] <= (n - m + torch.arange(m))[:, None]
+        o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, enable_gqa=True)
+        out[r0:r0 + m] = o[0].permute(1, 0, 2).numpy()
+    return out
+
+
+def pin_prefill_sdpa_full_prompts(orc):
+    """Full prefill (chunk = whole prompt) == torch SDPA with is_causal=True, the
+    library's own causal mask, which is the right one when queries and keys
+    cover the same positions."""
+    import torch
+    import torch.nn.functional as F
+    pb = W.make_prefill_batch([0, 0, 0, 0], [1, 16, 37, 90], 31)
+    out, _, _ = _prefill(orc, pb)
+    b = pb.base
+    for s in range(pb.num_seqs):
+        m, r0 = int(pb.query_lens[s]), int(pb.query_start[s])
+        k, v = b.logical_kv(s)
+        qt = torch.from_numpy(_f64(pb.q[r0:r0 + m])).permute(1, 0, 2)[None].contiguous()
+        kt = torch.from_numpy(_f64(k)).permute(1, 0, 2)[None].contiguous()
+        vt = torch.from_numpy(_f64(v)).permute(1, 0, 2)[None].contiguous()
+        o = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True, enable_gqa=True)
+        err = np.abs(out[r0:r0 + m] - o[0].permute(1, 0, 2).numpy()).max()
+        assert err <= 1e-12, f"sequence {s}: SDPA causal mismatch {err}"
+
+
+def pin_prefill_sdpa_chunks(orc):
+    """Chunks on top of cached positions == torch SDPA with the bottom-right mask."""
+    pb = W.make_prefill_batch([0, 5, 40, 100, 17], [3, 20, 33, 1, 64], 32)
+    out, _, _ = _prefill(orc, pb)
+    err = np.abs(out - _sdpa_prefill_reference(pb)).max()
+    assert err <= 1e-12, f"SDPA chunk mismatch {err}"
+
+
+def pin_prefill_chunking_invariance(orc):
+    """A prompt run as one chunk and as several consecutive chunks gives the same
+    rows bit for bit (each chunk on the pools that hold the whole prompt)."""
+    pb = W.make_prefill_batch([0, 0], [70, 129], 33)
+    full, kc, vc = _prefill(orc, pb)
+    b = pb.base
+    for s, chunks in ((0, [30, 40]), (1, [16, 100, 13])):
+        done = 0
+        for m in chunks:
+            r = int(pb.query_start[s]) + done
+            out = orc.paged_prefill(pb.q[r:r + m], np.array([0, m], np.int32), kc, vc,
+                                    b.block_tables[s:s + 1], np.array([done + m], np.int32),
+                                    b.scale, 2)
+            assert np.array_equal(out, full[r:r + m]), f"sequence {s}, chunk at {done}"
+            done += m
+
+
+def pin_prefill_single_rows_are_decode(orc):
+    """One query row per sequence is a decode step: equal to the decode oracle,
+    which has pins of its own."""
+    pb = W.make_prefill_batch([0, 15, 64, 200], [1, 1, 1, 1], 34)
+    out, kc, vc = _prefill(orc, pb)
+    dec = orc.paged_attention(pb.q, kc, vc, pb.base.block_tables, pb.context_lens,
+                              pb.base.scale, 2)
+    assert np.array_equal(out, dec)
+
+
+def pin_prefill_first_position(orc):
+    """The row at position 0 sees one key, so its output is V_0 of its K/V head."""
+    pb = W.make_prefill_batch([0, 0], [5, 21], 35)
+    out, _, _ = _prefill(orc, pb)
+    b = pb.base
+    kv_of = _kv_of_head()
+    for s in range(2):
+        _, v = b.logical_kv(s)
+        row = out[int(pb.query_start[s])]
+        for h in range(b.num_q_heads):
+            assert np.array_equal(row[h], _f64(v[0, kv_of[h]])), f"sequence {s} head {h}"
+
+
+def pin_prefill_rows_before_context(orc):
+    """A chunk longer than the context: rows at negative positions are zero and
+    the rest equal the rows of the chunk that fits."""
+    pb = W.make_prefill_batch([0], [10], 36)
+    full, kc, vc = _prefill(orc, pb)
+    b = pb.base
+    q = np.concatenate([pb.q[:4], pb.q])                        # 14 rows, context 10
+    out = orc.paged_prefill(q, np.array([0, 14], np.int32), kc, vc, b.block_tables,
+                            np.array([10], np.int32), b.scale, 2)
+    assert not out[:4].any(), "rows before the context are not zero"
+    assert np.array_equal(out[4:], full)
+
+
+def pin_prefill_block_permutation(orc):
+    """Moving physical blocks (and rewriting the tables) leaves prefill bit-identical."""
+    pb = W.make_prefill_batch([3, 40], [30, 50], 37)
+    out, kc, vc = _prefill(orc, pb)
+    b = pb.base
+    perm = np.random.default_rng(98).permutation(b.num_blocks)
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm] = kc
+    vc2[perm] = vc
+    out2 = orc.paged_prefill(pb.q, pb.query_start, kc2, vc2, perm[b.block_tables].astype(np.int32),
+                             pb.context_lens, b.scale, 2)
+    assert np.array_equal(out, out2)
+
+
 ALL_PINS = [
     pin_contiguous_bruteforce, pin_torch_sdpa, pin_block_permutation, pin_single_token,
     pin_constant_v, pin_zero_query_mean, pin_gqa_figure, pin_one_dominant_key,
     pin_two_token_logistic, pin_score_shift, pin_paging_example, pin_cache_layout_literal,
     pin_cache_write_untouched, pin_empty, pin_thread_invariance, pin_block_copy_literal,
+    pin_prefill_sdpa_full_prompts, pin_prefill_sdpa_chunks, pin_prefill_chunking_invariance,
+    pin_prefill_single_rows_are_decode, pin_prefill_first_position,
+    pin_prefill_rows_before_context, pin_prefill_block_permutation,
 ]
 
 

@@ -132,6 +132,35 @@ def test_decode_append_validation(lib):
     assert _app(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
 
 
+def _pre(lib, S=2, hq=32, hkv=8, d=64, bs=16, mb=4, nb=8, mq=40, mctx=64, scale=0.125,
+         ptrs=(BAD,) * 7):
+    return lib.tv_paged_attention_prefill(*ptrs, S, hq, hkv, d, bs, mb, nb, mq, mctx, scale, None)
+
+
+def test_prefill_validation(lib):
+    assert _pre(lib, S=-1) == TV_ERR_SHAPE
+    assert _pre(lib, hq=30) == TV_ERR_SHAPE
+    assert _pre(lib, mq=-1) == TV_ERR_SHAPE
+    assert _pre(lib, mctx=65) == TV_ERR_SHAPE
+    assert _pre(lib, scale=0.0) == TV_ERR_SHAPE
+    assert _pre(lib, scale=float("inf")) == TV_ERR_SHAPE
+    assert _pre(lib, d=128) == TV_ERR_UNSUPPORTED
+    assert _pre(lib, bs=32, mb=2) == TV_ERR_UNSUPPORTED
+    assert _pre(lib, hq=24) == TV_ERR_UNSUPPORTED          # group 3
+    assert _pre(lib, hq=256) == TV_ERR_UNSUPPORTED         # group 32
+    assert _pre(lib, S=0) == TV_OK
+    assert _pre(lib, mq=0) == TV_OK
+    assert _pre(lib) == TV_ERR_ALIGNMENT
+    for i in range(7):
+        ptrs = [ALIGNED] * 7
+        ptrs[i] = None
+        assert _pre(lib, ptrs=tuple(ptrs)) == TV_ERR_NULL, i
+    for i, bad in ((0, 0x1004), (1, 0x1008), (2, 0x1002), (3, 0x1008)):   # out, q, query_start, k_cache
+        ptrs = [ALIGNED] * 7
+        ptrs[i] = bad
+        assert _pre(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT, i
+
+
 def _copy(lib, n=3, hkv=8, d=64, bs=16, nb=8, ptrs=(BAD,) * 3):
     return lib.tv_copy_blocks(*ptrs, n, hkv, d, bs, nb, None)
 

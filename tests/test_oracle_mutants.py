@@ -23,31 +23,30 @@ MUTANTS = [
     ("gqa-wrong-group-size", "const int g = h / group;", "const int g = h / (group * 2);"),
     ("scale-dropped", "score[t] = scale * dot;", "score[t] = dot;"),
     ("scale-squared", "score[t] = scale * dot;", "score[t] = scale * scale * dot;"),
-    ("context-one-short", "const int n = context_lens[s];",
-     "const int n = context_lens[s] - (context_lens[s] > 1);"),
-    ("context-one-long", "const int n = context_lens[s];",
-     "const int n = context_lens[s] + (context_lens[s] % 16 != 0);"),
+    ("context-one-short", "g, context_lens[s], num_kv_heads,",
+     "g, context_lens[s] - (context_lens[s] > 1), num_kv_heads,"),
+    ("context-one-long", "g, context_lens[s], num_kv_heads,",
+     "g, context_lens[s] + (context_lens[s] % 16 != 0), num_kv_heads,"),
     ("v-read-row-major", "vtile[(long)d * block_size + off]", "vtile[off * head_dim + d]"),
     ("k-offset-dropped", "((long)(d / KCHUNK) * block_size + off) * KCHUNK",
      "((long)(d / KCHUNK) * block_size) * KCHUNK"),
     ("k-token-major-layout", "((long)(d / KCHUNK) * block_size + off) * KCHUNK + d % KCHUNK",
      "(off * (head_dim / KCHUNK) + d / KCHUNK) * KCHUNK + d % KCHUNK"),
     ("k-chunk-dims-reversed", "* KCHUNK + d % KCHUNK;", "* KCHUNK + (KCHUNK - 1 - d % KCHUNK);"),
-    ("k-read-head-of-query", "dot += qv[d] * bf16_value(k_cache[k_index(blk, g, off, d,",
-     "dot += qv[d] * bf16_value(k_cache[k_index(blk, h % num_kv_heads, off, d,"),
+    ("k-read-other-head", "dot += qv[d] * bf16_value(k_cache[k_index(blk, g, off, d,",
+     "dot += qv[d] * bf16_value(k_cache[k_index(blk, (g + 1) % num_kv_heads, off, d,"),
     ("softmax-sign", "score[t] = exp(score[t] - m);", "score[t] = exp(m - score[t]);"),
     ("max-not-subtracted", "score[t] = exp(score[t] - m);", "score[t] = exp(score[t]);"),
     ("not-normalised", "double p = score[t] / l;", "double p = score[t];"),
-    ("table-index-by-offset", "block_tables[(long)s * max_blocks + t / block_size]",
-     "block_tables[(long)s * max_blocks + t % block_size]"),
-    ("table-ignored", "long blk = block_tables[(long)s * max_blocks + t / block_size];",
-     "long blk = t / block_size;"),
+    ("table-index-by-offset", "long blk = table_row[t / block_size];",
+     "long blk = table_row[t % block_size];"),
+    ("table-ignored", "long blk = table_row[t / block_size];", "long blk = t / block_size;"),
     ("query-of-group-leader", "qv[d] = bf16_value(q[pair * head_dim + d]);",
-     "qv[d] = bf16_value(q[(pair - h + g * group) * head_dim + d]);"),
-    ("dot-drops-last-dim", "for (int d = 0; d < head_dim; ++d)\n                dot +=",
-     "for (int d = 0; d < head_dim - 1; ++d)\n                dot +="),
-    ("max-is-first-score", "if (score[t] > m)\n                m = score[t];",
-     "if (0)\n                m = score[t];"),
+     "qv[d] = bf16_value(q[(pair - h + (h / group) * group) * head_dim + d]);"),
+    ("dot-drops-last-dim", "for (int d = 0; d < head_dim; ++d)\n            dot +=",
+     "for (int d = 0; d < head_dim - 1; ++d)\n            dot +="),
+    ("max-is-first-score", "if (score[t] > m)\n            m = score[t];",
+     "if (0)\n            m = score[t];"),
     ("write-v-row-major",
      "long vdst = ((blk * num_kv_heads + h) * head_dim + d) * block_size + off;",
      "long vdst = ((blk * num_kv_heads + h) * block_size + off) * head_dim + d;"),
@@ -63,6 +62,15 @@ MUTANTS = [
     ("copy-skips-nothing", "|| src == dst)\n            continue;\n        for (long e",
      ")\n            continue;\n        for (long e"),
     ("copy-half-block", "for (long e = 0; e < block_elems; ++e)", "for (long e = 0; e < block_elems / 2; ++e)"),
+    ("prefill-top-left-causal",
+     "const int p = context_lens[s] - m + (int)(row - query_start[s]);",
+     "const int p = (int)(row - query_start[s]);"),
+    ("prefill-mask-excludes-self", "p >= 0 ? p + 1 : 0,", "p >= 0 ? p : 0,"),
+    ("prefill-mask-sees-next", "p >= 0 ? p + 1 : 0,", "p >= 0 ? p + 2 : 0,"),
+    ("prefill-negative-rows-clamped", "p >= 0 ? p + 1 : 0,", "p >= 0 ? p + 1 : 1,"),
+    ("prefill-rows-of-first-sequence", "seq_of_row[r] = s;", "seq_of_row[r] = 0;"),
+    ("prefill-kv-head-of-query", "block_tables + (long)s * max_blocks, h / group, p",
+     "block_tables + (long)s * max_blocks, h % num_kv_heads, p"),
     ("pv-uses-first-token", "o[d] += p * bf16_value(vtile[(long)d * block_size + off]);",
      "o[d] += p * bf16_value(v_cache[(long)d * block_size]);"),
 ]
