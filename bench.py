@@ -46,6 +46,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged GQA decode attention: achieved HBM GB/s (% of peak) and seq-tokens/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, 2.5 PFLOP/s
 FLUSH_BYTES = 512 << 20
 COPY_CALIBRATION_BYTES = 1 << 30
 DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_tv_amd", "csrc", "paged_decode.hip")
@@ -154,6 +155,61 @@ def block_manager_rate(tv, steps, prompts=64, samples=4, prefix=1024, seed=7):
             "host_us_per_step": round(us, 2)}
 
 
+def prefill_rate(tv, dev, stream, flush, steps, index=3):
+    """Prefill attention (tv_paged_attention_prefill) on the prefill workload
+    `index` (default: 8 prompts of 2048 tokens, full prefill).  The prompts'
+    K/V are written into fresh pools with tv_cache_write first; each timed
+    launch follows a cache eviction and is bracketed by its own pair of
+    events.  FLOPs counted: 2 x 2 x head_dim per (query head, query, key)
+    pair the causal mask keeps (QK^T and PV)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_tv_amd import workloads as W
+    pb = W.make_prefill_workload(index)
+    b = pb.base
+
+    def dev_arr(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    kc, vc = tv.new_pools(b.num_blocks, b.num_kv_heads, b.head_dim, b.block_size, dev,
+                          fill=W.BF16_NAN)
+    for k, v, sl in (pb.prior_inputs(), pb.chunk_inputs()):
+        if len(sl):
+            tv.cache_write(dev_arr(k), dev_arr(v), kc, vc, dev_arr(sl), stream)
+    q, qs = dev_arr(pb.q), dev_arr(pb.query_start)
+    bt, cl = dev_arr(b.block_tables), dev_arr(b.context_lens)
+    out = torch.empty((pb.num_rows, b.num_q_heads, b.head_dim), dtype=torch.float32, device=dev)
+    mq, mc = pb.max_query_len, int(b.context_lens.max())
+
+    def launch():
+        tv.paged_attention_prefill(out, q, qs, kc, vc, bt, cl, mq, mc, b.scale, stream)
+
+    launch()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(ev):
+        flush(i)
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+    flops = pb.causal_flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    finite = bool(torch.isfinite(out).all().item())
+    del kc, vc, out
+    return {"workload": pb.name, "kernel": "paged_prefill_kernel<4>", "rows": pb.num_rows,
+            "flops_per_launch": flops, "us_per_launch": round(ms * 1e3, 2),
+            "TFLOP_per_s": round(tflops, 1), "output_finite": finite,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
+
+
 def cpu_baseline(batch, target_seconds: float):
     """Time the CPU oracle doing the same step (cache write + attention) on this host."""
     import oracle as O
@@ -184,6 +240,8 @@ def main(argv=None):
     ap.add_argument("--step", choices=["fused", "separate"], default="fused",
                     help="two launches (write folded into the partition pass) or three")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill attention measurement")
     ap.add_argument("--no-block-copy", action="store_true",
                     help="skip the copy-on-write block copy measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -372,6 +430,8 @@ def main(argv=None):
     if not args.no_block_copy:
         result["block_copy"] = block_copy_rate(tv, dev, stream, flush, K)
         result["block_manager"] = block_manager_rate(tv, K)
+    if not args.no_prefill:
+        result["prefill"] = prefill_rate(tv, dev, stream, flush, K)
 
     if not args.no_cpu_baseline:
         ref, times, threads = cpu_baseline(batch, args.cpu_seconds)

@@ -10,18 +10,22 @@
 // context, and row i (position n - m + i) attends to positions 0 .. n - m + i.
 //
 // Mapping to CDNA4:
-//   * One 256-thread workgroup (4 wavefronts) per (sequence, K/V head, tile of
+//   * One 512-thread workgroup (8 wavefronts) per (sequence, K/V head, tile of
 //     256 / G chunk rows), G = query heads per K/V head.  The G query heads of
 //     a token are stacked as MFMA columns, so each K/V element loaded feeds
 //     every head of the group.  Launch index: K/V head fastest (one XCD per
 //     head, so the tiles of one (sequence, head) share an L2), and the last,
 //     heaviest tiles of every sequence first.
-//   * Keys go in chunks of 64 (4 blocks).  All 256 threads load a chunk's K
+//   * Keys go in chunks of 64 (4 blocks).  All 512 threads load a chunk's K
 //     and V tiles (16 KiB) into registers one chunk ahead and store them to
 //     LDS, double-buffered, with one barrier per chunk.  Each wavefront then
-//     reads MFMA operands from LDS: every 1 KiB K operand read and 512 B V
-//     operand read is contiguous, so there are no bank conflicts.
-//   * Each wavefront owns 64 rows (4 tiles of 16 MFMA columns).  Scores
+//     reads MFMA operands from LDS: K tiles verbatim (every 1 KiB operand
+//     read contiguous), V rearranged so that one 16-byte read is a whole PV
+//     operand and 16 consecutive dims fall on distinct banks.
+//   * Each wavefront owns 32 rows (2 tiles of 16 MFMA columns); the register
+//     budget is cut to 128 so that four wavefronts share each SIMD, which
+//     hides the latency of the LDS reads, the cross-lane maximum and the
+//     MFMA results.  Scores
 //     S^T[16 keys][16 rows] = K . Q^T take two v_mfma_f32_16x16x32_bf16 per
 //     tile (dims 0-31, 32-63).  Lane (q = lane/16, c = lane%16) then holds
 //     keys 4q..4q+3 of every 16-key tile for row c, and two such tiles form
@@ -47,9 +51,10 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = kHeadDim;
 constexpr int BS = kBlockSize;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                        // wavefronts per workgroup
+constexpr int kRowTiles = 2;                     // 16-column MFMA tiles per wavefront
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowTiles = 4;                     // 16-column MFMA tiles per wavefront
+constexpr int kWavesPerSimd = 4;                 // occupancy the register budget is cut for
 constexpr int kChunkBlocks = 4;                  // blocks per key chunk
 constexpr int kChunkKeys = kChunkBlocks * BS;    // 64
 constexpr int kTileBytes = BS * D * 2;           // one (block, K/V head) tile: 2 KiB
@@ -64,9 +69,9 @@ __device__ __forceinline__ unsigned zero_from(unsigned w, int lim, int e)
 }
 
 template <int G>
-__global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillArgs a)
+__global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(PrefillArgs a)
 {
-    constexpr int kTokPerWave = 64 / G;
+    constexpr int kTokPerWave = 16 * kRowTiles / G;
     constexpr int kTokPerWg = kWaves * kTokPerWave;
     __shared__ __attribute__((aligned(16))) char lds[2 * kBufBytes];
 
@@ -127,16 +132,19 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillArgs a)
         qop[rt][1] = __builtin_bit_cast(bf16x8, x1);
     }
 
-    // Chunk loading: thread tid moves 16 bytes of each of the chunk's 4 blocks:
-    // K tile bytes 16 tid (tid < 128) or V tile bytes 16 (tid - 128).
-    const bool is_v = tid >= 128;
+    // Chunk loading: a chunk is 4 blocks x (K tile, V tile) x 128 pieces of
+    // 16 bytes.  Piece p = tid + kThreads * u (u < kLoads) is byte 16 (p & 127)
+    // of the K (bit 7 of p clear) or V tile of block p / 256.
+    constexpr int kLoads = kChunkBlocks * 256 / kThreads;
+    static_assert(kLoads * kThreads == kChunkBlocks * 256, "pieces per thread");
+    const bool is_v = (tid >> 7) & 1;
     const int piece = tid & 127;
     const char *pool = reinterpret_cast<const char *>(is_v ? a.v_cache : a.k_cache);
     const int32_t *table = a.block_tables + (int64_t)s * a.max_blocks;
     // V piece = dimension piece / 2, tokens 8 (piece & 1) .. + 8 of its block.
     const int v_tok0 = 8 * (piece & 1);
 
-    u32x4 pre[kChunkBlocks];
+    u32x4 pre[kLoads];
     unsigned valid_next = 0;
     auto load_chunk = [&](int c) {
         valid_next = 0;
@@ -144,19 +152,24 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillArgs a)
         for (int j = 0; j < kChunkBlocks; ++j) {
             const int b = c * kChunkBlocks + j;
             const int32_t phys = b * BS < n ? table[b] : -1;
-            const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
-            valid_next |= (ok ? 1u : 0u) << j;
+            valid_next |= (phys >= 0 && (int64_t)phys < a.num_blocks ? 1u : 0u) << j;
+        }
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int j = (tid + kThreads * u) >> 8;
+            const int b = c * kChunkBlocks + j;
             const u32x4 zero = {0u, 0u, 0u, 0u};
-            pre[j] = zero;
-            if (ok)
-                pre[j] = *reinterpret_cast<const u32x4 *>(
-                    pool + ((int64_t)phys * a.num_kv_heads + kvh) * kTileBytes + 16 * piece);
+            pre[u] = zero;
+            if ((valid_next >> j) & 1u)
+                pre[u] = *reinterpret_cast<const u32x4 *>(
+                    pool + ((int64_t)table[b] * a.num_kv_heads + kvh) * kTileBytes + 16 * piece);
         }
     };
     auto store_chunk = [&](int c, char *buf) {
 #pragma unroll
-        for (int j = 0; j < kChunkBlocks; ++j) {
-            u32x4 x = pre[j];
+        for (int u = 0; u < kLoads; ++u) {
+            const int j = (tid + kThreads * u) >> 8;
+            u32x4 x = pre[u];
             if (is_v) {
                 // Keys at or past the context end: V = 0 (the slot may hold NaN).
                 const int lim = n - ((c * kChunkBlocks + j) * BS + v_tok0);
@@ -166,8 +179,22 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillArgs a)
                         x[w] = zero_from(x[w], lim, 2 * w);
                 }
             }
-            *reinterpret_cast<u32x4 *>(buf + (is_v ? kChunkBlocks * kTileBytes : 0) +
-                                       j * kTileBytes + 16 * piece) = x;
+            if (is_v) {
+                // V of a chunk in LDS: [block pair kp][dim d][slot][block of the
+                // pair], 8 bytes (4 tokens) each, so that one 16-byte read gives
+                // the PV operand of 4 tokens of both blocks.  Token group g of
+                // dim d sits in slot g ^ f(d % 16), f(c) = (c ^ (c >> 2)) & 3,
+                // which keeps the operand reads of 16 consecutive dims on
+                // distinct banks.
+                const int d = piece >> 1, g0 = 2 * (piece & 1);
+                const int f = (d ^ (d >> 2)) & 3;
+                char *row = buf + kChunkBlocks * kTileBytes + (j >> 1) * 4096 + d * 64 + 8 * (j & 1);
+                const u32x2 lo = {x[0], x[1]}, hi = {x[2], x[3]};
+                *reinterpret_cast<u32x2 *>(row + 16 * (g0 ^ f)) = lo;
+                *reinterpret_cast<u32x2 *>(row + 16 * ((g0 + 1) ^ f)) = hi;
+            } else {
+                *reinterpret_cast<u32x4 *>(buf + j * kTileBytes + 16 * piece) = x;
+            }
         }
     };
 
@@ -261,16 +288,14 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillArgs a)
 
         // O^T[dims][rows] += V^T . P^T: V^T lane (dim 16 dt + col, keys of k-slots
         // 8 lq .. 8 lq + 7) = V[2 kp][dim][4 lq .. 4 lq + 3], V[2 kp + 1][dim][4 lq ..].
-        const char *vb = buf + kChunkBlocks * kTileBytes + col * 32 + 8 * lq;
+        const char *vb = buf + kChunkBlocks * kTileBytes + col * 64 +
+                         16 * (lq ^ ((col ^ (col >> 2)) & 3));
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const char *vp = vb + (2 * kp) * kTileBytes + dt * 16 * 32;
-                const u32x2 v0 = *reinterpret_cast<const u32x2 *>(vp);
-                const u32x2 v1 = *reinterpret_cast<const u32x2 *>(vp + kTileBytes);
-                const u32x4 vv = {v0[0], v0[1], v1[0], v1[1]};
-                const bf16x8 vop = __builtin_bit_cast(bf16x8, vv);
+                const bf16x8 vop = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4 *>(vb + kp * 4096 + dt * 16 * 64));
 #pragma unroll
                 for (int rt = 0; rt < kRowTiles; ++rt)
                     o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[rt][kp], o[rt][dt],
@@ -298,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillArgs a)
 template <int G>
 hipError_t launch_g(const PrefillArgs &a, hipStream_t stream)
 {
-    constexpr int kTokPerWg = kWaves * 64 / G;
+    constexpr int kTokPerWg = kWaves * 16 * kRowTiles / G;
     const int64_t tiles = (a.max_query_len + kTokPerWg - 1) / kTokPerWg;
     const int64_t grid = tiles * a.num_seqs * a.num_kv_heads;
     if (grid == 0)
