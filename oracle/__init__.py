@@ -17,6 +17,12 @@ Parity status of each function (pins live in ``tests/test_oracle.py`` and
                            example).
   * ``copy_blocks``     -- pinned (hand-derived literal pools; skip rules;
                            refused conflicting pairs).
+  * ``rope``            -- pinned (single-pair closed form with numpy's
+                           cos/sin, numpy complex multiplication, half-split
+                           = interleaved on permuted dims, position 0,
+                           relative-position identity, R_a R_b = R_(a+b),
+                           bf16 rounding against a brute-force neighbour
+                           search).
   * ``paged_prefill``   -- pinned (torch SDPA with a causal mask on full
                            prompts, chunking invariance, one row per sequence
                            equals decode, first position equals V_0, block
@@ -73,6 +79,11 @@ class Oracle:
                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_long, ctypes.c_double, ctypes.c_int]
+        lib.oracle_rope.restype = ctypes.c_int
+        lib.oracle_rope.argtypes = [_u16p, _i32p, ctypes.POINTER(ctypes.c_float), ctypes.c_long,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _u16p]
+        lib.oracle_bf16_round.restype = None
+        lib.oracle_bf16_round.argtypes = [_f64p, ctypes.c_long, _u16p]
         lib.oracle_copy_blocks.restype = ctypes.c_long
         lib.oracle_copy_blocks.argtypes = [_u16p, _u16p, _i64p, ctypes.c_long, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_long]
@@ -171,6 +182,30 @@ class Oracle:
                                           max(bt.shape[1], 1), nb, float(scale), threads)
         if r != 0:
             raise ValueError("oracle_paged_prefill rejected its arguments")
+        return out
+
+    def rope(self, x: np.ndarray, positions: np.ndarray, inv_freq: np.ndarray, style: int = 0):
+        """Rotary embedding of x ([T, H, D] bf16 bits) at the given positions:
+        (rotated values in float64, the same rounded to bf16 bits)."""
+        x = np.ascontiguousarray(x, np.uint16)
+        pos = np.ascontiguousarray(positions, np.int32)
+        f = np.ascontiguousarray(inv_freq, np.float32)
+        T, H, D = x.shape
+        assert pos.shape == (T,) and f.shape == (D // 2,)
+        out = np.zeros((T, H, D), np.float64)
+        bits = np.zeros((T, H, D), np.uint16)
+        r = self.lib.oracle_rope(_ptr(x, _u16p), _ptr(pos, _i32p),
+                                 f.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), T, H, D,
+                                 int(style), _ptr(out, _f64p), _ptr(bits, _u16p))
+        if r != 0:
+            raise ValueError("oracle_rope rejected its arguments")
+        return out, bits
+
+    def bf16_round(self, v: np.ndarray) -> np.ndarray:
+        """Nearest bf16 (ties to even) of each double, as bits."""
+        v = np.ascontiguousarray(v, np.float64)
+        out = np.zeros(v.shape, np.uint16)
+        self.lib.oracle_bf16_round(_ptr(v, _f64p), v.size, _ptr(out, _u16p))
         return out
 
     def max_threads(self) -> int:

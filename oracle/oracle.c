@@ -1,6 +1,6 @@
 /*
  * oracle.c -- plain, slow CPU reference for paged GQA attention (decode step,
- * prefill / chunked prefill, block copy).
+ * prefill / chunked prefill, block copy, rotary position embedding).
  *
  * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg load this library.  The GPU library never
@@ -345,6 +345,81 @@ int oracle_paged_prefill(double *out, const uint16_t *q, const int32_t *query_st
     }
     free(seq_of_row);
     return bad ? -1 : 0;
+}
+
+/*
+ * Nearest bf16 to v, ties to even, taken directly from the double (no
+ * intermediate float rounding): v = m * 2^e with 0.5 <= |m| < 1, so the 8
+ * significant bits of bf16 are rint(m * 2^8).  Finite, normal-range inputs
+ * only (the rotated values of bf16 data); 0 maps to +0 or -0.
+ */
+static uint16_t bf16_round(double v)
+{
+    if (v == 0.0)
+        return signbit(v) ? 0x8000u : 0u;
+    int e;
+    double m = frexp(v, &e);
+    double r = rint(m * 256.0);                      /* default rounding mode: ties to even */
+    float f = (float)ldexp(r, e - 8);                /* 8 significant bits: exact in float */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    return (uint16_t)(bits >> 16);
+}
+
+/* out[i] = bf16_round(v[i]) for i < n (exported so the rounding can be pinned). */
+void oracle_bf16_round(const double *v, long n, uint16_t *out)
+{
+    for (long i = 0; i < n; ++i)
+        out[i] = bf16_round(v[i]);
+}
+
+/*
+ * Rotary position embedding ("tiny-vllm 씹뜯맛즐 - (1)" page, section "5. 절대
+ * 위치 임베딩 대신 RoPE": q and k at position p are multiplied by a rotation
+ * R_p, so that (R_i q)^T (R_j k) = q^T R_{j-i} k; "tiny-vLLM으로 처음부터 고성능
+ * LLM 추론 엔진 구축하기" page: complex-number math with sine and cosine).
+ *
+ * R_p turns each pair of dimensions (a, b) = pair k by the angle
+ * p * inv_freq[k]:  a' = a cos - b sin,  b' = a sin + b cos.
+ *   style 0: pair k is dims (2k, 2k+1), the complex number a + i b times e^{i angle};
+ *   style 1: pair k is dims (k, k + D/2).
+ * x: [T][H][D] bf16 bits; positions: int32 [T]; inv_freq: float [D/2].
+ * out_f64 ([T][H][D], may be NULL) gets the rotated values in double
+ * precision, out_bits (may be NULL) the same rounded to bf16 (ties to even).
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_rope(const uint16_t *x, const int32_t *positions, const float *inv_freq,
+                long num_tokens, int num_heads, int head_dim, int style, double *out_f64,
+                uint16_t *out_bits)
+{
+    if (num_tokens < 0 || num_heads < 1 || head_dim < 2 || head_dim % 2 != 0 ||
+        (style != 0 && style != 1))
+        return -1;
+    const int half = head_dim / 2;
+    for (long t = 0; t < num_tokens; ++t) {
+        for (int k = 0; k < half; ++k) {
+            const double angle = (double)positions[t] * (double)inv_freq[k];
+            const double c = cos(angle), sn = sin(angle);
+            const int ia = style == 0 ? 2 * k : k;
+            const int ib = style == 0 ? 2 * k + 1 : k + half;
+            for (int h = 0; h < num_heads; ++h) {
+                const long row = (t * num_heads + h) * (long)head_dim;
+                const double a = bf16_value(x[row + ia]);
+                const double b = bf16_value(x[row + ib]);
+                const double ra = a * c - b * sn;
+                const double rb = a * sn + b * c;
+                if (out_f64) {
+                    out_f64[row + ia] = ra;
+                    out_f64[row + ib] = rb;
+                }
+                if (out_bits) {
+                    out_bits[row + ia] = bf16_round(ra);
+                    out_bits[row + ib] = bf16_round(rb);
+                }
+            }
+        }
+    }
+    return 0;
 }
 
 /* Number of OpenMP threads the library would use by default (1 without OpenMP). */

@@ -506,6 +506,127 @@ def pin_prefill_block_permutation(orc):
     assert np.array_equal(out, out2)
 
 
+# --------------------------------------------------------------------- RoPE pins
+
+
+def _inv_freq(d, base=500000.0):
+    return (base ** (-np.arange(0, d, 2, dtype=np.float64) / d)).astype(np.float32)
+
+
+def _pair_dims(style, k, d):
+    return (2 * k, 2 * k + 1) if style == 0 else (k, k + d // 2)
+
+
+def pin_rope_pair_closed_form(orc):
+    """A unit vector in the first (second) dim of pair k turns into
+    (cos, sin) ((-sin, cos)) of position * inv_freq[k], numpy's cos and sin."""
+    d = 16
+    f = _inv_freq(d, 10000.0)
+    pos = np.array([0, 1, 7, 1000, 131071, -5], np.int32)
+    for style in (0, 1):
+        for k in (0, 3, 7):
+            ia, ib = _pair_dims(style, k, d)
+            x = np.zeros((len(pos), 2, d), np.uint16)
+            x[:, 0, ia] = 0x3F80                               # 1.0
+            x[:, 1, ib] = 0x3F80
+            out, _ = orc.rope(x, pos, f, style)
+            ang = pos.astype(np.float64) * np.float64(f[k])
+            c, s_ = np.cos(ang), np.sin(ang)
+            for h, (ea, eb) in enumerate(((c, s_), (-s_, c))):
+                assert np.abs(out[:, h, ia] - ea).max() <= 1e-15, (style, k, h)
+                assert np.abs(out[:, h, ib] - eb).max() <= 1e-15, (style, k, h)
+            rest = np.ones(d, bool)
+            rest[[ia, ib]] = False
+            assert not out[:, :, rest].any(), "other dims must stay zero"
+
+
+def pin_rope_complex_form(orc):
+    """Style 0 is multiplication of a + i b by e^{i p f_k} (numpy complex)."""
+    rng = np.random.default_rng(41)
+    d = 64
+    x = W.round_to_bf16_bits(rng.standard_normal((9, 4, d)).astype(np.float32))
+    pos = rng.integers(0, 140000, 9).astype(np.int32)
+    f = _inv_freq(d)
+    out, _ = orc.rope(x, pos, f, 0)
+    xf = _f64(x)
+    z = xf[..., 0::2] + 1j * xf[..., 1::2]
+    zr = z * np.exp(1j * pos[:, None, None] * f.astype(np.float64)[None, None, :])
+    assert np.abs(out[..., 0::2] - zr.real).max() <= 1e-12
+    assert np.abs(out[..., 1::2] - zr.imag).max() <= 1e-12
+
+
+def pin_rope_half_split_is_permuted_interleaved(orc):
+    """Style 1 equals style 0 applied after moving dims (k, k + D/2) to (2k, 2k+1)."""
+    rng = np.random.default_rng(42)
+    d = 64
+    x = W.round_to_bf16_bits(rng.standard_normal((5, 3, d)).astype(np.float32))
+    pos = rng.integers(0, 5000, 5).astype(np.int32)
+    f = _inv_freq(d)
+    perm = np.empty(d, np.int64)
+    perm[0::2] = np.arange(d // 2)
+    perm[1::2] = np.arange(d // 2) + d // 2                    # interleaved dim j <- half-split perm[j]
+    o1, b1 = orc.rope(x, pos, f, 1)
+    o0, b0 = orc.rope(x[..., perm], pos, f, 0)
+    assert np.array_equal(o1[..., perm], o0) and np.array_equal(b1[..., perm], b0)
+
+
+def pin_rope_position_zero(orc):
+    """Position 0 is the identity, bit for bit."""
+    rng = np.random.default_rng(43)
+    x = W.round_to_bf16_bits(rng.standard_normal((4, 8, 64)).astype(np.float32))
+    for style in (0, 1):
+        out, bits = orc.rope(x, np.zeros(4, np.int32), _inv_freq(64), style)
+        assert np.array_equal(bits, x) and np.array_equal(out, _f64(x))
+
+
+def pin_rope_relative_identity(orc):
+    """The pages' identity (R_i q)^T (R_j k) = q^T R_{j-i} k, per head and pair
+    of positions, and the norm of every pair is kept."""
+    rng = np.random.default_rng(44)
+    d = 64
+    f = _inv_freq(d, 10000.0)
+    q = W.round_to_bf16_bits(rng.standard_normal((1, 2, d)).astype(np.float32))
+    k = W.round_to_bf16_bits(rng.standard_normal((1, 2, d)).astype(np.float32))
+    for style in (0, 1):
+        for i, j in ((0, 5), (3, 3), (100, 37), (70000, 131000), (9, -4)):
+            qi, _ = orc.rope(q, np.array([i], np.int32), f, style)
+            kj, _ = orc.rope(k, np.array([j], np.int32), f, style)
+            kd, _ = orc.rope(k, np.array([j - i], np.int32), f, style)
+            lhs = (qi[0] * kj[0]).sum(-1)
+            rhs = (_f64(q[0]) * kd[0]).sum(-1)
+            assert np.abs(lhs - rhs).max() <= 1e-9 * (1 + np.abs(rhs).max()), (style, i, j)
+        out, _ = orc.rope(k, np.array([12345], np.int32), f, style)
+        a, b = (slice(0, None, 2), slice(1, None, 2)) if style == 0 else \
+            (slice(0, d // 2), slice(d // 2, None))
+        n0 = _f64(k)[..., a] ** 2 + _f64(k)[..., b] ** 2
+        n1 = out[..., a] ** 2 + out[..., b] ** 2
+        assert np.abs(n0 - n1).max() <= 1e-12
+
+
+def pin_bf16_round(orc):
+    """Rounding to bf16: the nearest of the two bf16 neighbours, ties to even,
+    found by brute force on the float32 bit patterns."""
+    rng = np.random.default_rng(45)
+    v = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-3, 4, 4000),
+                        [1.0, -2.5, 1.00390625, 1.01171875, -1.01171875, 3.0e-5]])
+    # exact ties: midpoints of adjacent bf16 values
+    lo = W.round_to_bf16_bits(rng.standard_normal(200).astype(np.float32))
+    lof = W.bf16_bits_to_float32(lo).astype(np.float64)
+    hif = W.bf16_bits_to_float32((lo.astype(np.uint32) + 1).astype(np.uint16)).astype(np.float64)
+    v = np.concatenate([v, (lof + hif) / 2])
+    got = orc.bf16_round(v)
+    for x, g in zip(v, got):
+        f32 = np.float32(x)
+        b = int(np.array([f32]).view(np.uint32)[0]) >> 16
+        cands = [(b + dlt) & 0xFFFF for dlt in (-1, 0, 1, 2)]
+        vals = [float(W.bf16_bits_to_float32(np.array([c], np.uint16))[0]) for c in cands]
+        errs = [abs(val - x) for val in vals]
+        best = min(errs)
+        ties = [c for c, e in zip(cands, errs) if e == best]
+        want = ties[0] if len(ties) == 1 else [c for c in ties if c % 2 == 0][0]
+        assert int(g) == want, (x, hex(int(g)), hex(want))
+
+
 ALL_PINS = [
     pin_contiguous_bruteforce, pin_torch_sdpa, pin_block_permutation, pin_single_token,
     pin_constant_v, pin_zero_query_mean, pin_gqa_figure, pin_one_dominant_key,
@@ -514,6 +635,8 @@ ALL_PINS = [
     pin_prefill_sdpa_full_prompts, pin_prefill_sdpa_chunks, pin_prefill_chunking_invariance,
     pin_prefill_single_rows_are_decode, pin_prefill_first_position,
     pin_prefill_rows_before_context, pin_prefill_block_permutation,
+    pin_rope_pair_closed_form, pin_rope_complex_form, pin_rope_half_split_is_permuted_interleaved,
+    pin_rope_position_zero, pin_rope_relative_identity, pin_bf16_round,
 ]
 
 

@@ -71,6 +71,17 @@ MUTANTS = [
     ("prefill-rows-of-first-sequence", "seq_of_row[r] = s;", "seq_of_row[r] = 0;"),
     ("prefill-kv-head-of-query", "block_tables + (long)s * max_blocks, h / group, p",
      "block_tables + (long)s * max_blocks, h % num_kv_heads, p"),
+    ("rope-sin-sign", "const double ra = a * c - b * sn;", "const double ra = a * c + b * sn;"),
+    ("rope-half-split-off-by-one", "const int ib = style == 0 ? 2 * k + 1 : k + half;",
+     "const int ib = style == 0 ? 2 * k + 1 : (k + half + 1) % head_dim;"),
+    ("rope-one-frequency", "(double)positions[t] * (double)inv_freq[k];",
+     "(double)positions[t] * (double)inv_freq[0];"),
+    ("rope-first-position-only", "(double)positions[t] * (double)inv_freq[k];",
+     "(double)positions[0] * (double)inv_freq[k];"),
+    ("rope-pairs-swapped", "const int ia = style == 0 ? 2 * k : k;",
+     "const int ia = style == 0 ? 2 * k + 1 : k;\n            const int ib_ = 0; (void)ib_;"),
+    ("bf16-round-truncates", "double r = rint(m * 256.0);", "double r = trunc(m * 256.0);"),
+    ("bf16-round-ties-away", "double r = rint(m * 256.0);", "double r = round(m * 256.0);"),
     ("pv-uses-first-token", "o[d] += p * bf16_value(vtile[(long)d * block_size + off]);",
      "o[d] += p * bf16_value(v_cache[(long)d * block_size]);"),
 ]
