@@ -210,6 +210,58 @@ def prefill_rate(tv, dev, stream, flush, steps, index=3):
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
 
+def rope_rate(tv, dev, stream, flush, steps, index=3):
+    """Rotary embedding on the prefill workload `index` (8 prompts x 2048
+    tokens): the K/V cache write of all prompt tokens plain (tv_cache_write)
+    and with K rotated (tv_cache_write_rope), and q rotated in place
+    (tv_rope).  Each launch follows a cache eviction and has its own events.
+    Bytes counted: K and V read and written (cache writes), q read and
+    written (tv_rope), plus slots and positions."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_tv_amd import workloads as W
+    pb = W.make_prefill_workload(index)
+    b = pb.base
+
+    def dev_arr(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    k, v, sl = pb.chunk_inputs()
+    pos = np.concatenate([np.arange(n, dtype=np.int32) for n in pb.query_lens])
+    kd, vd, sd, pd = dev_arr(k), dev_arr(v), dev_arr(sl), dev_arr(pos)
+    qd = dev_arr(pb.q)
+    f = dev_arr(tv.rope_inv_freq(b.head_dim, 500000.0))
+    kc, vc = tv.new_pools(b.num_blocks, b.num_kv_heads, b.head_dim, b.block_size, dev, fill=0)
+    T = int(len(sl))
+    kv_bytes = 2 * 2 * T * b.num_kv_heads * b.head_dim * 2 + T * 8
+    q_bytes = 2 * pb.num_rows * b.num_q_heads * b.head_dim * 2 + pb.num_rows * 4
+    cases = {
+        "cache_write": (lambda: tv.cache_write(kd, vd, kc, vc, sd, stream), kv_bytes),
+        "cache_write_rope": (lambda: tv.cache_write_rope(kd, vd, kc, vc, sd, pd, f, 0, stream),
+                             kv_bytes + T * 4),
+        "rope_q": (lambda: tv.rope(qd, pd, f, 0, stream), q_bytes),
+    }
+    res = {"workload": pb.name, "tokens": T}
+    for name, (fn, nbytes) in cases.items():
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i, (e0, e1) in enumerate(ev):
+            flush(i)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"bytes_per_launch": nbytes, "us_per_launch": round(ms * 1e3, 2),
+                     "GB_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del kc, vc
+    return res
+
+
 def cpu_baseline(batch, target_seconds: float):
     """Time the CPU oracle doing the same step (cache write + attention) on this host."""
     import oracle as O
@@ -432,6 +484,7 @@ def main(argv=None):
         result["block_manager"] = block_manager_rate(tv, K)
     if not args.no_prefill:
         result["prefill"] = prefill_rate(tv, dev, stream, flush, K)
+        result["rope"] = rope_rate(tv, dev, stream, flush, K)
 
     if not args.no_cpu_baseline:
         ref, times, threads = cpu_baseline(batch, args.cpu_seconds)

@@ -111,6 +111,44 @@ tv_status tv_cache_write(const uint16_t *k, const uint16_t *v,
                          int32_t block_size, int64_t num_blocks, void *stream);
 
 /*
+ * Rotary position embedding ("tiny-vllm 씹뜯맛즐 - (1)" page, section "5. 절대
+ * 위치 임베딩 대신 RoPE": q and k of position p are turned by a rotation R_p,
+ * so that (R_i q)^T (R_j k) = q^T R_{j-i} k; "tiny-vLLM으로 처음부터 고성능 LLM
+ * 추론 엔진 구축하기" page: complex-number math with sine and cosine, done
+ * inline in the kernels).
+ *
+ * R_p turns each pair of dimensions (a, b) = pair k, k < head_dim / 2, by the
+ * angle positions[i] * inv_freq[k]:  a' = a cos - b sin,  b' = a sin + b cos.
+ *   rope_style 0: pair k = dims (2k, 2k+1) (the pair as a complex number);
+ *   rope_style 1: pair k = dims (k, k + head_dim/2).
+ * The angle is formed exactly and reduced modulo 2 pi in the kernel; the
+ * rotated values are computed in fp32 and rounded to bf16 (ties to even).
+ * inv_freq (float [head_dim / 2], device) is the caller's: base^(-2k/D) for
+ * plain RoPE, or any scaled table (context-extension schemes only change it).
+ *
+ * tv_cache_write_rope: tv_cache_write with every written token's K turned by
+ * R_{positions[i]} (V is copied unchanged).
+ *   positions  int32 [num_tokens] (device), 4-byte aligned; the position of
+ *              each token in its sequence (not its slot)
+ *   other arguments as for tv_cache_write
+ * tv_rope: x [num_tokens][num_heads][head_dim] bf16 (16-byte aligned) turned
+ * in place by R_{positions[i]} (q before attention, or a new token's K before
+ * tv_paged_attention_decode_append).
+ * Supported: head_dim a multiple of 8, at most 128.  Errors: TV_ERR_NULL,
+ * TV_ERR_SHAPE (negative counts, non-positive sizes, a style other than 0/1),
+ * TV_ERR_UNSUPPORTED, TV_ERR_ALIGNMENT, TV_ERR_HIP.  num_tokens == 0 is a no-op.
+ */
+tv_status tv_cache_write_rope(const uint16_t *k, const uint16_t *v, uint16_t *k_cache,
+                              uint16_t *v_cache, const int64_t *slot_mapping,
+                              const int32_t *positions, const float *inv_freq,
+                              int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int64_t num_blocks, int32_t rope_style,
+                              void *stream);
+tv_status tv_rope(uint16_t *x, const int32_t *positions, const float *inv_freq,
+                  int64_t num_tokens, int32_t num_heads, int32_t head_dim, int32_t rope_style,
+                  void *stream);
+
+/*
  * Paged decode attention, partition pass ("vLLM" page: PagedAttention and
  * Flash Attention's online softmax; "tiny-vllm" page: GQA grouping).
  *

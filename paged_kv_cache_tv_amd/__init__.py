@@ -6,13 +6,15 @@ copies and the host block manager run in ``libtv.so``; this package only
 marshals torch tensors into the C calls declared in ``include/tv.h``.
 """
 
-from .binding import (LIB_PATH, BlockManager, TvError, cache_write, copy_blocks, lib,
+from .binding import (LIB_PATH, BlockManager, TvError, cache_write, cache_write_rope,
+                      copy_blocks, lib, rope, rope_inv_freq,
                       load_library, new_pools,
                       new_workspace, num_partitions, paged_attention, paged_attention_decode,
                       paged_attention_decode_append, paged_attention_prefill,
                       paged_attention_reduce)
 
-__all__ = ["LIB_PATH", "BlockManager", "TvError", "cache_write", "copy_blocks", "lib",
+__all__ = ["LIB_PATH", "BlockManager", "TvError", "cache_write", "cache_write_rope",
+           "copy_blocks", "lib", "rope", "rope_inv_freq",
            "load_library", "new_pools",
            "new_workspace", "num_partitions", "paged_attention", "paged_attention_decode",
            "paged_attention_decode_append", "paged_attention_prefill", "paged_attention_reduce"]

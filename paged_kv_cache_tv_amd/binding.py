@@ -56,6 +56,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_paged_attention_prefill.restype = ctypes.c_int
     lib.tv_paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                                i32, i32, i64, i32, i32, ctypes.c_float, vp]
+    lib.tv_cache_write_rope.restype = ctypes.c_int
+    lib.tv_cache_write_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, i32,
+                                        vp]
+    lib.tv_rope.restype = ctypes.c_int
+    lib.tv_rope.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp]
     lib.tv_copy_blocks.restype = ctypes.c_int
     lib.tv_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, vp]
     i32p, i64p = ctypes.POINTER(i32), ctypes.POINTER(i64)
@@ -198,6 +203,51 @@ def paged_attention_decode(part_acc, part_max, part_sum, q, k_cache, v_cache, bl
         S, hq, hkv, d, bs, block_tables.shape[1], nb, int(max_context_len), int(partition_size),
         float(scale), _stream_handle(stream, q.device))
     _check("tv_paged_attention_decode", st)
+
+
+def rope_inv_freq(head_dim: int, base: float):
+    """Plain RoPE frequencies base^(-2k / head_dim), k < head_dim / 2, as float32
+    (host numpy; copy to the device for the calls below)."""
+    import numpy as np
+    k = np.arange(0, head_dim, 2, dtype=np.float64)
+    return (base ** (-k / head_dim)).astype(np.float32)
+
+
+def cache_write_rope(k, v, k_cache, v_cache, slot_mapping, positions, inv_freq,
+                     rope_style: int = 0, stream=None) -> None:
+    """tv_cache_write_rope: tv_cache_write with K turned by the rotary embedding
+    of positions (int32 [T]); inv_freq: float32 [D/2] on the device."""
+    import torch
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, n, itemsize=2, ndim=3)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1)
+    _need(positions, "positions", dtype=torch.int32, ndim=1)
+    _need(inv_freq, "inv_freq", dtype=torch.float32, ndim=1)
+    T, hkv, d = k.shape
+    nb, hkv2, bs, d2 = _pool_dims(k_cache, v_cache)
+    if (hkv2, d2) != (hkv, d) or tuple(v.shape) != (T, hkv, d):
+        raise ValueError("k, v and the cache must agree on [Hkv, D]")
+    if slot_mapping.shape[0] != T or positions.shape[0] != T or inv_freq.shape[0] != d // 2:
+        raise ValueError("slot_mapping, positions: [T]; inv_freq: [D/2]")
+    st = lib().tv_cache_write_rope(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(),
+                                   v_cache.data_ptr(), slot_mapping.data_ptr(),
+                                   positions.data_ptr(), inv_freq.data_ptr(), T, hkv, d, bs, nb,
+                                   int(rope_style), _stream_handle(stream, k.device))
+    _check("tv_cache_write_rope", st)
+
+
+def rope(x, positions, inv_freq, rope_style: int = 0, stream=None) -> None:
+    """tv_rope: turn x ([T, H, D] bf16) in place by the rotary embedding of positions."""
+    import torch
+    _need(x, "x", itemsize=2, ndim=3)
+    _need(positions, "positions", dtype=torch.int32, ndim=1)
+    _need(inv_freq, "inv_freq", dtype=torch.float32, ndim=1)
+    T, h, d = x.shape
+    if positions.shape[0] != T or inv_freq.shape[0] != d // 2:
+        raise ValueError("positions: [T]; inv_freq: [D/2]")
+    st = lib().tv_rope(x.data_ptr(), positions.data_ptr(), inv_freq.data_ptr(), T, h, d,
+                       int(rope_style), _stream_handle(stream, x.device))
+    _check("tv_rope", st)
 
 
 def paged_attention_prefill(out, q, query_start, k_cache, v_cache, block_tables, context_lens,

@@ -1,6 +1,7 @@
 // Cache write: scatter each new token's K and V rows into the slot the engine
 // chose for it ("Tiny-vLLM" page, slot_mapping; "vLLM" page, fixed 16-token
-// blocks).  A pure bit copy.
+// blocks).  A pure bit copy, or with K turned by the rotary position
+// embedding on the way in (and the same rotation in place for q).
 //
 // One wavefront per token.  A token's K (or V) is num_kv_heads * head_dim bf16
 // values, contiguous in the input; lanes take 16-byte chunks (8 values of one
@@ -8,6 +9,7 @@
 // head_dim / 8 chunks of [block_size tokens][8 dims], so each K chunk is one
 // 16-byte store at (chunk, token offset); V values go to 8 consecutive rows of
 // the dimension-major V tile, one 2-byte store each.
+#include "rope_math.h"
 #include "tv_internal.h"
 
 namespace tv {
@@ -15,6 +17,14 @@ namespace {
 
 constexpr int kWavesPerGroup = 4;
 
+// ROPE: K is turned by the rotary embedding of positions[tok] before the
+// store (see rope_math.h).  Lanes 0 .. head_dim/2 - 1 compute the token's
+// (cos, sin) per pair once; a lane handling pairs 4q .. 4q+3 of a head (q =
+// its group within the head) fetches them with shuffles, in a loop whose trip
+// count is the same for every lane.  Style 0 pairs dims (2k, 2k+1), so group
+// q is the 16-byte chunk q of the head; style 1 pairs (k, k + head_dim/2), so
+// group q is dims 4q .. 4q+3 and their partners, two 8-byte pieces.
+template <bool ROPE>
 __global__ __launch_bounds__(64 * kWavesPerGroup) void cache_write_kernel(CacheWriteArgs a)
 {
     const int64_t tok = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
@@ -35,14 +45,72 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void cache_write_kernel(CacheW
         return;
     const int64_t blk = slot / a.block_size;
     const int off = (int)(slot - blk * a.block_size);
-    for (int c = lane; c < chunks; c += 64) {
-        const uint4 kk = c == lane ? k0 : ksrc[c];
+    float pc = 1.f, ps = 0.f;
+    if (ROPE) {
+        const int half = a.head_dim >> 1;
+        rope_cos_sin(a.positions[tok], a.inv_freq[lane % half], pc, ps);
+    }
+    for (int base = 0; base < chunks; base += 64) {
+        const int c = base + lane;
+        float cs[4], sn[4];
+        if (ROPE) {
+            const int q = c % (a.head_dim >> 3);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                cs[i] = __shfl(pc, 4 * q + i);
+                sn[i] = __shfl(ps, 4 * q + i);
+            }
+        }
+        if (c >= chunks)
+            continue;
         const uint4 vv = c == lane ? v0 : vsrc[c];
         const int h = (c << 3) / a.head_dim;
         const int d = (c << 3) - h * a.head_dim;
         const int64_t tile = blk * a.num_kv_heads + h;
-        *reinterpret_cast<uint4 *>(a.k_cache + tile * a.head_dim * a.block_size +
-                                   ((int64_t)(d >> 3) * a.block_size + off) * 8) = kk;
+        uint16_t *ktile = a.k_cache + tile * a.head_dim * a.block_size;
+        if (!ROPE) {
+            const uint4 kk = c == lane ? k0 : ksrc[c];
+            *reinterpret_cast<uint4 *>(ktile + ((int64_t)(d >> 3) * a.block_size + off) * 8) = kk;
+        } else if (a.rope_style == 0) {
+            // Pairs (d + 2i, d + 2i + 1), i < 4: one 16-byte chunk in and out.
+            const uint4 kk = c == lane ? k0 : ksrc[c];
+            const uint32_t w[4] = {kk.x, kk.y, kk.z, kk.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float ra, rb;
+                rope_turn(__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xFFFF0000u),
+                          cs[i], sn[i], ra, rb);
+                o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ra) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << 16);
+            }
+            *reinterpret_cast<uint4 *>(ktile + ((int64_t)(d >> 3) * a.block_size + off) * 8) =
+                make_uint4(o[0], o[1], o[2], o[3]);
+        } else {
+            // Pairs (4q + i, 4q + i + head_dim/2), i < 4, q = d / 8 within the head.
+            const int half = a.head_dim >> 1;
+            const int da = d >> 1;                           // 4q
+            const uint16_t *src = a.k + tok * row + h * a.head_dim;
+            const uint2 pa = *reinterpret_cast<const uint2 *>(src + da);
+            const uint2 pb = *reinterpret_cast<const uint2 *>(src + da + half);
+            const uint32_t wa[2] = {pa.x, pa.y}, wb[2] = {pb.x, pb.y};
+            uint32_t oa[2] = {0u, 0u}, ob[2] = {0u, 0u};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t xa = (wa[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                const uint32_t xb = (wb[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                float ra, rb;
+                rope_turn(__uint_as_float(xa << 16), __uint_as_float(xb << 16), cs[i], sn[i], ra,
+                          rb);
+                oa[i >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ra) << (16 * (i & 1));
+                ob[i >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << (16 * (i & 1));
+            }
+            const int db = da + half;
+            *reinterpret_cast<uint2 *>(ktile + ((int64_t)(da >> 3) * a.block_size + off) * 8 +
+                                       (da & 7)) = make_uint2(oa[0], oa[1]);
+            *reinterpret_cast<uint2 *>(ktile + ((int64_t)(db >> 3) * a.block_size + off) * 8 +
+                                       (db & 7)) = make_uint2(ob[0], ob[1]);
+        }
         uint16_t *vdst = a.v_cache + (tile * a.head_dim + d) * a.block_size + off;
         const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
@@ -53,13 +121,87 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void cache_write_kernel(CacheW
     }
 }
 
+// In-place rotary embedding of x [tokens][heads][head_dim], one wavefront per
+// token, with the same lane layout as the cache write above.
+__global__ __launch_bounds__(64 * kWavesPerGroup) void rope_kernel(RopeArgs a)
+{
+    const int64_t tok = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    if (tok >= a.num_tokens)
+        return;
+    const int lane = threadIdx.x & 63;
+    const int half = a.head_dim >> 1;
+    const int groups = (a.num_heads * a.head_dim) >> 3;
+    float pc, ps;
+    rope_cos_sin(a.positions[tok], a.inv_freq[lane % half], pc, ps);
+    uint16_t *xt = a.x + tok * a.num_heads * a.head_dim;
+    for (int base = 0; base < groups; base += 64) {
+        const int c = base + lane;
+        const int q = c % (a.head_dim >> 3);
+        float cs[4], sn[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            cs[i] = __shfl(pc, 4 * q + i);
+            sn[i] = __shfl(ps, 4 * q + i);
+        }
+        if (c >= groups)
+            continue;
+        const int h = (c << 3) / a.head_dim;
+        if (a.style == 0) {
+            uint4 *p = reinterpret_cast<uint4 *>(xt) + c;
+            const uint4 kk = *p;
+            const uint32_t w[4] = {kk.x, kk.y, kk.z, kk.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float ra, rb;
+                rope_turn(__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xFFFF0000u),
+                          cs[i], sn[i], ra, rb);
+                o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ra) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << 16);
+            }
+            *p = make_uint4(o[0], o[1], o[2], o[3]);
+        } else {
+            uint16_t *hx = xt + h * a.head_dim + 4 * q;
+            uint2 *qa = reinterpret_cast<uint2 *>(hx);
+            uint2 *qb = reinterpret_cast<uint2 *>(hx + half);
+            const uint2 pa = *qa, pb = *qb;
+            const uint32_t wa[2] = {pa.x, pa.y}, wb[2] = {pb.x, pb.y};
+            uint32_t oa[2] = {0u, 0u}, ob[2] = {0u, 0u};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t xa = (wa[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                const uint32_t xb = (wb[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                float ra, rb;
+                rope_turn(__uint_as_float(xa << 16), __uint_as_float(xb << 16), cs[i], sn[i], ra,
+                          rb);
+                oa[i >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ra) << (16 * (i & 1));
+                ob[i >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << (16 * (i & 1));
+            }
+            *qa = make_uint2(oa[0], oa[1]);
+            *qb = make_uint2(ob[0], ob[1]);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream)
 {
     const int64_t groups = (a.num_tokens + kWavesPerGroup - 1) / kWavesPerGroup;
-    hipLaunchKernelGGL(cache_write_kernel, dim3((unsigned)groups), dim3(64 * kWavesPerGroup), 0,
-                       stream, a);
+    if (a.positions)
+        hipLaunchKernelGGL(cache_write_kernel<true>, dim3((unsigned)groups),
+                           dim3(64 * kWavesPerGroup), 0, stream, a);
+    else
+        hipLaunchKernelGGL(cache_write_kernel<false>, dim3((unsigned)groups),
+                           dim3(64 * kWavesPerGroup), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope(const RopeArgs &a, hipStream_t stream)
+{
+    const int64_t groups = (a.num_tokens + kWavesPerGroup - 1) / kWavesPerGroup;
+    hipLaunchKernelGGL(rope_kernel, dim3((unsigned)groups), dim3(64 * kWavesPerGroup), 0, stream,
+                       a);
     return hipGetLastError();
 }
 

@@ -68,6 +68,59 @@ tv_status tv_cache_write(const uint16_t *k, const uint16_t *v, uint16_t *k_cache
     return from_hip(tv::launch_cache_write(a, static_cast<hipStream_t>(stream)));
 }
 
+tv_status tv_cache_write_rope(const uint16_t *k, const uint16_t *v, uint16_t *k_cache,
+                              uint16_t *v_cache, const int64_t *slot_mapping,
+                              const int32_t *positions, const float *inv_freq,
+                              int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int64_t num_blocks, int32_t rope_style,
+                              void *stream)
+{
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks <= 0 || (rope_style != 0 && rope_style != 1))
+        return TV_ERR_SHAPE;
+    if (num_tokens == 0)
+        return TV_OK;
+    if (!k || !v || !k_cache || !v_cache || !slot_mapping || !positions || !inv_freq)
+        return TV_ERR_NULL;
+    if (head_dim % 8 != 0 || head_dim > 128)
+        return TV_ERR_UNSUPPORTED;
+    if (num_blocks > INT64_MAX / block_size)
+        return TV_ERR_SHAPE;
+    if ((int64_t)num_kv_heads * head_dim > (1 << 24))
+        return TV_ERR_UNSUPPORTED;
+    if (ceil_div(num_tokens, 4) > 0x7fffffff)
+        return TV_ERR_UNSUPPORTED;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 2) ||
+        !aligned(slot_mapping, 8) || !aligned(positions, 4) || !aligned(inv_freq, 4))
+        return TV_ERR_ALIGNMENT;
+    tv::CacheWriteArgs a{k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
+                         head_dim, block_size, num_blocks * block_size};
+    a.positions = positions;
+    a.inv_freq = inv_freq;
+    a.rope_style = rope_style;
+    return from_hip(tv::launch_cache_write(a, static_cast<hipStream_t>(stream)));
+}
+
+tv_status tv_rope(uint16_t *x, const int32_t *positions, const float *inv_freq,
+                  int64_t num_tokens, int32_t num_heads, int32_t head_dim, int32_t rope_style,
+                  void *stream)
+{
+    if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0 || (rope_style != 0 && rope_style != 1))
+        return TV_ERR_SHAPE;
+    if (num_tokens == 0)
+        return TV_OK;
+    if (!x || !positions || !inv_freq)
+        return TV_ERR_NULL;
+    if (head_dim % 8 != 0 || head_dim > 128 || (int64_t)num_heads * head_dim > (1 << 24))
+        return TV_ERR_UNSUPPORTED;
+    if (ceil_div(num_tokens, 4) > 0x7fffffff)
+        return TV_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(positions, 4) || !aligned(inv_freq, 4))
+        return TV_ERR_ALIGNMENT;
+    tv::RopeArgs a{x, positions, inv_freq, num_tokens, num_heads, head_dim, rope_style};
+    return from_hip(tv::launch_rope(a, static_cast<hipStream_t>(stream)));
+}
+
 namespace {
 
 // Checks shared by both decode entry points; fills `a` on success.  Returns

@@ -24,6 +24,20 @@ struct CacheWriteArgs {
     int32_t head_dim;
     int32_t block_size;
     int64_t num_slots;          // num_blocks * block_size
+    // Rotary embedding of K on the way in; positions == nullptr: plain copy.
+    const int32_t *positions;   // [num_tokens]
+    const float *inv_freq;      // [head_dim / 2]
+    int32_t rope_style;         // 0: pairs (2k, 2k+1); 1: pairs (k, k + head_dim/2)
+};
+
+struct RopeArgs {
+    uint16_t *x;                // [num_tokens][num_heads][head_dim], rotated in place
+    const int32_t *positions;
+    const float *inv_freq;
+    int64_t num_tokens;
+    int32_t num_heads;
+    int32_t head_dim;
+    int32_t style;
 };
 
 struct DecodeArgs {
@@ -94,6 +108,7 @@ struct BlockCopyArgs {
 };
 
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream);
+hipError_t launch_rope(const RopeArgs &a, hipStream_t stream);
 hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t stream);
 hipError_t launch_paged_prefill(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream);

@@ -161,6 +161,43 @@ def test_prefill_validation(lib):
         assert _pre(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT, i
 
 
+def _cwr(lib, T=4, hkv=8, d=64, bs=16, nb=8, style=0, ptrs=(BAD,) * 7):
+    return lib.tv_cache_write_rope(*ptrs, T, hkv, d, bs, nb, style, None)
+
+
+def _rope(lib, T=4, h=8, d=64, style=0, ptrs=(BAD,) * 3):
+    return lib.tv_rope(*ptrs, T, h, d, style, None)
+
+
+def test_rope_validation(lib):
+    assert _cwr(lib, T=-1) == TV_ERR_SHAPE
+    assert _cwr(lib, style=2) == TV_ERR_SHAPE
+    assert _cwr(lib, nb=0) == TV_ERR_SHAPE
+    assert _cwr(lib, T=0) == TV_OK
+    assert _cwr(lib, d=12) == TV_ERR_UNSUPPORTED
+    assert _cwr(lib, d=136) == TV_ERR_UNSUPPORTED
+    assert _cwr(lib) == TV_ERR_ALIGNMENT
+    for i in range(7):
+        ptrs = [ALIGNED] * 7
+        ptrs[i] = None
+        assert _cwr(lib, ptrs=tuple(ptrs)) == TV_ERR_NULL, i
+    for i, bad in ((0, 0x1008), (4, 0x1004), (5, 0x1002), (6, 0x1001)):   # k, slots, positions, inv_freq
+        ptrs = [ALIGNED] * 7
+        ptrs[i] = bad
+        assert _cwr(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT, i
+    assert _rope(lib, T=-1) == TV_ERR_SHAPE
+    assert _rope(lib, style=-1) == TV_ERR_SHAPE
+    assert _rope(lib, T=0) == TV_OK
+    assert _rope(lib, d=20) == TV_ERR_UNSUPPORTED
+    assert _rope(lib) == TV_ERR_ALIGNMENT
+    for i in range(3):
+        ptrs = [ALIGNED] * 3
+        ptrs[i] = None
+        assert _rope(lib, ptrs=tuple(ptrs)) == TV_ERR_NULL, i
+    ptrs = [0x1008, ALIGNED, ALIGNED]
+    assert _rope(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
+
+
 def _copy(lib, n=3, hkv=8, d=64, bs=16, nb=8, ptrs=(BAD,) * 3):
     return lib.tv_copy_blocks(*ptrs, n, hkv, d, bs, nb, None)
 
