@@ -3,20 +3,27 @@
 // blocks).  A pure bit copy, or with K turned by the rotary position
 // embedding on the way in (and the same rotation in place for q).
 //
-// One wavefront per token.  A token's K (or V) is num_kv_heads * head_dim bf16
-// values, contiguous in the input; lanes take 16-byte chunks (8 values of one
-// head, since head_dim % 8 == 0).  The K tile of a (block, head) is stored as
-// head_dim / 8 chunks of [block_size tokens][8 dims], so each K chunk is one
-// 16-byte store at (chunk, token offset); V values go to 8 consecutive rows of
-// the dimension-major V tile, one 2-byte store each.
+// A token's K (or V) is num_kv_heads * head_dim bf16 values, contiguous in
+// the input; lanes take 16-byte chunks (8 values of one head, since head_dim %
+// 8 == 0).  The K tile of a (block, head) is stored as head_dim / 8 chunks of
+// [block_size tokens][8 dims], so each K chunk is one 16-byte store at
+// (chunk, token offset); the V tile is dimension-major [head_dim][block_size].
 #include "rope_math.h"
 #include "tv_internal.h"
 
 namespace tv {
 namespace {
 
-constexpr int kWavesPerGroup = 4;
+constexpr int kWavesPerGroup = 4;      // tokens per workgroup of the in-place RoPE kernel
+constexpr int kTokensPerGroup = 16;    // tokens (one wavefront each) per cache-write workgroup
 
+// One wavefront per token, 16 consecutive tokens per workgroup.  K goes out
+// per token as 16-byte chunk stores.  V: when the 16 tokens fill one whole
+// block in order (slots 16b .. 16b + 15, the common case of a prompt), their
+// V rows are staged in LDS and every thread writes one 16-byte run of 8
+// tokens of one dim of the dimension-major V tile; otherwise each token's V
+// goes out as 2-byte stores down its column.
+//
 // ROPE: K is turned by the rotary embedding of positions[tok] before the
 // store (see rope_math.h).  Lanes 0 .. head_dim/2 - 1 compute the token's
 // (cos, sin) per pair once; a lane handling pairs 4q .. 4q+3 of a head (q =
@@ -25,28 +32,44 @@ constexpr int kWavesPerGroup = 4;
 // q is the 16-byte chunk q of the head; style 1 pairs (k, k + head_dim/2), so
 // group q is dims 4q .. 4q+3 and their partners, two 8-byte pieces.
 template <bool ROPE>
-__global__ __launch_bounds__(64 * kWavesPerGroup) void cache_write_kernel(CacheWriteArgs a)
+__global__ __launch_bounds__(64 * kTokensPerGroup) void cache_write_kernel(CacheWriteArgs a)
 {
-    const int64_t tok = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
-    if (tok >= a.num_tokens)
-        return;
+    __shared__ int64_t s_slot[kTokensPerGroup];
+    __shared__ uint4 s_v[kTokensPerGroup * 64];              // V rows of a full block (<= 512 values each)
+    const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
+    const int64_t tok = (int64_t)blockIdx.x * kTokensPerGroup + w;
+    const bool live_tok = tok < a.num_tokens;
     const int row = a.num_kv_heads * a.head_dim;
     const int chunks = row >> 3;
     const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.k + tok * row);
     const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.v + tok * row);
     // The first chunk of each lane is loaded together with the slot number, so
     // the common case (num_kv_heads * head_dim <= 512) waits on memory once.
-    const bool have0 = lane < chunks;
+    const bool have0 = live_tok && lane < chunks;
     const uint4 k0 = have0 ? ksrc[lane] : make_uint4(0, 0, 0, 0);
     const uint4 v0 = have0 ? vsrc[lane] : make_uint4(0, 0, 0, 0);
-    const int64_t slot = a.slot_mapping[tok];
-    if (slot < 0 || slot >= a.num_slots)
-        return;
-    const int64_t blk = slot / a.block_size;
-    const int off = (int)(slot - blk * a.block_size);
+    const int64_t slot = live_tok ? a.slot_mapping[tok] : -1;
+    if (lane == 0)
+        s_slot[w] = slot;
+    // A full block: 16 tokens, slots 16b .. 16b + 15 in order, V rows that fit
+    // in LDS, and a V pool aligned for 16-byte stores.
+    bool full = row <= 512 && a.block_size == kTokensPerGroup &&
+                (reinterpret_cast<uintptr_t>(a.v_cache) & 15) == 0;
+    __syncthreads();
+    const int64_t s0 = s_slot[0];
+    full = full && s0 >= 0 && s0 % kTokensPerGroup == 0 && s0 + kTokensPerGroup <= a.num_slots;
+#pragma unroll
+    for (int i = 1; i < kTokensPerGroup; ++i)
+        full = full && s_slot[i] == s0 + i;
+    if (full && lane < chunks)
+        s_v[w * 64 + lane] = v0;
+
+    const bool write = slot >= 0 && slot < a.num_slots;
+    const int64_t blk = write ? slot / a.block_size : 0;
+    const int off = write ? (int)(slot - blk * a.block_size) : 0;
     float pc = 1.f, ps = 0.f;
-    if (ROPE) {
+    if (ROPE && live_tok) {
         const int half = a.head_dim >> 1;
         rope_cos_sin(a.positions[tok], a.inv_freq[lane % half], pc, ps);
     }
@@ -61,9 +84,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void cache_write_kernel(CacheW
                 sn[i] = __shfl(ps, 4 * q + i);
             }
         }
-        if (c >= chunks)
+        if (!write || c >= chunks)
             continue;
-        const uint4 vv = c == lane ? v0 : vsrc[c];
         const int h = (c << 3) / a.head_dim;
         const int d = (c << 3) - h * a.head_dim;
         const int64_t tile = blk * a.num_kv_heads + h;
@@ -74,12 +96,12 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void cache_write_kernel(CacheW
         } else if (a.rope_style == 0) {
             // Pairs (d + 2i, d + 2i + 1), i < 4: one 16-byte chunk in and out.
             const uint4 kk = c == lane ? k0 : ksrc[c];
-            const uint32_t w[4] = {kk.x, kk.y, kk.z, kk.w};
+            const uint32_t wd[4] = {kk.x, kk.y, kk.z, kk.w};
             uint32_t o[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float ra, rb;
-                rope_turn(__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xFFFF0000u),
+                rope_turn(__uint_as_float(wd[i] << 16), __uint_as_float(wd[i] & 0xFFFF0000u),
                           cs[i], sn[i], ra, rb);
                 o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ra) |
                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << 16);
@@ -111,13 +133,37 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void cache_write_kernel(CacheW
             *reinterpret_cast<uint2 *>(ktile + ((int64_t)(db >> 3) * a.block_size + off) * 8 +
                                        (db & 7)) = make_uint2(ob[0], ob[1]);
         }
+        if (full)
+            continue;
+        const uint4 vv = c == lane ? v0 : vsrc[c];
         uint16_t *vdst = a.v_cache + (tile * a.head_dim + d) * a.block_size + off;
-        const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+        const uint32_t wd[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint32_t word = w[i >> 1];
+            const uint32_t word = wd[i >> 1];
             vdst[(int64_t)i * a.block_size] = (uint16_t)((i & 1) ? (word >> 16) : (word & 0xFFFFu));
         }
+    }
+    if (!full)
+        return;
+    // Full block: thread t writes tokens 8 (t & 1) .. + 7 of dim d = (t / 2) %
+    // head_dim of head t / (2 head_dim), 16 bytes of the V tile.
+    __syncthreads();
+    const uint16_t *sv = reinterpret_cast<const uint16_t *>(s_v);
+    const int64_t vblk = s0 / kTokensPerGroup;
+    for (int t = threadIdx.x; t < 2 * row; t += 64 * kTokensPerGroup) {
+        const int e = t >> 1;                                  // h * head_dim + d
+        const int t0 = 8 * (t & 1);
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = (uint32_t)sv[(t0 + 2 * i) * 512 + e] |
+                   ((uint32_t)sv[(t0 + 2 * i + 1) * 512 + e] << 16);
+        const int h = e / a.head_dim;
+        const int d = e - h * a.head_dim;
+        *reinterpret_cast<uint4 *>(a.v_cache + ((vblk * a.num_kv_heads + h) * a.head_dim + d) *
+                                                   a.block_size + t0) =
+            make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
 
@@ -187,13 +233,13 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void rope_kernel(RopeArgs a)
 
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream)
 {
-    const int64_t groups = (a.num_tokens + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int64_t groups = (a.num_tokens + kTokensPerGroup - 1) / kTokensPerGroup;
     if (a.positions)
         hipLaunchKernelGGL(cache_write_kernel<true>, dim3((unsigned)groups),
-                           dim3(64 * kWavesPerGroup), 0, stream, a);
+                           dim3(64 * kTokensPerGroup), 0, stream, a);
     else
         hipLaunchKernelGGL(cache_write_kernel<false>, dim3((unsigned)groups),
-                           dim3(64 * kWavesPerGroup), 0, stream, a);
+                           dim3(64 * kTokensPerGroup), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -1,0 +1,100 @@
+"""The cache write's two V paths on the GPU, against the oracle's cache write.
+
+Sixteen consecutive tokens that fill one block in order take the staged path
+(V tile rows written 16 bytes at a time); any other group takes the
+per-token path.  One call here mixes both, plus a ragged tail and a V pool
+that is only 2-byte aligned (which must fall back to the per-token path),
+with and without RoPE.  Pools are compared bit for bit (K within the RoPE
+bound of tests/test_gpu_rope.py when rotated).
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from paged_kv_cache_tv_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+NB, HKV, D, BS = 12, 8, 64, 16
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import paged_kv_cache_tv_amd as tv
+    tv.lib()
+    return torch.device("cuda:0")
+
+
+def _to_dev(a, dev):
+    import torch
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def _slots():
+    g = []
+    g.append(3 * BS + np.arange(BS))                       # full block, in order
+    g.append(5 * BS + np.arange(BS)[::-1])                 # one block, reversed: per token
+    s = 7 * BS + np.arange(BS)
+    s[9] = -1                                              # one token skipped: per token
+    g.append(s)
+    g.append(1 * BS + np.arange(BS))                       # full block, in order
+    g.append(np.concatenate([10 * BS + np.arange(8, 16), 11 * BS + np.arange(8)]))  # two blocks
+    g.append(9 * BS + np.arange(7))                        # ragged tail
+    return np.concatenate(g).astype(np.int64)
+
+
+def _pools(dev, aligned):
+    import torch
+    import paged_kv_cache_tv_amd as tv
+    kc, vc = tv.new_pools(NB, HKV, D, BS, dev, fill=W.BF16_NAN)
+    if aligned:
+        return kc, vc
+    n = vc.numel()
+    buf = torch.full((n + 8,), W.BF16_NAN, dtype=torch.int16, device=dev)
+    vc2 = buf[1:1 + n].view(vc.shape)                      # 2-byte aligned only
+    assert vc2.data_ptr() % 16 != 0
+    return kc, vc2
+
+
+@pytest.mark.parametrize("aligned", [True, False], ids=["v-aligned", "v-2-byte"])
+@pytest.mark.parametrize("rope_style", [None, 0, 1], ids=["plain", "rope0", "rope1"])
+def test_cache_write_paths(dev, oracle_lib, aligned, rope_style):
+    import torch
+    import paged_kv_cache_tv_amd as tv
+    from test_gpu_rope import _check_rotated
+    rng = np.random.default_rng(110)
+    slots = _slots()
+    T = len(slots)
+    k = W.round_to_bf16_bits(rng.standard_normal((T, HKV, D)).astype(np.float32))
+    v = W.round_to_bf16_bits(rng.standard_normal((T, HKV, D)).astype(np.float32))
+    pos = rng.integers(0, 70000, T).astype(np.int32)
+    f = tv.rope_inv_freq(D, 500000.0)
+    kc, vc = _pools(dev, aligned)
+    if rope_style is None:
+        tv.cache_write(_to_dev(k, dev), _to_dev(v, dev), kc, vc, _to_dev(slots, dev))
+        kin = k
+    else:
+        tv.cache_write_rope(_to_dev(k, dev), _to_dev(v, dev), kc, vc, _to_dev(slots, dev),
+                            _to_dev(pos, dev), _to_dev(f, dev), rope_style)
+        kin = oracle_lib.rope(k, pos, f, rope_style)[1]
+    torch.cuda.synchronize()
+    kr, vr = O.Oracle.new_pools(NB, HKV, D, BS)
+    oracle_lib.cache_write(kin, v, kr, vr, slots)
+    kc_h, vc_h = kc.cpu().numpy().view(np.uint16), vc.cpu().numpy().view(np.uint16)
+    assert np.array_equal(vc_h, vr), "V pool"
+    if rope_style is None:
+        assert np.array_equal(kc_h, kr), "K pool"
+        return
+    live = slots >= 0
+    blk, off = slots[live] // BS, slots[live] % BS
+    mask = np.ones(kc_h.shape, bool)
+    mask[blk, :, :, off, :] = False
+    assert np.array_equal(kc_h[mask], kr[mask]), "K outside the written slots"
+    got_k = kc_h[blk, :, :, off, :].reshape(live.sum(), HKV, D)
+    _check_rotated(oracle_lib, got_k, k[live], pos[live], f, rope_style, "K of both paths")
