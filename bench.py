@@ -262,6 +262,51 @@ def rope_rate(tv, dev, stream, flush, steps, index=3):
     return res
 
 
+def shared_prefix_rate(tv, dev, stream, flush, steps):
+    """The partition pass on the shared-prefix workload (64 prompts x 4
+    samples, 1024 shared tokens): per sequence (tv_paged_attention_decode)
+    against groups of 4 (tv_paged_attention_decode_shared), cold, events
+    around each launch.  Bytes: the K/V each path must read at least --
+    logical (every sequence's context) and unique (shared blocks once)."""
+    import torch
+    from paged_kv_cache_tv_amd import workloads as W
+    from paged_kv_cache_tv_amd.step import DeviceBatch
+    b = W.make_workload(4)
+    db = DeviceBatch(b, dev)
+    db.fill()
+    shared = torch.full((b.num_seqs // 4,), 1024, dtype=torch.int32, device=dev)
+    pa, pm, ps = db.workspace
+
+    def plain():
+        tv.paged_attention_decode(pa, pm, ps, db.q, db.k_cache, db.v_cache, db.block_tables,
+                                  db.context_lens, db.max_context_len, db.partition_size,
+                                  b.scale, stream)
+
+    def grouped():
+        tv.paged_attention_decode_shared(pa, pm, ps, db.q, db.k_cache, db.v_cache,
+                                         db.block_tables, db.context_lens, shared, 4,
+                                         db.max_context_len, db.partition_size, b.scale, stream)
+
+    res = {"workload": b.name, "group_size": 4, "shared_tokens": 1024,
+           "kv_bytes_logical": b.kv_bytes_logical(), "kv_bytes_unique": b.kv_bytes_unique()}
+    for name, fn in (("per_sequence", plain), ("shared", grouped)):
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i, (e0, e1) in enumerate(ev):
+            flush(i)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+        res[name + "_us"] = round(ms * 1e3, 2)
+    res["unique_GB_per_s_shared"] = round(b.kv_bytes_unique() / (res["shared_us"] * 1e-6) / 1e9, 1)
+    del db
+    return res
+
+
 def cpu_baseline(batch, target_seconds: float):
     """Time the CPU oracle doing the same step (cache write + attention) on this host."""
     import oracle as O
@@ -485,6 +530,7 @@ def main(argv=None):
     if not args.no_prefill:
         result["prefill"] = prefill_rate(tv, dev, stream, flush, K)
         result["rope"] = rope_rate(tv, dev, stream, flush, K)
+        result["shared_prefix"] = shared_prefix_rate(tv, dev, stream, flush, K)
 
     if not args.no_cpu_baseline:
         ref, times, threads = cpu_baseline(batch, args.cpu_seconds)

@@ -199,6 +199,39 @@ tv_status tv_paged_attention_decode(float *part_acc, float *part_max, float *par
                                     float scale, void *stream);
 
 /*
+ * Partition pass for sequences that share a prompt prefix ("vLLM" page,
+ * section "가상 메모리 방식의 해결": the samples of one prompt share its
+ * blocks).  The same partials as tv_paged_attention_decode; the shared
+ * prefix's tiles are read once per group instead of once per sequence.
+ *
+ * Sequences g*group_size .. min((g+1)*group_size, num_seqs) - 1 form group g.
+ * With sh = min(shared_len[g], context length of every member of g), the
+ * partitions p < floor(sh / partition_size) of the group's members are
+ * computed together from the block table of the group's first sequence.
+ * Precondition: for those positions every member's table holds the same
+ * blocks as the first member's (as after tv_bm_fork).  Then the partials are
+ * those of tv_paged_attention_decode bit for bit.  shared_len[g] = 0 (or
+ * group_size 1) leaves a group to the per-sequence pass.
+ *
+ *   shared_len   int32 [ceil(num_seqs / group_size)] (device), 4-byte aligned
+ *   group_size   1 .. 16 / (num_q_heads / num_kv_heads)  (4 for groups of 4 heads)
+ *   other arguments as for tv_paged_attention_decode.
+ * Errors: as for tv_paged_attention_decode, plus TV_ERR_SHAPE for
+ * group_size < 1, TV_ERR_UNSUPPORTED for a group too large for one MFMA's 16
+ * columns, TV_ERR_NULL for a NULL shared_len.
+ */
+tv_status tv_paged_attention_decode_shared(float *part_acc, float *part_max, float *part_sum,
+                                           const uint16_t *q, const uint16_t *k_cache,
+                                           const uint16_t *v_cache, const int32_t *block_tables,
+                                           const int32_t *context_lens, const int32_t *shared_len,
+                                           int32_t group_size, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t max_blocks_per_seq, int64_t num_blocks,
+                                           int32_t max_context_len, int32_t partition_size,
+                                           float scale, void *stream);
+
+/*
  * Partition pass with the cache write folded in (the same two steps as
  * tv_cache_write of one new token per sequence followed by
  * tv_paged_attention_decode, in one launch).

@@ -10,11 +10,13 @@ from .binding import (LIB_PATH, BlockManager, TvError, cache_write, cache_write_
                       copy_blocks, lib, rope, rope_inv_freq,
                       load_library, new_pools,
                       new_workspace, num_partitions, paged_attention, paged_attention_decode,
-                      paged_attention_decode_append, paged_attention_prefill,
+                      paged_attention_decode_append, paged_attention_decode_shared,
+                      paged_attention_prefill,
                       paged_attention_reduce)
 
 __all__ = ["LIB_PATH", "BlockManager", "TvError", "cache_write", "cache_write_rope",
            "copy_blocks", "lib", "rope", "rope_inv_freq",
            "load_library", "new_pools",
            "new_workspace", "num_partitions", "paged_attention", "paged_attention_decode",
-           "paged_attention_decode_append", "paged_attention_prefill", "paged_attention_reduce"]
+           "paged_attention_decode_append", "paged_attention_decode_shared",
+           "paged_attention_prefill", "paged_attention_reduce"]

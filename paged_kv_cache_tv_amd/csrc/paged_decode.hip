@@ -152,16 +152,49 @@ __device__ __forceinline__ void attend_tile(const Tile &t, bf16x8 qb0, bf16x8 qb
 // the token's K/V of its head into the pools, and -- when that slot is the one
 // the block table gives for position n-1 -- attends to the new values straight
 // from registers, so no other workgroup and no earlier kernel is involved.
-template <bool APPEND>
+//
+// Shared prefixes (a.shared_len != nullptr): sequences g*group_size ..
+// g*group_size + group_size - 1 form group g, and the partitions lying wholly
+// inside its first shared_len[g] tokens (clamped to every member's context)
+// hold the same blocks for all members.  SHARED: one workgroup per (group,
+// K/V head, such partition) attends for every member at once -- column r of
+// the MFMAs is query head r % G of member r / G -- reading each tile once.
+// The per-sequence pass skips those partitions.
+template <bool APPEND, bool SHARED>
 __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
 {
     const int kvh = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
     const int rest = (int)(blockIdx.x / (unsigned)a.num_kv_heads);
-    const int s = rest % a.num_seqs;
-    const int part = rest / a.num_seqs;
-
-    int n = a.context_lens[s];
-    n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
+    const int units = SHARED ? a.num_groups : a.num_seqs;
+    const int part = rest / units;
+    int s = rest % units;                      // SHARED: the group; the sequence below
+    int members = 1;
+    int n = 0;
+    if (a.shared_len) {
+        const int grp = SHARED ? s : s / a.group_size;
+        const int first = grp * a.group_size;
+        const int cnt = min(a.group_size, a.num_seqs - first);
+        int sh = a.shared_len[grp];
+        for (int m = 0; m < cnt; ++m) {
+            int nm = a.context_lens[first + m];
+            nm = nm < 0 ? 0 : (nm > a.max_context_len ? a.max_context_len : nm);
+            sh = min(sh, nm);
+        }
+        const int shared_parts = sh > 0 ? sh / (a.part_tiles * BS) : 0;
+        if (SHARED) {
+            if (part >= shared_parts)
+                return;
+            s = first;
+            members = cnt;
+            n = shared_parts * a.part_tiles * BS;
+        } else if (part < shared_parts) {
+            return;                            // computed by the shared pass
+        }
+    }
+    if (!SHARED) {
+        n = a.context_lens[s];
+        n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
+    }
     const int first_tok = part * a.part_tiles * BS;
     if (first_tok >= n)
         return;
@@ -174,11 +207,14 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
     const float c = a.scale_log2;
     const int G = a.group;
 
-    // B operands of the score MFMAs: column r = query head kvh*G + r, rows =
-    // dims 8g..8g+7 (first MFMA) and 32+8g..32+8g+7 (second).
+    // B operands of the score MFMAs: column r = query head kvh*G + r % G of
+    // sequence s + r / G (r < G except in the shared pass), rows = dims
+    // 8g..8g+7 (first MFMA) and 32+8g..32+8g+7 (second).
+    const int col_seq = s + r / G;
+    const bool col_ok = SHARED ? r < members * G : r < G;
     bf16x8 qb0 = {}, qb1 = {};
-    if (r < G) {
-        const uint16_t *qp = a.q + ((int64_t)s * a.num_kv_heads * G + (int64_t)kvh * G + r) * D + g * 8;
+    if (col_ok) {
+        const uint16_t *qp = a.q + ((int64_t)col_seq * a.num_kv_heads * G + (int64_t)kvh * G + r % G) * D + g * 8;
         qb0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp));
         qb1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 32));
     }
@@ -303,9 +339,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
 
-    if (r < G) {
+    if (col_ok) {
         const int hq = a.num_kv_heads * G;
-        const int64_t row = ((int64_t)s * hq + (int64_t)kvh * G + r) * a.num_parts + part;
+        const int64_t row = ((int64_t)col_seq * hq + (int64_t)kvh * G + r % G) * a.num_parts + part;
         if (g == 0) {
             a.part_max[row] = m_run;
             a.part_sum[row] = l_run;
@@ -321,11 +357,22 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
 
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream)
 {
+    if (a.shared_len) {
+        // Shared partitions first (one workgroup per group, head and partition).
+        const int64_t shared_groups = (int64_t)a.num_kv_heads * a.num_groups * a.num_parts;
+        hipLaunchKernelGGL((paged_decode_kernel<false, true>), dim3((unsigned)shared_groups),
+                           dim3(64), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     const int64_t groups = (int64_t)a.num_kv_heads * a.num_seqs * a.num_parts;
     if (a.k_new)
-        hipLaunchKernelGGL(paged_decode_kernel<true>, dim3((unsigned)groups), dim3(64), 0, stream, a);
+        hipLaunchKernelGGL((paged_decode_kernel<true, false>), dim3((unsigned)groups), dim3(64), 0,
+                           stream, a);
     else
-        hipLaunchKernelGGL(paged_decode_kernel<false>, dim3((unsigned)groups), dim3(64), 0, stream, a);
+        hipLaunchKernelGGL((paged_decode_kernel<false, false>), dim3((unsigned)groups), dim3(64),
+                           0, stream, a);
     return hipGetLastError();
 }
 

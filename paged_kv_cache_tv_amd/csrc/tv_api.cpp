@@ -286,6 +286,41 @@ tv_status tv_paged_attention_prefill(float *out, const uint16_t *q, const int32_
     return from_hip(tv::launch_paged_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
+tv_status tv_paged_attention_decode_shared(float *part_acc, float *part_max, float *part_sum,
+                                           const uint16_t *q, const uint16_t *k_cache,
+                                           const uint16_t *v_cache, const int32_t *block_tables,
+                                           const int32_t *context_lens, const int32_t *shared_len,
+                                           int32_t group_size, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t max_blocks_per_seq, int64_t num_blocks,
+                                           int32_t max_context_len, int32_t partition_size,
+                                           float scale, void *stream)
+{
+    if (group_size < 1)
+        return TV_ERR_SHAPE;
+    if (num_kv_heads > 0 && num_q_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+        (int64_t)group_size * (num_q_heads / num_kv_heads) > tv::kMaxGroup)
+        return TV_ERR_UNSUPPORTED;
+    tv::DecodeArgs a;
+    const tv_status st = check_decode(a, part_acc, part_max, part_sum, q, k_cache, v_cache,
+                                      block_tables, context_lens, num_seqs, num_q_heads,
+                                      num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                      num_blocks, max_context_len, partition_size, scale);
+    if (st != TV_OK)
+        return st;
+    if (a.num_parts == 0)
+        return TV_OK;
+    if (!shared_len)
+        return TV_ERR_NULL;
+    if (!aligned(shared_len, 4))
+        return TV_ERR_ALIGNMENT;
+    a.shared_len = shared_len;
+    a.group_size = group_size;
+    a.num_groups = (int32_t)ceil_div(num_seqs, group_size);
+    return from_hip(tv::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
+}
+
 tv_status tv_paged_attention_reduce(float *out, const float *part_acc, const float *part_max,
                                     const float *part_sum, const int32_t *context_lens,
                                     int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,

@@ -65,6 +65,10 @@ struct DecodeArgs {
     const int64_t *slot_mapping;   // [num_seqs]
     uint16_t *k_cache_w;        // the pools again, writable
     uint16_t *v_cache_w;
+    // Shared prefixes (tv_paged_attention_decode_shared): shared_len == nullptr: none.
+    const int32_t *shared_len;  // [num_groups]: leading tokens shared by group g's sequences
+    int32_t group_size;         // sequences per group (consecutive), 1 .. 16 / group
+    int32_t num_groups;         // ceil(num_seqs / group_size)
 };
 
 struct ReduceArgs {

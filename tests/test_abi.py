@@ -132,6 +132,26 @@ def test_decode_append_validation(lib):
     assert _app(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
 
 
+def _shd(lib, S=2, hq=32, hkv=8, gs=4, mctx=64, part=32, ptrs=(BAD,) * 9):
+    return lib.tv_paged_attention_decode_shared(*ptrs, gs, S, hq, hkv, 64, 16, 4, 8, mctx, part,
+                                                0.125, None)
+
+
+def test_decode_shared_validation(lib):
+    assert _shd(lib, S=-1) == TV_ERR_SHAPE
+    assert _shd(lib, gs=0) == TV_ERR_SHAPE
+    assert _shd(lib, gs=5) == TV_ERR_UNSUPPORTED         # 5 sequences x 4 heads > 16 columns
+    assert _shd(lib, hq=64, gs=3) == TV_ERR_UNSUPPORTED  # 3 x 8 heads
+    assert _shd(lib, S=0) == TV_OK
+    assert _shd(lib, mctx=0) == TV_OK
+    assert _shd(lib) == TV_ERR_ALIGNMENT                  # the decode arguments are checked first
+    ptrs = [ALIGNED] * 9
+    ptrs[8] = None
+    assert _shd(lib, ptrs=tuple(ptrs)) == TV_ERR_NULL
+    ptrs[8] = 0x1002
+    assert _shd(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
+
+
 def _pre(lib, S=2, hq=32, hkv=8, d=64, bs=16, mb=4, nb=8, mq=40, mctx=64, scale=0.125,
          ptrs=(BAD,) * 7):
     return lib.tv_paged_attention_prefill(*ptrs, S, hq, hkv, d, bs, mb, nb, mq, mctx, scale, None)

@@ -1,0 +1,110 @@
+"""Shared-prefix decode (tv_paged_attention_decode_shared) on the GPU.
+
+Each MFMA column is computed independently, so reading a shared prefix once
+for the whole group must give the same partials, and after the merge the
+same output, as the per-sequence pass, bit for bit.  The tests compare the
+two paths on the shared-prefix workload and on ragged groups, and the output
+against the oracle.  Pools are NaN-poisoned outside the written slots.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from paged_kv_cache_tv_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import paged_kv_cache_tv_amd as tv
+    tv.lib()
+    return torch.device("cuda:0")
+
+
+def _to_dev(a, dev):
+    import torch
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def _run(b, dev, part, shared=None, group_size=1, lens=None):
+    """Both pools written, then either pass and the merge: (out, partials)."""
+    import torch
+    import paged_kv_cache_tv_amd as tv
+    lens = b.context_lens if lens is None else lens
+    kc, vc = tv.new_pools(b.num_blocks, b.num_kv_heads, b.head_dim, b.block_size, dev,
+                          fill=W.BF16_NAN)
+    for k, v, sl in (b.fill_inputs(), b.step_inputs()):
+        live = sl >= 0
+        tv.cache_write(_to_dev(k[live], dev), _to_dev(v[live], dev), kc, vc,
+                       _to_dev(sl[live], dev))
+    mc = int(lens.max())
+    ws = tv.new_workspace(b.num_seqs, b.num_q_heads, b.head_dim, mc, part, dev)
+    for t in ws:
+        t.fill_(float("nan"))
+    q, bt, cl = _to_dev(b.q, dev), _to_dev(b.block_tables, dev), _to_dev(lens, dev)
+    if shared is None:
+        tv.paged_attention_decode(*ws, q, kc, vc, bt, cl, mc, part, b.scale)
+    else:
+        tv.paged_attention_decode_shared(*ws, q, kc, vc, bt, cl, _to_dev(shared, dev), group_size,
+                                         mc, part, b.scale)
+    out = torch.empty((b.num_seqs, b.num_q_heads, b.head_dim), dtype=torch.float32, device=dev)
+    tv.paged_attention_reduce(out, *ws, cl, mc, part)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), [t.cpu().numpy() for t in ws]
+
+
+def _same_partials(pa, pb, lens, part):
+    """Partials equal bit for bit wherever the call defines them."""
+    for s, n in enumerate(lens):
+        P = -(-int(n) // part)
+        for x, y in zip(pa, pb):
+            assert np.array_equal(x[s, :, :P].view(np.uint32), y[s, :, :P].view(np.uint32)), s
+
+
+def test_shared_prefix_workload(dev, oracle_lib):
+    """64 prompts x 4 samples sharing 1024 tokens, partitions of 512: two
+    shared partitions per group."""
+    b = W.make_workload(4)
+    shared = np.full(64, 1024, np.int32)
+    out_s, part_s = _run(b, dev, 512, shared, 4)
+    out_p, part_p = _run(b, dev, 512)
+    _same_partials(part_s, part_p, b.context_lens, 512)
+    assert np.array_equal(out_s.view(np.uint32), out_p.view(np.uint32))
+    ref, _, _ = O.decode_step(oracle_lib, b)
+    err = np.abs(out_s.astype(np.float64) - ref)
+    print(f"shared-prefix workload: max_abs={err.max():.3e}", flush=True)
+    assert err.max() <= 1e-4 and err.mean() <= 1e-6
+
+
+@pytest.mark.parametrize("samples,prefix,part", [(3, 704, 64), (2, 1536, 512), (4, 512, 512),
+                                                 (4, 256, 64)])
+def test_shared_prefix_ragged_groups(dev, samples, prefix, part):
+    """Groups of 2-4, prefixes that are not a whole number of partitions, a
+    partial last group, a member whose context is cut below the prefix, and a
+    group that declares no sharing."""
+    rng = np.random.default_rng(120 + samples + part)
+    prompts = 5
+    priv = rng.integers(0, 300, prompts * samples)
+    b = W.make_shared_prefix_batch(prompts, samples, prefix, priv, 121 + prefix)
+    S = b.num_seqs - 1                               # drop the last sequence: partial last group
+    b.context_lens = b.context_lens[:S].copy()
+    b.block_tables = b.block_tables[:S]
+    b.q = b.q[:S]
+    b.new_slots = b.new_slots[:S]
+    b.new_rows = b.new_rows[:S]
+    lens = b.context_lens.copy()
+    lens[samples] = prefix // 2                      # member of group 1 cut below the prefix
+    ngroups = -(-S // samples)
+    shared = np.full(ngroups, prefix, np.int32)
+    shared[2] = 0                                    # group 2: no sharing declared
+    out_s, part_s = _run(b, dev, part, shared, samples, lens)
+    out_p, part_p = _run(b, dev, part, lens=lens)
+    _same_partials(part_s, part_p, lens, part)
+    assert np.array_equal(out_s.view(np.uint32), out_p.view(np.uint32))
