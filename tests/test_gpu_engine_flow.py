@@ -5,7 +5,9 @@ Prompts are admitted by the block manager and prefilled:
     (tv_cache_write_rope);
   * q is rotated in place (tv_rope);
   * prefill attention runs (tv_paged_attention_prefill).
-Each prompt is then forked into samples, and several decode steps follow.
+Each prompt is then forked into samples, and several decode steps follow
+(while all samples live, the shared-prefix pass is run on the same pools too
+and must reproduce the step's output bit for bit).
 Each step:
   * reserves slots and copy-on-write pairs (tv_bm_prepare_decode);
   * copies the shared blocks (tv_copy_blocks);
@@ -137,6 +139,19 @@ def test_engine_flow(dev, oracle_lib):
         print(f"decode step {step}: {S} sequences, {len(pairs)} block copies, "
               f"max_abs={err.max():.3e}", flush=True)
         assert np.isfinite(err).all() and err.max() <= 1e-3 and err.mean() <= 1e-4
+        if step < 3:
+            # Before any sample ends, rows 3i .. 3i+2 are prompt i's samples:
+            # the shared-prefix pass over the same pools must give the fused
+            # step's output bit for bit (prompt blocks never written since the
+            # fork stay shared; partial blocks were copied on write).
+            shared = np.array([(n // BS) * BS for n in prompts], np.int32)
+            ws2 = tv.new_workspace(S, HQ, D, mc, PART, dev)
+            out2 = torch.empty_like(outd)
+            tv.paged_attention_decode_shared(*ws2, qd, kc, vc, bt, cl, _to_dev(shared, dev),
+                                             SAMPLES, mc, PART, SCALE)
+            tv.paged_attention_reduce(out2, *ws2, cl, mc, PART)
+            torch.cuda.synchronize()
+            assert torch.equal(out2.view(torch.int32), outd.view(torch.int32)), step
         for r, seq in enumerate(live):
             k, v = hist[seq]
             hist[seq] = (np.concatenate([k, k_new[r:r + 1]]), np.concatenate([v, v_new[r:r + 1]]))
