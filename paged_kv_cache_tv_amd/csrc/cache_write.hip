@@ -14,15 +14,18 @@
 namespace tv {
 namespace {
 
-constexpr int kWavesPerGroup = 4;      // tokens per workgroup of the in-place RoPE kernel
-constexpr int kTokensPerGroup = 16;    // tokens (one wavefront each) per cache-write workgroup
+constexpr int kWavesPerGroup = 4;      // tokens (wavefronts) per workgroup, unstaged forms
+constexpr int kTokensPerGroup = 16;    // tokens (wavefronts) per workgroup, staged form
+constexpr int64_t kStagedFrom = 512;   // launches of at least this many tokens use the staged form
 
-// One wavefront per token, 16 consecutive tokens per workgroup.  K goes out
-// per token as 16-byte chunk stores.  V: when the 16 tokens fill one whole
-// block in order (slots 16b .. 16b + 15, the common case of a prompt), their
-// V rows are staged in LDS and every thread writes one 16-byte run of 8
-// tokens of one dim of the dimension-major V tile; otherwise each token's V
-// goes out as 2-byte stores down its column.
+// One wavefront per token.  K goes out per token as 16-byte chunk stores.
+// STAGED (launches of many tokens, e.g. a prompt): 16 consecutive tokens per
+// workgroup; when they fill one whole block in order (slots 16b .. 16b + 15)
+// their V rows are staged in LDS and every thread writes one 16-byte run of
+// 8 tokens of one dim of the dimension-major V tile.  Otherwise (and in the
+// unstaged form, 4 tokens per workgroup with no LDS and no barrier, for the
+// few tokens of a decode step) each token's V goes out as 2-byte stores down
+// its column.
 //
 // ROPE: K is turned by the rotary embedding of positions[tok] before the
 // store (see rope_math.h).  Lanes 0 .. head_dim/2 - 1 compute the token's
@@ -31,14 +34,16 @@ constexpr int kTokensPerGroup = 16;    // tokens (one wavefront each) per cache-
 // count is the same for every lane.  Style 0 pairs dims (2k, 2k+1), so group
 // q is the 16-byte chunk q of the head; style 1 pairs (k, k + head_dim/2), so
 // group q is dims 4q .. 4q+3 and their partners, two 8-byte pieces.
-template <bool ROPE>
-__global__ __launch_bounds__(64 * kTokensPerGroup) void cache_write_kernel(CacheWriteArgs a)
+template <bool ROPE, bool STAGED>
+__global__ __launch_bounds__(64 * (STAGED ? kTokensPerGroup : kWavesPerGroup))
+void cache_write_kernel(CacheWriteArgs a)
 {
-    __shared__ int64_t s_slot[kTokensPerGroup];
-    __shared__ uint4 s_v[kTokensPerGroup * 64];              // V rows of a full block (<= 512 values each)
+    constexpr int kTok = STAGED ? kTokensPerGroup : kWavesPerGroup;
+    __shared__ int64_t s_slot[STAGED ? kTokensPerGroup : 1];
+    __shared__ uint4 s_v[STAGED ? kTokensPerGroup * 64 : 1];   // V rows of a full block (<= 512 values each)
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int64_t tok = (int64_t)blockIdx.x * kTokensPerGroup + w;
+    const int64_t tok = (int64_t)blockIdx.x * kTok + w;
     const bool live_tok = tok < a.num_tokens;
     const int row = a.num_kv_heads * a.head_dim;
     const int chunks = row >> 3;
@@ -50,20 +55,26 @@ __global__ __launch_bounds__(64 * kTokensPerGroup) void cache_write_kernel(Cache
     const uint4 k0 = have0 ? ksrc[lane] : make_uint4(0, 0, 0, 0);
     const uint4 v0 = have0 ? vsrc[lane] : make_uint4(0, 0, 0, 0);
     const int64_t slot = live_tok ? a.slot_mapping[tok] : -1;
-    if (lane == 0)
-        s_slot[w] = slot;
-    // A full block: 16 tokens, slots 16b .. 16b + 15 in order, V rows that fit
-    // in LDS, and a V pool aligned for 16-byte stores.
-    bool full = row <= 512 && a.block_size == kTokensPerGroup &&
-                (reinterpret_cast<uintptr_t>(a.v_cache) & 15) == 0;
-    __syncthreads();
-    const int64_t s0 = s_slot[0];
-    full = full && s0 >= 0 && s0 % kTokensPerGroup == 0 && s0 + kTokensPerGroup <= a.num_slots;
+    bool full = false;
+    int64_t s0 = 0;
+    if (STAGED) {
+        if (lane == 0)
+            s_slot[w] = slot;
+        // A full block: 16 tokens, slots 16b .. 16b + 15 in order, V rows that
+        // fit in LDS, and a V pool aligned for 16-byte stores.
+        full = row <= 512 && a.block_size == kTokensPerGroup &&
+               (reinterpret_cast<uintptr_t>(a.v_cache) & 15) == 0;
+        __syncthreads();
+        s0 = s_slot[0];
+        full = full && s0 >= 0 && s0 % kTokensPerGroup == 0 && s0 + kTokensPerGroup <= a.num_slots;
 #pragma unroll
-    for (int i = 1; i < kTokensPerGroup; ++i)
-        full = full && s_slot[i] == s0 + i;
-    if (full && lane < chunks)
-        s_v[w * 64 + lane] = v0;
+        for (int i = 1; i < kTokensPerGroup; ++i)
+            full = full && s_slot[i] == s0 + i;
+        if (full && lane < chunks)
+            s_v[w * 64 + lane] = v0;
+    } else if (!live_tok) {
+        return;
+    }
 
     const bool write = slot >= 0 && slot < a.num_slots;
     const int64_t blk = write ? slot / a.block_size : 0;
@@ -144,7 +155,7 @@ __global__ __launch_bounds__(64 * kTokensPerGroup) void cache_write_kernel(Cache
             vdst[(int64_t)i * a.block_size] = (uint16_t)((i & 1) ? (word >> 16) : (word & 0xFFFFu));
         }
     }
-    if (!full)
+    if (!STAGED || !full)
         return;
     // Full block: thread t writes tokens 8 (t & 1) .. + 7 of dim d = (t / 2) %
     // head_dim of head t / (2 head_dim), 16 bytes of the V tile.
@@ -231,15 +242,26 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void rope_kernel(RopeArgs a)
 
 }  // namespace
 
+template <bool ROPE>
+void launch_cw(const CacheWriteArgs &a, hipStream_t stream)
+{
+    if (a.num_tokens >= kStagedFrom) {
+        const int64_t groups = (a.num_tokens + kTokensPerGroup - 1) / kTokensPerGroup;
+        hipLaunchKernelGGL((cache_write_kernel<ROPE, true>), dim3((unsigned)groups),
+                           dim3(64 * kTokensPerGroup), 0, stream, a);
+    } else {
+        const int64_t groups = (a.num_tokens + kWavesPerGroup - 1) / kWavesPerGroup;
+        hipLaunchKernelGGL((cache_write_kernel<ROPE, false>), dim3((unsigned)groups),
+                           dim3(64 * kWavesPerGroup), 0, stream, a);
+    }
+}
+
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream)
 {
-    const int64_t groups = (a.num_tokens + kTokensPerGroup - 1) / kTokensPerGroup;
     if (a.positions)
-        hipLaunchKernelGGL(cache_write_kernel<true>, dim3((unsigned)groups),
-                           dim3(64 * kTokensPerGroup), 0, stream, a);
+        launch_cw<true>(a, stream);
     else
-        hipLaunchKernelGGL(cache_write_kernel<false>, dim3((unsigned)groups),
-                           dim3(64 * kTokensPerGroup), 0, stream, a);
+        launch_cw<false>(a, stream);
     return hipGetLastError();
 }
 

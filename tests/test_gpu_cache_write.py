@@ -1,11 +1,13 @@
-"""The cache write's two V paths on the GPU, against the oracle's cache write.
+"""The cache write's V paths on the GPU, against the oracle's cache write.
 
-Sixteen consecutive tokens that fill one block in order take the staged path
-(V tile rows written 16 bytes at a time); any other group takes the
-per-token path.  One call here mixes both, plus a ragged tail and a V pool
-that is only 2-byte aligned (which must fall back to the per-token path),
-with and without RoPE.  Pools are compared bit for bit (K within the RoPE
-bound of tests/test_gpu_rope.py when rotated).
+In a launch of 512 tokens or more, sixteen consecutive tokens that fill one
+block in order take the staged path (V tile rows written 16 bytes at a
+time); any other group takes the per-token path, as do all tokens of
+smaller launches.  The large call here mixes both, plus a ragged tail and a
+V pool that is only 2-byte aligned (which must fall back to the per-token
+path), with and without RoPE; the small call writes the same pattern once.
+Pools are compared bit for bit (K within the RoPE bound of
+tests/test_gpu_rope.py when rotated).
 """
 
 import numpy as np
@@ -16,7 +18,7 @@ from paged_kv_cache_tv_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-NB, HKV, D, BS = 12, 8, 64, 16
+NB, HKV, D, BS = 12 * 8, 8, 64, 16
 
 
 @pytest.fixture(scope="module")
@@ -36,7 +38,15 @@ def _to_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def _slots():
+def _slots(reps):
+    out = []
+    for r in range(reps):
+        p = _pattern()
+        out.append(np.where(p >= 0, p + 12 * BS * r, p))     # skipped slots stay skipped
+    return np.concatenate(out)
+
+
+def _pattern():
     g = []
     g.append(3 * BS + np.arange(BS))                       # full block, in order
     g.append(5 * BS + np.arange(BS)[::-1])                 # one block, reversed: per token
@@ -62,14 +72,15 @@ def _pools(dev, aligned):
     return kc, vc2
 
 
+@pytest.mark.parametrize("reps", [8, 1], ids=["696-tokens", "87-tokens"])
 @pytest.mark.parametrize("aligned", [True, False], ids=["v-aligned", "v-2-byte"])
 @pytest.mark.parametrize("rope_style", [None, 0, 1], ids=["plain", "rope0", "rope1"])
-def test_cache_write_paths(dev, oracle_lib, aligned, rope_style):
+def test_cache_write_paths(dev, oracle_lib, aligned, rope_style, reps):
     import torch
     import paged_kv_cache_tv_amd as tv
     from test_gpu_rope import _check_rotated
     rng = np.random.default_rng(110)
-    slots = _slots()
+    slots = _slots(reps)
     T = len(slots)
     k = W.round_to_bf16_bits(rng.standard_normal((T, HKV, D)).astype(np.float32))
     v = W.round_to_bf16_bits(rng.standard_normal((T, HKV, D)).astype(np.float32))
