@@ -10,10 +10,16 @@
 // triple is written for the merge kernel.
 //
 // Mapping to CDNA4:
-//   * One wavefront (a 64-thread workgroup) per (sequence, K/V head,
-//     partition).  The launch index runs K/V head fastest, so the workgroups
-//     reading one physical block land on the same XCD (dispatch is round-robin
-//     over the 8 XCDs) when several sequences share it.
+//   * One workgroup per (sequence, K/V head, partition), of 4 wavefronts or
+//     of 1 (the launch policy is at launch_paged_decode).  The launch index
+//     runs K/V head fastest, so with 8 K/V heads each head's workgroups run
+//     on one XCD (dispatch is round-robin over the 8 XCDs) and workgroups
+//     reading one shared physical block share that XCD's L2.  Within an XCD
+//     the dispatcher deals consecutive workgroups round-robin over its
+//     compute units, each wavefront to the next SIMD; a SIMD's finishing time
+//     follows the tiles it was dealt.  With 4 wavefronts the partition's
+//     tiles are split evenly over the CU's 4 SIMDs.  With 1, large grids
+//     take a balanced order derived from the context lengths (plan_unit).
 //   * One block of one K/V head is a 2 KiB K tile, stored as 8 chunks of
 //     [16 tokens][8 dims], plus a 2 KiB V tile [64 dims][16 tokens].  Each
 //     K load instruction reads 1 KiB contiguous (lane l: bytes 16l..16l+15 of
@@ -37,11 +43,15 @@
 //   * exp is computed as 2^x (v_exp_f32) with scale*log2(e) folded into the
 //     scores; the running maximum is kept in those base-2 units.  The only
 //     cross-lane traffic is the max over the 4 lane groups (2 shuffles per
-//     tile) and one final sum; no barrier.  (LDS holds only the appended
-//     token's row in the append variant.)
+//     tile) and one final sum; no barrier inside the tile loop.  LDS holds
+//     the appended token's row in the append variant and, with 4 wavefronts,
+//     the wavefronts' (max, sum, output) for the one barrier at the end.
 #include "tv_internal.h"
 
 #include <math.h>
+
+#include <atomic>
+#include <numeric>
 
 namespace tv {
 namespace {
@@ -147,6 +157,116 @@ __device__ __forceinline__ void attend_tile(const Tile &t, bf16x8 qb0, bf16x8 qb
     o[3] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v3, plo, o[3], 0, 0, 0);
 }
 
+constexpr int kPlanChunks = 4;            // the balanced order serves up to 4 x 64 sequences
+
+__device__ __forceinline__ int wave_scan_incl(int x, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d)
+            x += y;
+    }
+    return x;
+}
+
+struct Unit {
+    int s;       // sequence (-1: this workgroup has no partition)
+    int part;
+};
+
+// The partition that workgroup j of a K/V head takes in the balanced order.
+// The work is every partition of every sequence; a partition's cost is its
+// tile count.  Consecutive workgroups of a head are dealt round-robin over
+// a.plan_width compute units, so the order is:
+//   1. every partition that is not its sequence's last one (all full-sized),
+//      sequence by sequence;
+//   2. the sequences' last partitions from the largest to the smallest (ties:
+//      lower sequence first), placed along a path that runs forward over the
+//      CUs in one round and backward in the next, so a CU that got a large
+//      one gets a small one next;
+//   3. workgroups past the work (none).
+// Every workgroup computes the same order from the same lengths, so each
+// partition is taken exactly once.  num_seqs <= 64 * kPlanChunks.
+__device__ Unit plan_unit(const DecodeArgs &a, int j, int lane)
+{
+    const int PT = a.part_tiles;
+    int len[kPlanChunks];
+#pragma unroll
+    for (int k = 0; k < kPlanChunks; ++k) {
+        const int s = k * 64 + lane;
+        len[k] = s < a.num_seqs ? a.context_lens[s] : 0;
+    }
+    int last[kPlanChunks], nparts[kPlanChunks];
+    int F = 0, L = 0;                            // partitions in step 1; sequences in step 2
+    Unit u = {-1, 0};
+#pragma unroll
+    for (int k = 0; k < kPlanChunks; ++k) {
+        int n = len[k];
+        n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
+        const int tiles = (n + BS - 1) / BS;
+        const int P = (tiles + PT - 1) / PT;
+        const int nonlast = P > 0 ? P - 1 : 0;
+        nparts[k] = P;
+        last[k] = P > 0 ? tiles - nonlast * PT : 0;
+        const int incl = wave_scan_incl(nonlast, lane);
+        const int excl = incl - nonlast;
+        const uint64_t m = __ballot(j >= F + excl && j < F + incl);
+        if (u.s < 0 && m) {
+            const int l = (int)__builtin_ctzll(m);
+            u.s = k * 64 + l;
+            u.part = j - F - __builtin_amdgcn_readlane(excl, l);
+        }
+        F += __builtin_amdgcn_readlane(incl, 63);
+        L += (int)__popcll(__ballot(P > 0));
+    }
+    if (u.s >= 0 || j >= F + L)
+        return u;
+
+    // Position t of j along the path over positions F .. F+L-1: rounds of C
+    // positions, forward in the first round (which starts at F) and
+    // alternating after it; the last round may be partial.
+    const int C = a.plan_width;
+    const int E = F + L;
+    const int r = j / C, c = j - r * C;
+    const int lo = max(F, r * C) - r * C;
+    const int hi = min(E, (r + 1) * C) - r * C - 1;
+    const int t = (max(r * C, F) - F) + (((r - F / C) & 1) ? hi - c : c - lo);
+
+    // The t-th largest last partition: the largest size b with more than t
+    // last partitions of size >= b, then the right one among those of size b.
+    auto count_ge = [&](int b) {
+        int cnt = 0;
+#pragma unroll
+        for (int k = 0; k < kPlanChunks; ++k)
+            cnt += (int)__popcll(__ballot(last[k] >= b));
+        return cnt;
+    };
+    int blo = 1, bhi = PT;
+    while (blo < bhi) {
+        const int mid = (blo + bhi + 1) >> 1;
+        if (count_ge(mid) > t)
+            blo = mid;
+        else
+            bhi = mid - 1;
+    }
+    int rank = t - count_ge(blo + 1);
+#pragma unroll
+    for (int k = 0; k < kPlanChunks; ++k) {
+        uint64_t m = __ballot(last[k] == blo);
+        const int cnt = (int)__popcll(m);
+        if (u.s < 0 && rank < cnt) {
+            for (int i = 0; i < rank; ++i)
+                m &= m - 1;                      // drop the lowest set lanes
+            const int l = (int)__builtin_ctzll(m);
+            u.s = k * 64 + l;
+            u.part = __builtin_amdgcn_readlane(nparts[k], l) - 1;
+        }
+        rank -= cnt;
+    }
+    return u;
+}
+
 // APPEND: sequence s also brings a new token (k_new, v_new) for slot
 // slot_mapping[s].  The workgroup holding the sequence's last partition writes
 // the token's K/V of its head into the pools, and -- when that slot is the one
@@ -160,14 +280,29 @@ __device__ __forceinline__ void attend_tile(const Tile &t, bf16x8 qb0, bf16x8 qb
 // K/V head, such partition) attends for every member at once -- column r of
 // the MFMAs is query head r % G of member r / G -- reading each tile once.
 // The per-sequence pass skips those partitions.
-template <bool APPEND, bool SHARED>
-__global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
+//
+// SPLIT wavefronts per workgroup (1 or 4): the partition's tiles are divided
+// into SPLIT equal consecutive ranges, wavefront w attends to range w with
+// its own running (max, sum, output), and the ranges' triples are merged in
+// LDS, in range order, by the same log-sum-exp rule the merge kernel uses
+// across partitions.  With 4 wavefronts one workgroup occupies one slot on
+// each SIMD of its CU, so the CU's SIMDs share every partition's bytes
+// equally.
+template <bool APPEND, bool SHARED, bool PLAN, int SPLIT>
+__global__ __launch_bounds__(64 * SPLIT) void paged_decode_kernel(DecodeArgs a)
 {
     const int kvh = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
     const int rest = (int)(blockIdx.x / (unsigned)a.num_kv_heads);
     const int units = SHARED ? a.num_groups : a.num_seqs;
-    const int part = rest / units;
+    int part = rest / units;
     int s = rest % units;                      // SHARED: the group; the sequence below
+    if (PLAN) {
+        const Unit u = plan_unit(a, rest, (int)(threadIdx.x & 63));
+        if (u.s < 0)
+            return;
+        s = u.s;
+        part = u.part;
+    }
     int members = 1;
     int n = 0;
     if (a.shared_len) {
@@ -201,7 +336,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
     const int ptok = min(n - first_tok, a.part_tiles * BS);    // tokens in this partition
     const int ntiles = (ptok + BS - 1) / BS;
 
-    const int lane = threadIdx.x;
+    const int lane = (int)(threadIdx.x & 63);
+    const int wv = (int)(threadIdx.x >> 6);       // wavefront in the workgroup
     const int r = lane & 15;
     const int g = lane >> 4;
     const float c = a.scale_log2;
@@ -219,13 +355,22 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
         qb1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 32));
     }
 
-    // Append: the partition holding position n-1 loads the new token's K/V row
+    // This wavefront's tiles of the partition: [t_lo, t_hi).
+    int t_lo = 0, t_hi = ntiles;
+    if (SPLIT > 1) {
+        const int per = (ntiles + SPLIT - 1) / SPLIT;
+        t_lo = min(ntiles, wv * per);
+        t_hi = min(ntiles, t_lo + per);
+    }
+
+    // Append: the wavefront holding position n-1 loads the new token's K/V row
     // of this head with its first loads, stages it in LDS once its first tile
     // loads are out, replaces position n-1 with the staged row when the slot
     // is that position's (the pool copy of that slot is never read back in
     // this launch), and writes the row into the pools after its loop.
-    __shared__ uint16_t s_new[2 * D];     // K row then V row of the new token
-    const bool append_here = APPEND && first_tok + ptok == n;
+    __shared__ uint16_t s_new_all[SPLIT][2 * D];   // per wavefront: K row then V row
+    uint16_t *const s_new = s_new_all[wv];
+    const bool append_here = APPEND && first_tok + ptok == n && t_lo < t_hi && t_hi == ntiles;
     int64_t wslot = -1;                   // slot to write (-1: none)
     int32_t tblk = -1;                    // table entry of position n-1
     uint32_t new_pair = 0;                // lane l: K dims 2l, 2l+1 (l < 32) or V dims 2(l-32), +1
@@ -244,7 +389,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
     for (int j = 0; j < 4; ++j)
         o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int32_t *bt = a.block_tables + (int64_t)s * a.max_blocks + (int64_t)part * a.part_tiles;
+    const int32_t *bt = a.block_tables + (int64_t)s * a.max_blocks + (int64_t)part * a.part_tiles +
+                        t_lo;
     const char *kpool = reinterpret_cast<const char *>(a.k_cache) + (int64_t)kvh * kTileBytes;
     const char *vpool = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * kTileBytes;
     const int64_t tile_stride = (int64_t)a.num_kv_heads * kTileBytes;
@@ -286,8 +432,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
     // iteration issues the same loads, so each wait leaves exactly
     // (kRing-1) tiles outstanding.  Past the last tile the ring re-loads the
     // last tile (an L2 hit) instead of branching around the loads.
-    for (int c0 = 0; c0 < ntiles; c0 += 64) {
-        const int cn = min(64, ntiles - c0);
+    const int nt = t_hi - t_lo;
+    for (int c0 = 0; c0 < nt; c0 += 64) {
+        const int cn = min(64, nt - c0);
         const int32_t phys_lane = lane < cn ? bt[c0 + lane] : 0;   // one table entry per lane
         auto block_of = [&](int k) -> int32_t {
             return __builtin_amdgcn_readlane(phys_lane, min(k, cn - 1));
@@ -312,7 +459,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
 #pragma unroll
             for (int u = 0; u < kRing; ++u) {
                 const int k = it * kRing + u;
-                consume(ring[u], c0 + k, block_of(k));
+                consume(ring[u], t_lo + c0 + k, block_of(k));
                 issue(ring[u], block_of(k + kRing));
             }
         }
@@ -320,7 +467,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
         for (int u = 0; u < kRing; ++u) {
             const int k = (nit - 1) * kRing + u;
             if (k < cn)
-                consume(ring[u], c0 + k, block_of(k));
+                consume(ring[u], t_lo + c0 + k, block_of(k));
         }
     }
 
@@ -333,6 +480,43 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
             *reinterpret_cast<uint4 *>(kt + (lane * BS + woff) * 8) =
                 *reinterpret_cast<const uint4 *>(s_new + 8 * lane);
         vt[lane * BS + woff] = s_new[D + lane];   // V: dimension `lane`
+    }
+
+    if (SPLIT > 1) {
+        // Merge the wavefronts' (max, sum, output) per lane, in range order.
+        // A wavefront with no usable token holds (-inf, 0, 0) and weighs 0.
+        __shared__ float s_m[SPLIT][64], s_l[SPLIT][64];
+        __shared__ f32x4 s_o[SPLIT][4][64];
+        if (wv > 0) {
+            s_m[wv][lane] = m_run;
+            s_l[wv][lane] = l_run;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                s_o[wv][j][lane] = o[j];
+        }
+        __syncthreads();
+        if (wv > 0)
+            return;
+        float mm = m_run;
+#pragma unroll
+        for (int w = 1; w < SPLIT; ++w)
+            mm = fmaxf(mm, s_m[w][lane]);
+        if (mm != -INFINITY) {
+            const float a0 = __builtin_amdgcn_exp2f(m_run - mm);
+            l_run *= a0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] *= a0;
+#pragma unroll
+            for (int w = 1; w < SPLIT; ++w) {
+                const float aw = __builtin_amdgcn_exp2f(s_m[w][lane] - mm);
+                l_run = fmaf(s_l[w][lane], aw, l_run);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[j] += s_o[w][j][lane] * aw;
+            }
+            m_run = mm;
+        }
     }
 
     // Sum the lane groups' partial l (same query head, different tokens).
@@ -353,26 +537,102 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeArgs a)
     }
 }
 
+// What the launcher needs to know of the device: its compute units and how
+// many one-wavefront decode workgroups each holds at once (cached per device;
+// zeros if unknown).
+struct DeviceShape {
+    int cus;
+    int waves_per_cu;
+};
+
+DeviceShape device_shape()
+{
+    static std::atomic<int> cus_cache[64], waves_cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return {0, 0};
+    if (dev < 64) {
+        const int c = cus_cache[dev].load(std::memory_order_relaxed);
+        const int w = waves_cache[dev].load(std::memory_order_relaxed);
+        if (c > 0 && w > 0)
+            return {c, w};
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(paged_decode_kernel<false, false, false, 1>), 64,
+            0) != hipSuccess)
+        return {0, 0};
+    if (dev < 64) {
+        cus_cache[dev].store(cus, std::memory_order_relaxed);
+        waves_cache[dev].store(per_cu, std::memory_order_relaxed);
+    }
+    return {cus, per_cu};
+}
+
+template <bool APPEND, bool SHARED, bool PLAN, int SPLIT>
+void launch(const DecodeArgs &a, int64_t groups, hipStream_t stream)
+{
+    hipLaunchKernelGGL((paged_decode_kernel<APPEND, SHARED, PLAN, SPLIT>), dim3((unsigned)groups),
+                       dim3(64 * SPLIT), 0, stream, a);
+}
+
 }  // namespace
 
-hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream)
+// Launch policy, from the grid of one-wavefront workgroups per (sequence,
+// head, partition) that the host bounds give:
+//   * up to two rounds of what the device holds at once: 4 wavefronts per
+//     partition.  The launch then has many small workgroups, the hardware
+//     hands them out as slots free up, and each CU's 4 SIMDs share every
+//     partition's bytes, so no SIMD is left with more tiles than the others
+//     at the end (measured on batch 64 x 512-4096 tokens: 53.6 against
+//     56.6 us), and small batches get 4x the wavefronts;
+//   * beyond that (few very long sequences, or many sequences with room for
+//     long ones): one wavefront per partition, and for up to 256 sequences
+//     the balanced order of plan_unit, which moves the grid's empty
+//     partitions behind the work (batch 4 x 32k-128k tokens: 110.8 against
+//     121.9 us).
+// The shared-prefix launch takes the split its per-sequence grid would get,
+// so its partitions round exactly as the per-sequence pass's do.
+hipError_t launch_paged_decode(const DecodeArgs &args, hipStream_t stream)
 {
+    DecodeArgs a = args;
+    const DeviceShape dev = device_shape();
+    const int64_t groups = (int64_t)a.num_kv_heads * a.num_seqs * a.num_parts;
+    const int64_t resident = (int64_t)dev.cus * dev.waves_per_cu;
+    const bool split = resident > 0 && groups <= 2 * resident;
     if (a.shared_len) {
         // Shared partitions first (one workgroup per group, head and partition).
         const int64_t shared_groups = (int64_t)a.num_kv_heads * a.num_groups * a.num_parts;
-        hipLaunchKernelGGL((paged_decode_kernel<false, true>), dim3((unsigned)shared_groups),
-                           dim3(64), 0, stream, a);
+        if (split)
+            launch<false, true, false, 4>(a, shared_groups, stream);
+        else
+            launch<false, true, false, 1>(a, shared_groups, stream);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
-    const int64_t groups = (int64_t)a.num_kv_heads * a.num_seqs * a.num_parts;
-    if (a.k_new)
-        hipLaunchKernelGGL((paged_decode_kernel<true, false>), dim3((unsigned)groups), dim3(64), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((paged_decode_kernel<false, false>), dim3((unsigned)groups), dim3(64),
-                           0, stream, a);
+    // Balanced order: consecutive workgroups of one head cycle over
+    // cus / gcd(heads, cus) compute units (32 on one XCD for 8 heads).
+    a.plan_width = 0;
+    if (!split && !a.shared_len && a.num_seqs <= 64 * kPlanChunks && dev.cus > 0)
+        a.plan_width = dev.cus / std::gcd(a.num_kv_heads, dev.cus);
+    if (split) {
+        if (a.k_new)
+            launch<true, false, false, 4>(a, groups, stream);
+        else
+            launch<false, false, false, 4>(a, groups, stream);
+    } else if (a.plan_width > 0) {
+        if (a.k_new)
+            launch<true, false, true, 1>(a, groups, stream);
+        else
+            launch<false, false, true, 1>(a, groups, stream);
+    } else {
+        if (a.k_new)
+            launch<true, false, false, 1>(a, groups, stream);
+        else
+            launch<false, false, false, 1>(a, groups, stream);
+    }
     return hipGetLastError();
 }
 

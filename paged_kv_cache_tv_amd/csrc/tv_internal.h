@@ -69,6 +69,10 @@ struct DecodeArgs {
     const int32_t *shared_len;  // [num_groups]: leading tokens shared by group g's sequences
     int32_t group_size;         // sequences per group (consecutive), 1 .. 16 / group
     int32_t num_groups;         // ceil(num_seqs / group_size)
+    // Set by the launcher: > 0 selects the balanced workgroup order and gives
+    // how many compute units consecutive workgroups of one K/V head are dealt
+    // over; 0 keeps the plain (partition, sequence, head) order.
+    int32_t plan_width;
 };
 
 struct ReduceArgs {
