@@ -178,7 +178,8 @@ tv_status tv_rope(uint16_t *x, const int32_t *positions, const float *inv_freq,
  *   scale         score factor (1/sqrt(head_dim) for standard attention), > 0
  *
  * Supported shapes: head_dim == 64, block_size == 16, 1 <= num_q_heads /
- * num_kv_heads <= 16 (num_q_heads a multiple of num_kv_heads).
+ * num_kv_heads <= 16 (num_q_heads a multiple of num_kv_heads), and
+ * num_kv_heads * num_seqs * P < 2^24 (the launch grid).
  * Odd device data: a context length below 0 counts as 0 and one above
  * max_context_len is cut to max_context_len; a table entry outside
  * [0, num_blocks) drops that block's tokens from the softmax (a partition with

@@ -153,7 +153,8 @@ tv_status check_decode(tv::DecodeArgs &a, float *part_acc, float *part_max, floa
         !context_lens)
         return TV_ERR_NULL;
     const int64_t parts = ceil_div(max_context_len, partition_size);
-    if ((int64_t)num_kv_heads * num_seqs * parts > 0x7fffffff)
+    // Workgroups of up to 256 work-items: the grid must stay below 2^32 of them.
+    if ((int64_t)num_kv_heads * num_seqs * parts > 0xffffff)
         return TV_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(part_acc, 4) ||

@@ -93,6 +93,9 @@ def test_decode_validation(lib):
     assert _dec(lib, d=128) == TV_ERR_UNSUPPORTED
     assert _dec(lib, bs=32, part=64, mctx=64) == TV_ERR_UNSUPPORTED
     assert _dec(lib, hq=8 * 17) == TV_ERR_UNSUPPORTED       # group of 17
+    # launch grid of 8 heads x S x 2 partitions: 2^24 - 1 workgroups is the limit
+    assert _dec(lib, S=(1 << 20)) == TV_ERR_UNSUPPORTED    # 2^24
+    assert _dec(lib, S=(1 << 20) - 1) == TV_ERR_ALIGNMENT   # 2^24 - 16 passes the grid check
     assert _dec(lib, S=0) == TV_OK
     assert _dec(lib, mctx=0) == TV_OK
     assert _dec(lib, ptrs=(BAD,) * 7 + (None,)) == TV_ERR_NULL

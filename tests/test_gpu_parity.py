@@ -273,6 +273,29 @@ def test_short_sequences(dev, oracle_lib):
     _assert_close(got, ref, "300 short sequences")
 
 
+@pytest.mark.parametrize("num_seqs", [64, 300])
+def test_launch_policy_paths(dev, oracle_lib, num_seqs):
+    """The same batch through each launch form of the partition pass: a tight
+    host bound on the lengths gives a small grid (4 wavefronts per partition);
+    a loose one (65536) gives a grid of mostly empty partitions, served in the
+    balanced order for up to 256 sequences and in the plain order beyond.
+    Every form meets the bars, its two-launch step equals its three-launch step
+    bit for bit, and the forms agree with each other to rounding."""
+    rng = np.random.default_rng(43 + num_seqs)
+    lens = rng.integers(0, 1500, size=num_seqs)
+    lens[:3] = [0, 1, 1500]
+    batch = W.make_batch(lens, 43 + num_seqs, table_width=65536 // 16)
+    ref, _, _ = O.decode_step(oracle_lib, batch)
+    outs = []
+    for mc in (int(lens.max()), 65536):
+        got, _ = _gpu_step(batch, dev, max_context_len=mc)
+        _assert_close(got, ref, f"{num_seqs} sequences, max_context_len {mc}")
+        fused, _ = _gpu_step(batch, dev, max_context_len=mc, fused=True)
+        assert np.array_equal(got, fused), "two-launch step differs from the three-launch step"
+        outs.append(got)
+    assert np.abs(outs[0] - outs[1]).max() <= 1e-5
+
+
 # ---------------------------------------------------------------------------
 # tv_paged_attention_decode_append: the cache write folded into the partition
 # pass.  Under its precondition it must equal the three-call step bit for bit.
