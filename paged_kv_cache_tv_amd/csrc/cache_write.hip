@@ -18,14 +18,17 @@ constexpr int kWavesPerGroup = 4;      // tokens (wavefronts) per workgroup, uns
 constexpr int kTokensPerGroup = 16;    // tokens (wavefronts) per workgroup, staged form
 constexpr int64_t kStagedFrom = 512;   // launches of at least this many tokens use the staged form
 
-// One wavefront per token.  K goes out per token as 16-byte chunk stores.
+// One wavefront per token.
 // STAGED (launches of many tokens, e.g. a prompt): 16 consecutive tokens per
-// workgroup; when they fill one whole block in order (slots 16b .. 16b + 15)
-// their V rows are staged in LDS and every thread writes one 16-byte run of
-// 8 tokens of one dim of the dimension-major V tile.  Otherwise (and in the
-// unstaged form, 4 tokens per workgroup with no LDS and no barrier, for the
-// few tokens of a decode step) each token's V goes out as 2-byte stores down
-// its column.
+// workgroup.  When they fill one whole block in order (slots 16b .. 16b + 15)
+// their K rows (turned, with ROPE) and V rows are staged in LDS, and the
+// block goes out as whole 16-byte runs in address order: the block's K for
+// all heads is one contiguous [head][chunk][16 tokens][8 dims] region, each
+// thread storing one (chunk, token) piece; V's thread writes 8 tokens of one
+// dim of the dimension-major V tile.  Otherwise (and in the unstaged form, 4
+// tokens per workgroup with no LDS and no barrier, for the few tokens of a
+// decode step) each token's K goes out as 16-byte chunk stores and its V as
+// 2-byte stores down its column.
 //
 // ROPE: K is turned by the rotary embedding of positions[tok] before the
 // store (see rope_math.h).  Lanes 0 .. head_dim/2 - 1 compute the token's
@@ -41,9 +44,14 @@ void cache_write_kernel(CacheWriteArgs a)
     constexpr int kTok = STAGED ? kTokensPerGroup : kWavesPerGroup;
     __shared__ int64_t s_slot[STAGED ? kTokensPerGroup : 1];
     __shared__ uint4 s_v[STAGED ? kTokensPerGroup * 64 : 1];   // V rows of a full block (<= 512 values each)
+    // K rows of a full block, one row per token padded to 65 chunks so that
+    // the 16 tokens of one chunk sit on distinct banks.
+    constexpr int kKStride = 65;
+    __shared__ uint4 s_k[STAGED ? kTokensPerGroup * kKStride : 1];
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t tok = (int64_t)blockIdx.x * kTok + w;
+    uint16_t *const sk_row = reinterpret_cast<uint16_t *>(s_k + (STAGED ? w * kKStride : 0));
     const bool live_tok = tok < a.num_tokens;
     const int row = a.num_kv_heads * a.head_dim;
     const int chunks = row >> 3;
@@ -103,7 +111,10 @@ void cache_write_kernel(CacheWriteArgs a)
         uint16_t *ktile = a.k_cache + tile * a.head_dim * a.block_size;
         if (!ROPE) {
             const uint4 kk = c == lane ? k0 : ksrc[c];
-            *reinterpret_cast<uint4 *>(ktile + ((int64_t)(d >> 3) * a.block_size + off) * 8) = kk;
+            if (STAGED && full)
+                reinterpret_cast<uint4 *>(sk_row)[c] = kk;
+            else
+                *reinterpret_cast<uint4 *>(ktile + ((int64_t)(d >> 3) * a.block_size + off) * 8) = kk;
         } else if (a.rope_style == 0) {
             // Pairs (d + 2i, d + 2i + 1), i < 4: one 16-byte chunk in and out.
             const uint4 kk = c == lane ? k0 : ksrc[c];
@@ -117,8 +128,11 @@ void cache_write_kernel(CacheWriteArgs a)
                 o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ra) |
                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << 16);
             }
-            *reinterpret_cast<uint4 *>(ktile + ((int64_t)(d >> 3) * a.block_size + off) * 8) =
-                make_uint4(o[0], o[1], o[2], o[3]);
+            if (STAGED && full)
+                reinterpret_cast<uint4 *>(sk_row)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+            else
+                *reinterpret_cast<uint4 *>(ktile + ((int64_t)(d >> 3) * a.block_size + off) * 8) =
+                    make_uint4(o[0], o[1], o[2], o[3]);
         } else {
             // Pairs (4q + i, 4q + i + head_dim/2), i < 4, q = d / 8 within the head.
             const int half = a.head_dim >> 1;
@@ -139,10 +153,15 @@ void cache_write_kernel(CacheWriteArgs a)
                 ob[i >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << (16 * (i & 1));
             }
             const int db = da + half;
-            *reinterpret_cast<uint2 *>(ktile + ((int64_t)(da >> 3) * a.block_size + off) * 8 +
-                                       (da & 7)) = make_uint2(oa[0], oa[1]);
-            *reinterpret_cast<uint2 *>(ktile + ((int64_t)(db >> 3) * a.block_size + off) * 8 +
-                                       (db & 7)) = make_uint2(ob[0], ob[1]);
+            if (STAGED && full) {
+                *reinterpret_cast<uint2 *>(sk_row + h * a.head_dim + da) = make_uint2(oa[0], oa[1]);
+                *reinterpret_cast<uint2 *>(sk_row + h * a.head_dim + db) = make_uint2(ob[0], ob[1]);
+            } else {
+                *reinterpret_cast<uint2 *>(ktile + ((int64_t)(da >> 3) * a.block_size + off) * 8 +
+                                           (da & 7)) = make_uint2(oa[0], oa[1]);
+                *reinterpret_cast<uint2 *>(ktile + ((int64_t)(db >> 3) * a.block_size + off) * 8 +
+                                           (db & 7)) = make_uint2(ob[0], ob[1]);
+            }
         }
         if (full)
             continue;
@@ -162,6 +181,10 @@ void cache_write_kernel(CacheWriteArgs a)
     __syncthreads();
     const uint16_t *sv = reinterpret_cast<const uint16_t *>(s_v);
     const int64_t vblk = s0 / kTokensPerGroup;
+    // K: piece u = chunk * 16 + token of the block's contiguous K region.
+    for (int u = threadIdx.x; u < chunks * kTokensPerGroup; u += 64 * kTokensPerGroup)
+        reinterpret_cast<uint4 *>(a.k_cache + vblk * (int64_t)row * kTokensPerGroup)[u] =
+            s_k[(u & (kTokensPerGroup - 1)) * kKStride + (u >> 4)];
     for (int t = threadIdx.x; t < 2 * row; t += 64 * kTokensPerGroup) {
         const int e = t >> 1;                                  // h * head_dim + d
         const int t0 = 8 * (t & 1);
