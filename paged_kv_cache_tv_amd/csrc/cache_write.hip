@@ -14,8 +14,8 @@
 namespace tv {
 namespace {
 
-constexpr int kWavesPerGroup = 4;      // tokens (wavefronts) per workgroup, unstaged forms
-constexpr int kTokensPerGroup = 16;    // tokens (wavefronts) per workgroup, staged form
+constexpr int kWavesPerGroup = 4;      // wavefronts per workgroup (one token each, unstaged forms)
+constexpr int kTokensPerGroup = 16;    // tokens per workgroup, staged form (4 per wavefront)
 constexpr int64_t kStagedFrom = 512;   // launches of at least this many tokens use the staged form
 
 // One wavefront per token.
@@ -38,10 +38,11 @@ constexpr int64_t kStagedFrom = 512;   // launches of at least this many tokens 
 // q is the 16-byte chunk q of the head; style 1 pairs (k, k + head_dim/2), so
 // group q is dims 4q .. 4q+3 and their partners, two 8-byte pieces.
 template <bool ROPE, bool STAGED>
-__global__ __launch_bounds__(64 * (STAGED ? kTokensPerGroup : kWavesPerGroup))
+__global__ __launch_bounds__(64 * kWavesPerGroup)
 void cache_write_kernel(CacheWriteArgs a)
 {
-    constexpr int kTok = STAGED ? kTokensPerGroup : kWavesPerGroup;
+    constexpr int kPerWave = STAGED ? kTokensPerGroup / kWavesPerGroup : 1;   // tokens per wavefront
+    constexpr int kTok = kWavesPerGroup * kPerWave;                          // tokens per workgroup
     __shared__ int64_t s_slot[STAGED ? kTokensPerGroup : 1];
     __shared__ uint4 s_v[STAGED ? kTokensPerGroup * 64 : 1];   // V rows of a full block (<= 512 values each)
     // K rows of a full block, one row per token padded to 65 chunks so that
@@ -50,24 +51,37 @@ void cache_write_kernel(CacheWriteArgs a)
     __shared__ uint4 s_k[STAGED ? kTokensPerGroup * kKStride : 1];
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int64_t tok = (int64_t)blockIdx.x * kTok + w;
-    uint16_t *const sk_row = reinterpret_cast<uint16_t *>(s_k + (STAGED ? w * kKStride : 0));
-    const bool live_tok = tok < a.num_tokens;
     const int row = a.num_kv_heads * a.head_dim;
     const int chunks = row >> 3;
-    const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.k + tok * row);
-    const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.v + tok * row);
-    // The first chunk of each lane is loaded together with the slot number, so
-    // the common case (num_kv_heads * head_dim <= 512) waits on memory once.
-    const bool have0 = live_tok && lane < chunks;
-    const uint4 k0 = have0 ? ksrc[lane] : make_uint4(0, 0, 0, 0);
-    const uint4 v0 = have0 ? vsrc[lane] : make_uint4(0, 0, 0, 0);
-    const int64_t slot = live_tok ? a.slot_mapping[tok] : -1;
+    // Wavefront w takes tokens kPerWave*w .. kPerWave*w + kPerWave - 1 of the
+    // workgroup.  Every load the common case (num_kv_heads * head_dim <= 512)
+    // needs -- each token's slot, its first K and V chunk per lane and, with
+    // ROPE, its position -- is issued before any is used, so the wavefront
+    // waits on memory once.
+    int64_t toks[kPerWave], slots[kPerWave];
+    uint4 k0s[kPerWave], v0s[kPerWave];
+    int poss[kPerWave];
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+        toks[i] = (int64_t)blockIdx.x * kTok + w * kPerWave + i;
+        const bool live = toks[i] < a.num_tokens;
+        const bool have0 = live && lane < chunks;
+        k0s[i] = have0 ? reinterpret_cast<const uint4 *>(a.k + toks[i] * row)[lane]
+                       : make_uint4(0, 0, 0, 0);
+        v0s[i] = have0 ? reinterpret_cast<const uint4 *>(a.v + toks[i] * row)[lane]
+                       : make_uint4(0, 0, 0, 0);
+        slots[i] = live ? a.slot_mapping[toks[i]] : -1;
+        poss[i] = ROPE && live ? a.positions[toks[i]] : 0;
+    }
+    const float f_lane = ROPE ? a.inv_freq[lane % (a.head_dim >> 1)] : 0.f;
     bool full = false;
     int64_t s0 = 0;
     if (STAGED) {
-        if (lane == 0)
-            s_slot[w] = slot;
+        if (lane == 0) {
+#pragma unroll
+            for (int i = 0; i < kPerWave; ++i)
+                s_slot[w * kPerWave + i] = slots[i];
+        }
         // A full block: 16 tokens, slots 16b .. 16b + 15 in order, V rows that
         // fit in LDS, and a V pool aligned for 16-byte stores.
         full = row <= 512 && a.block_size == kTokensPerGroup &&
@@ -78,100 +92,113 @@ void cache_write_kernel(CacheWriteArgs a)
 #pragma unroll
         for (int i = 1; i < kTokensPerGroup; ++i)
             full = full && s_slot[i] == s0 + i;
-        if (full && lane < chunks)
-            s_v[w * 64 + lane] = v0;
-    } else if (!live_tok) {
+        if (full && lane < chunks) {
+#pragma unroll
+            for (int i = 0; i < kPerWave; ++i)
+                s_v[(w * kPerWave + i) * 64 + lane] = v0s[i];
+        }
+    } else if (toks[0] >= a.num_tokens) {
         return;
     }
 
-    const bool write = slot >= 0 && slot < a.num_slots;
-    const int64_t blk = write ? slot / a.block_size : 0;
-    const int off = write ? (int)(slot - blk * a.block_size) : 0;
-    float pc = 1.f, ps = 0.f;
-    if (ROPE && live_tok) {
-        const int half = a.head_dim >> 1;
-        rope_cos_sin(a.positions[tok], a.inv_freq[lane % half], pc, ps);
-    }
-    for (int base = 0; base < chunks; base += 64) {
-        const int c = base + lane;
-        float cs[4], sn[4];
-        if (ROPE) {
-            const int q = c % (a.head_dim >> 3);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                cs[i] = __shfl(pc, 4 * q + i);
-                sn[i] = __shfl(ps, 4 * q + i);
+    for (int ti = 0; ti < kPerWave; ++ti) {
+        const int64_t tok = toks[ti];
+        const bool live_tok = tok < a.num_tokens;
+        const int64_t slot = slots[ti];
+        const uint4 k0 = k0s[ti];
+        const uint4 v0 = v0s[ti];
+        const uint4 *ksrc = reinterpret_cast<const uint4 *>(a.k + tok * row);
+        const uint4 *vsrc = reinterpret_cast<const uint4 *>(a.v + tok * row);
+        uint16_t *const sk_row =
+            reinterpret_cast<uint16_t *>(s_k + (STAGED ? (w * kPerWave + ti) * kKStride : 0));
+        const bool write = slot >= 0 && slot < a.num_slots;
+        const int64_t blk = write ? slot / a.block_size : 0;
+        const int off = write ? (int)(slot - blk * a.block_size) : 0;
+        float pc = 1.f, ps = 0.f;
+        if (ROPE && live_tok)
+            rope_cos_sin(poss[ti], f_lane, pc, ps);
+        for (int base = 0; base < chunks; base += 64) {
+            const int c = base + lane;
+            float cs[4], sn[4];
+            if (ROPE) {
+                const int q = c % (a.head_dim >> 3);
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    cs[i] = __shfl(pc, 4 * q + i);
+                    sn[i] = __shfl(ps, 4 * q + i);
+                }
             }
-        }
-        if (!write || c >= chunks)
-            continue;
-        const int h = (c << 3) / a.head_dim;
-        const int d = (c << 3) - h * a.head_dim;
-        const int64_t tile = blk * a.num_kv_heads + h;
-        uint16_t *ktile = a.k_cache + tile * a.head_dim * a.block_size;
-        if (!ROPE) {
-            const uint4 kk = c == lane ? k0 : ksrc[c];
-            if (STAGED && full)
-                reinterpret_cast<uint4 *>(sk_row)[c] = kk;
-            else
-                *reinterpret_cast<uint4 *>(ktile + ((int64_t)(d >> 3) * a.block_size + off) * 8) = kk;
-        } else if (a.rope_style == 0) {
-            // Pairs (d + 2i, d + 2i + 1), i < 4: one 16-byte chunk in and out.
-            const uint4 kk = c == lane ? k0 : ksrc[c];
-            const uint32_t wd[4] = {kk.x, kk.y, kk.z, kk.w};
-            uint32_t o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float ra, rb;
-                rope_turn(__uint_as_float(wd[i] << 16), __uint_as_float(wd[i] & 0xFFFF0000u),
-                          cs[i], sn[i], ra, rb);
-                o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ra) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << 16);
-            }
-            if (STAGED && full)
-                reinterpret_cast<uint4 *>(sk_row)[c] = make_uint4(o[0], o[1], o[2], o[3]);
-            else
-                *reinterpret_cast<uint4 *>(ktile + ((int64_t)(d >> 3) * a.block_size + off) * 8) =
-                    make_uint4(o[0], o[1], o[2], o[3]);
-        } else {
-            // Pairs (4q + i, 4q + i + head_dim/2), i < 4, q = d / 8 within the head.
-            const int half = a.head_dim >> 1;
-            const int da = d >> 1;                           // 4q
-            const uint16_t *src = a.k + tok * row + h * a.head_dim;
-            const uint2 pa = *reinterpret_cast<const uint2 *>(src + da);
-            const uint2 pb = *reinterpret_cast<const uint2 *>(src + da + half);
-            const uint32_t wa[2] = {pa.x, pa.y}, wb[2] = {pb.x, pb.y};
-            uint32_t oa[2] = {0u, 0u}, ob[2] = {0u, 0u};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t xa = (wa[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-                const uint32_t xb = (wb[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-                float ra, rb;
-                rope_turn(__uint_as_float(xa << 16), __uint_as_float(xb << 16), cs[i], sn[i], ra,
-                          rb);
-                oa[i >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ra) << (16 * (i & 1));
-                ob[i >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << (16 * (i & 1));
-            }
-            const int db = da + half;
-            if (STAGED && full) {
-                *reinterpret_cast<uint2 *>(sk_row + h * a.head_dim + da) = make_uint2(oa[0], oa[1]);
-                *reinterpret_cast<uint2 *>(sk_row + h * a.head_dim + db) = make_uint2(ob[0], ob[1]);
+            if (!write || c >= chunks)
+                continue;
+            const int h = (c << 3) / a.head_dim;
+            const int d = (c << 3) - h * a.head_dim;
+            const int64_t tile = blk * a.num_kv_heads + h;
+            uint16_t *ktile = a.k_cache + tile * a.head_dim * a.block_size;
+            if (!ROPE) {
+                const uint4 kk = c == lane ? k0 : ksrc[c];
+                if (STAGED && full)
+                    reinterpret_cast<uint4 *>(sk_row)[c] = kk;
+                else
+                    *reinterpret_cast<uint4 *>(ktile + ((int64_t)(d >> 3) * a.block_size + off) * 8) = kk;
+            } else if (a.rope_style == 0) {
+                // Pairs (d + 2i, d + 2i + 1), i < 4: one 16-byte chunk in and out.
+                const uint4 kk = c == lane ? k0 : ksrc[c];
+                const uint32_t wd[4] = {kk.x, kk.y, kk.z, kk.w};
+                uint32_t o[4];
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float ra, rb;
+                    rope_turn(__uint_as_float(wd[i] << 16), __uint_as_float(wd[i] & 0xFFFF0000u),
+                              cs[i], sn[i], ra, rb);
+                    o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ra) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << 16);
+                }
+                if (STAGED && full)
+                    reinterpret_cast<uint4 *>(sk_row)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+                else
+                    *reinterpret_cast<uint4 *>(ktile + ((int64_t)(d >> 3) * a.block_size + off) * 8) =
+                        make_uint4(o[0], o[1], o[2], o[3]);
             } else {
-                *reinterpret_cast<uint2 *>(ktile + ((int64_t)(da >> 3) * a.block_size + off) * 8 +
-                                           (da & 7)) = make_uint2(oa[0], oa[1]);
-                *reinterpret_cast<uint2 *>(ktile + ((int64_t)(db >> 3) * a.block_size + off) * 8 +
-                                           (db & 7)) = make_uint2(ob[0], ob[1]);
+                // Pairs (4q + i, 4q + i + head_dim/2), i < 4, q = d / 8 within the head.
+                const int half = a.head_dim >> 1;
+                const int da = d >> 1;                           // 4q
+                const uint16_t *src = a.k + tok * row + h * a.head_dim;
+                const uint2 pa = *reinterpret_cast<const uint2 *>(src + da);
+                const uint2 pb = *reinterpret_cast<const uint2 *>(src + da + half);
+                const uint32_t wa[2] = {pa.x, pa.y}, wb[2] = {pb.x, pb.y};
+                uint32_t oa[2] = {0u, 0u}, ob[2] = {0u, 0u};
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t xa = (wa[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                    const uint32_t xb = (wb[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                    float ra, rb;
+                    rope_turn(__uint_as_float(xa << 16), __uint_as_float(xb << 16), cs[i], sn[i], ra,
+                              rb);
+                    oa[i >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ra) << (16 * (i & 1));
+                    ob[i >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << (16 * (i & 1));
+                }
+                const int db = da + half;
+                if (STAGED && full) {
+                    *reinterpret_cast<uint2 *>(sk_row + h * a.head_dim + da) = make_uint2(oa[0], oa[1]);
+                    *reinterpret_cast<uint2 *>(sk_row + h * a.head_dim + db) = make_uint2(ob[0], ob[1]);
+                } else {
+                    *reinterpret_cast<uint2 *>(ktile + ((int64_t)(da >> 3) * a.block_size + off) * 8 +
+                                               (da & 7)) = make_uint2(oa[0], oa[1]);
+                    *reinterpret_cast<uint2 *>(ktile + ((int64_t)(db >> 3) * a.block_size + off) * 8 +
+                                               (db & 7)) = make_uint2(ob[0], ob[1]);
+                }
             }
-        }
-        if (full)
-            continue;
-        const uint4 vv = c == lane ? v0 : vsrc[c];
-        uint16_t *vdst = a.v_cache + (tile * a.head_dim + d) * a.block_size + off;
-        const uint32_t wd[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t word = wd[i >> 1];
-            vdst[(int64_t)i * a.block_size] = (uint16_t)((i & 1) ? (word >> 16) : (word & 0xFFFFu));
+            if (full)
+                continue;
+            const uint4 vv = c == lane ? v0 : vsrc[c];
+            uint16_t *vdst = a.v_cache + (tile * a.head_dim + d) * a.block_size + off;
+            const uint32_t wd[4] = {vv.x, vv.y, vv.z, vv.w};
+    #pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t word = wd[i >> 1];
+                vdst[(int64_t)i * a.block_size] = (uint16_t)((i & 1) ? (word >> 16) : (word & 0xFFFFu));
+            }
         }
     }
     if (!STAGED || !full)
@@ -182,10 +209,10 @@ void cache_write_kernel(CacheWriteArgs a)
     const uint16_t *sv = reinterpret_cast<const uint16_t *>(s_v);
     const int64_t vblk = s0 / kTokensPerGroup;
     // K: piece u = chunk * 16 + token of the block's contiguous K region.
-    for (int u = threadIdx.x; u < chunks * kTokensPerGroup; u += 64 * kTokensPerGroup)
+    for (int u = threadIdx.x; u < chunks * kTokensPerGroup; u += 64 * kWavesPerGroup)
         reinterpret_cast<uint4 *>(a.k_cache + vblk * (int64_t)row * kTokensPerGroup)[u] =
             s_k[(u & (kTokensPerGroup - 1)) * kKStride + (u >> 4)];
-    for (int t = threadIdx.x; t < 2 * row; t += 64 * kTokensPerGroup) {
+    for (int t = threadIdx.x; t < 2 * row; t += 64 * kWavesPerGroup) {
         const int e = t >> 1;                                  // h * head_dim + d
         const int t0 = 8 * (t & 1);
         uint32_t o[4];
@@ -271,7 +298,7 @@ void launch_cw(const CacheWriteArgs &a, hipStream_t stream)
     if (a.num_tokens >= kStagedFrom) {
         const int64_t groups = (a.num_tokens + kTokensPerGroup - 1) / kTokensPerGroup;
         hipLaunchKernelGGL((cache_write_kernel<ROPE, true>), dim3((unsigned)groups),
-                           dim3(64 * kTokensPerGroup), 0, stream, a);
+                           dim3(64 * kWavesPerGroup), 0, stream, a);
     } else {
         const int64_t groups = (a.num_tokens + kWavesPerGroup - 1) / kWavesPerGroup;
         hipLaunchKernelGGL((cache_write_kernel<ROPE, false>), dim3((unsigned)groups),

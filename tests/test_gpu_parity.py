@@ -273,12 +273,13 @@ def test_short_sequences(dev, oracle_lib):
     _assert_close(got, ref, "300 short sequences")
 
 
-@pytest.mark.parametrize("num_seqs", [64, 300])
+@pytest.mark.parametrize("num_seqs", [64, 256, 300])
 def test_launch_policy_paths(dev, oracle_lib, num_seqs):
     """The same batch through each launch form of the partition pass: a tight
     host bound on the lengths gives a small grid (4 wavefronts per partition);
     a loose one (65536) gives a grid of mostly empty partitions, served in the
-    balanced order for up to 256 sequences and in the plain order beyond.
+    balanced order for up to 256 sequences (256: all four 64-sequence chunks
+    of the in-kernel order) and in the plain order beyond.
     Every form meets the bars, its two-launch step equals its three-launch step
     bit for bit, and the forms agree with each other to rounding."""
     rng = np.random.default_rng(43 + num_seqs)
