@@ -265,9 +265,11 @@ def rope_rate(tv, dev, stream, flush, steps, index=3):
 def shared_prefix_rate(tv, dev, stream, flush, steps):
     """The partition pass on the shared-prefix workload (64 prompts x 4
     samples, 1024 shared tokens): per sequence (tv_paged_attention_decode)
-    against groups of 4 (tv_paged_attention_decode_shared), cold, events
-    around each launch.  Bytes: the K/V each path must read at least --
-    logical (every sequence's context) and unique (shared blocks once)."""
+    against groups of 4 (tv_paged_attention_decode_shared), and the whole
+    two-launch step each way (tv_paged_attention_decode_append or
+    tv_paged_attention_decode_shared_append, then the merge); cold, events
+    around each.  Bytes: the K/V each path must read at least -- logical
+    (every sequence's context) and unique (shared blocks once)."""
     import torch
     from paged_kv_cache_tv_amd import workloads as W
     from paged_kv_cache_tv_amd.step import DeviceBatch
@@ -287,9 +289,23 @@ def shared_prefix_rate(tv, dev, stream, flush, steps):
                                          db.block_tables, db.context_lens, shared, 4,
                                          db.max_context_len, db.partition_size, b.scale, stream)
 
+    def grouped_step():
+        # The parallel-sampling decode step in two launches: the new tokens'
+        # cache write folded into the shared pass, then the merge.
+        tv.paged_attention_decode_shared_append(pa, pm, ps, db.q, db.step_k, db.step_v,
+                                                db.step_slots, db.k_cache, db.v_cache,
+                                                db.block_tables, db.context_lens, shared, 4,
+                                                db.max_context_len, db.partition_size, b.scale,
+                                                stream)
+        db.reduce(stream)
+
+    def plain_step():
+        db.fused_step(stream)
+
     res = {"workload": b.name, "group_size": 4, "shared_tokens": 1024,
            "kv_bytes_logical": b.kv_bytes_logical(), "kv_bytes_unique": b.kv_bytes_unique()}
-    for name, fn in (("per_sequence", plain), ("shared", grouped)):
+    for name, fn in (("per_sequence", plain), ("shared", grouped),
+                     ("per_sequence_step", plain_step), ("shared_step", grouped_step)):
         fn()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]

@@ -271,6 +271,39 @@ tv_status tv_paged_attention_decode_append(float *part_acc, float *part_max, flo
                                            int32_t partition_size, float scale, void *stream);
 
 /*
+ * Shared-prefix partition pass with the cache write folded in: the same
+ * results as tv_cache_write of one new token per sequence (as in
+ * tv_paged_attention_decode_append) followed by
+ * tv_paged_attention_decode_shared, in two launches on `stream` (the group
+ * pass, then the per-sequence pass that also writes the tokens).  The
+ * parallel-sampling decode step ("vLLM" page, section "가상 메모리 방식의
+ * 해결": samples share their prompt's blocks; each sample's new token goes
+ * to a block of its own).
+ *
+ * Preconditions: those of both calls -- slot_mapping[s] is negative or the
+ * slot the block table gives for position n - 1 of sequence s, and for the
+ * shared positions every member's table holds the first member's blocks --
+ * and position n - 1 of every member lies past its group's shared
+ * partitions (n - 1 >= floor(sh / partition_size) * partition_size, sh as
+ * for tv_paged_attention_decode_shared), which holds whenever the new token's
+ * block is the member's own.  Then the partials equal the two-call sequence
+ * bit for bit.  If a member's position n - 1 lies in a shared partition, its
+ * token is still written, but the group pass has attended that slot's
+ * previous contents.
+ *
+ *   arguments as for tv_paged_attention_decode_append, plus shared_len and
+ *   group_size as for tv_paged_attention_decode_shared.
+ * Supported shapes and errors: the union of both calls'.
+ */
+tv_status tv_paged_attention_decode_shared_append(
+    float *part_acc, float *part_max, float *part_sum, const uint16_t *q, const uint16_t *k_new,
+    const uint16_t *v_new, const int64_t *slot_mapping, uint16_t *k_cache, uint16_t *v_cache,
+    const int32_t *block_tables, const int32_t *context_lens, const int32_t *shared_len,
+    int32_t group_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+    int32_t max_context_len, int32_t partition_size, float scale, void *stream);
+
+/*
  * Log-sum-exp merge of the partitions ("vLLM" page, Flash Attention: the
  * running maximum / running sum rule applied across partitions).
  *

@@ -11,6 +11,7 @@ from .binding import (LIB_PATH, BlockManager, TvError, cache_write, cache_write_
                       load_library, new_pools,
                       new_workspace, num_partitions, paged_attention, paged_attention_decode,
                       paged_attention_decode_append, paged_attention_decode_shared,
+                      paged_attention_decode_shared_append,
                       paged_attention_prefill,
                       paged_attention_reduce)
 
@@ -19,4 +20,5 @@ __all__ = ["LIB_PATH", "BlockManager", "TvError", "cache_write", "cache_write_ro
            "load_library", "new_pools",
            "new_workspace", "num_partitions", "paged_attention", "paged_attention_decode",
            "paged_attention_decode_append", "paged_attention_decode_shared",
+           "paged_attention_decode_shared_append",
            "paged_attention_prefill", "paged_attention_reduce"]

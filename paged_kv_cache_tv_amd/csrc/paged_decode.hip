@@ -315,6 +315,7 @@ void paged_decode_kernel(DecodeArgs a)
     }
     int members = 1;
     int n = 0;
+    bool write_only = false;
     if (a.shared_len) {
         const int grp = SHARED ? s : s / a.group_size;
         const int first = grp * a.group_size;
@@ -333,7 +334,9 @@ void paged_decode_kernel(DecodeArgs a)
             members = cnt;
             n = shared_parts * a.part_tiles * BS;
         } else if (part < shared_parts) {
-            return;                            // computed by the shared pass
+            if (!APPEND)
+                return;                        // computed by the shared pass
+            write_only = true;                 // the shared pass attends; only the cache write here
         }
     }
     if (!SHARED) {
@@ -392,6 +395,30 @@ void paged_decode_kernel(DecodeArgs a)
                                                        2 * (lane & 31));
     }
     int sub_off = -1;                     // token of the last tile replaced (-1: none)
+
+    // The cache write of the new token, this head, from the row staged in LDS.
+    auto store_new_row = [&]() {
+        const int64_t wblk = wslot / BS;
+        const int woff = (int)(wslot - wblk * BS);
+        uint16_t *kt = a.k_cache_w + (wblk * a.num_kv_heads + kvh) * (int64_t)(BS * D);
+        uint16_t *vt = a.v_cache_w + (wblk * a.num_kv_heads + kvh) * (int64_t)(BS * D);
+        if (lane < D / 8)                 // K: chunk `lane` (16 bytes)
+            *reinterpret_cast<uint4 *>(kt + (lane * BS + woff) * 8) =
+                *reinterpret_cast<const uint4 *>(s_new + 8 * lane);
+        vt[lane * BS + woff] = s_new[D + lane];   // V: dimension `lane`
+    };
+    if (APPEND && write_only) {
+        // The sequence's last partition lies in its group's shared prefix (a
+        // broken precondition of the shared call): the shared pass has
+        // attended it already; the new token is still written.
+        if (append_here && wslot >= 0 && wslot < a.num_blocks * BS) {
+            reinterpret_cast<uint32_t *>(s_new)[lane] = new_pair;
+            __builtin_amdgcn_s_waitcnt(0xC07F);           // LDS stores done (lgkmcnt 0)
+            __builtin_amdgcn_wave_barrier();
+            store_new_row();
+        }
+        return;
+    }
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 o[4];
@@ -481,16 +508,8 @@ void paged_decode_kernel(DecodeArgs a)
         }
     }
 
-    if (APPEND && wslot >= 0) {           // the cache write of the new token, this head
-        const int64_t wblk = wslot / BS;
-        const int woff = (int)(wslot - wblk * BS);
-        uint16_t *kt = a.k_cache_w + (wblk * a.num_kv_heads + kvh) * (int64_t)(BS * D);
-        uint16_t *vt = a.v_cache_w + (wblk * a.num_kv_heads + kvh) * (int64_t)(BS * D);
-        if (lane < D / 8)                 // K: chunk `lane` (16 bytes)
-            *reinterpret_cast<uint4 *>(kt + (lane * BS + woff) * 8) =
-                *reinterpret_cast<const uint4 *>(s_new + 8 * lane);
-        vt[lane * BS + woff] = s_new[D + lane];   // V: dimension `lane`
-    }
+    if (APPEND && wslot >= 0)
+        store_new_row();
 
     if (SPLIT > 1) {
         // Merge the wavefronts' (max, sum, output) per lane, in range order.

@@ -322,6 +322,44 @@ tv_status tv_paged_attention_decode_shared(float *part_acc, float *part_max, flo
     return from_hip(tv::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+tv_status tv_paged_attention_decode_shared_append(
+    float *part_acc, float *part_max, float *part_sum, const uint16_t *q, const uint16_t *k_new,
+    const uint16_t *v_new, const int64_t *slot_mapping, uint16_t *k_cache, uint16_t *v_cache,
+    const int32_t *block_tables, const int32_t *context_lens, const int32_t *shared_len,
+    int32_t group_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+    int32_t max_context_len, int32_t partition_size, float scale, void *stream)
+{
+    if (group_size < 1)
+        return TV_ERR_SHAPE;
+    if (num_kv_heads > 0 && num_q_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+        (int64_t)group_size * (num_q_heads / num_kv_heads) > tv::kMaxGroup)
+        return TV_ERR_UNSUPPORTED;
+    tv::DecodeArgs a;
+    const tv_status st = check_decode(a, part_acc, part_max, part_sum, q, k_cache, v_cache,
+                                      block_tables, context_lens, num_seqs, num_q_heads,
+                                      num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                      num_blocks, max_context_len, partition_size, scale);
+    if (st != TV_OK || a.num_parts == 0)
+        return st;
+    if (!shared_len || !k_new || !v_new || !slot_mapping)
+        return TV_ERR_NULL;
+    if (!aligned(shared_len, 4) || !aligned(k_new, 16) || !aligned(v_new, 2) ||
+        !aligned(slot_mapping, 8))
+        return TV_ERR_ALIGNMENT;
+    if (num_blocks > INT64_MAX / block_size)
+        return TV_ERR_SHAPE;
+    a.shared_len = shared_len;
+    a.group_size = group_size;
+    a.num_groups = (int32_t)ceil_div(num_seqs, group_size);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.slot_mapping = slot_mapping;
+    a.k_cache_w = k_cache;
+    a.v_cache_w = v_cache;
+    return from_hip(tv::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
+}
+
 tv_status tv_paged_attention_reduce(float *out, const float *part_acc, const float *part_max,
                                     const float *part_sum, const int32_t *context_lens,
                                     int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,

@@ -36,7 +36,7 @@ def _declared():
 def test_header_declares_the_three_calls():
     names = _declared()
     for n in ("tv_cache_write", "tv_paged_attention_decode", "tv_paged_attention_reduce",
-              "tv_paged_attention_decode_append"):
+              "tv_paged_attention_decode_append", "tv_paged_attention_decode_shared_append"):
         assert n in names
 
 
@@ -153,6 +153,29 @@ def test_decode_shared_validation(lib):
     assert _shd(lib, ptrs=tuple(ptrs)) == TV_ERR_NULL
     ptrs[8] = 0x1002
     assert _shd(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
+
+
+def _sha(lib, S=2, hq=32, hkv=8, gs=4, mctx=64, part=32, ptrs=(BAD,) * 12):
+    return lib.tv_paged_attention_decode_shared_append(*ptrs, gs, S, hq, hkv, 64, 16, 4, 8, mctx,
+                                                       part, 0.125, None)
+
+
+def test_decode_shared_append_validation(lib):
+    assert _sha(lib, S=-1) == TV_ERR_SHAPE
+    assert _sha(lib, gs=0) == TV_ERR_SHAPE
+    assert _sha(lib, gs=5) == TV_ERR_UNSUPPORTED
+    assert _sha(lib, part=24) == TV_ERR_SHAPE
+    assert _sha(lib, S=0) == TV_OK
+    assert _sha(lib, mctx=0) == TV_OK
+    assert _sha(lib) == TV_ERR_ALIGNMENT                  # the decode arguments are checked first
+    # The partition-pass arguments pass their checks; each of the shared and
+    # append ones is then refused when NULL or misaligned (nothing launches).
+    for i in (4, 5, 6, 11):                               # k_new, v_new, slot_mapping, shared_len
+        ptrs = [ALIGNED] * 12
+        ptrs[i] = None
+        assert _sha(lib, ptrs=tuple(ptrs)) == TV_ERR_NULL
+        ptrs[i] = BAD
+        assert _sha(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
 
 
 def _pre(lib, S=2, hq=32, hkv=8, d=64, bs=16, mb=4, nb=8, mq=40, mctx=64, scale=0.125,

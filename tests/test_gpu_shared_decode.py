@@ -108,3 +108,85 @@ def test_shared_prefix_ragged_groups(dev, samples, prefix, part):
     out_p, part_p = _run(b, dev, part, lens=lens)
     _same_partials(part_s, part_p, lens, part)
     assert np.array_equal(out_s.view(np.uint32), out_p.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# tv_paged_attention_decode_shared_append: the new tokens' cache write folded
+# into the shared-prefix pass.  Under its preconditions it must equal
+# tv_cache_write of the new tokens followed by tv_paged_attention_decode_shared
+# bit for bit: pools and partials.
+# ---------------------------------------------------------------------------
+
+def _run_append(b, dev, part, shared, group_size, lens=None):
+    """Cached tokens written with tv_cache_write, then the shared pass with the
+    new tokens appended: (out, partials, pools)."""
+    import torch
+    import paged_kv_cache_tv_amd as tv
+    lens = b.context_lens if lens is None else lens
+    kc, vc = tv.new_pools(b.num_blocks, b.num_kv_heads, b.head_dim, b.block_size, dev,
+                          fill=W.BF16_NAN)
+    k, v, sl = b.fill_inputs()
+    live = sl >= 0
+    tv.cache_write(_to_dev(k[live], dev), _to_dev(v[live], dev), kc, vc, _to_dev(sl[live], dev))
+    sk, sv, ss = b.step_inputs()
+    mc = int(lens.max())
+    ws = tv.new_workspace(b.num_seqs, b.num_q_heads, b.head_dim, mc, part, dev)
+    for t in ws:
+        t.fill_(float("nan"))
+    q, bt, cl = _to_dev(b.q, dev), _to_dev(b.block_tables, dev), _to_dev(lens, dev)
+    tv.paged_attention_decode_shared_append(*ws, q, _to_dev(sk, dev), _to_dev(sv, dev),
+                                            _to_dev(ss.astype(np.int64), dev), kc, vc, bt, cl,
+                                            _to_dev(shared, dev), group_size, mc, part, b.scale)
+    out = torch.empty((b.num_seqs, b.num_q_heads, b.head_dim), dtype=torch.float32, device=dev)
+    tv.paged_attention_reduce(out, *ws, cl, mc, part)
+    torch.cuda.synchronize()
+    return (out.cpu().numpy(), [t.cpu().numpy() for t in ws],
+            (kc.cpu().numpy().view(np.uint16), vc.cpu().numpy().view(np.uint16)))
+
+
+def test_shared_append_workload(dev, oracle_lib):
+    """The parallel-sampling step of the shared-prefix workload in two
+    launches: pools bit-exact against the oracle's cache write, partials and
+    output bitwise equal to the write followed by the shared pass."""
+    b = W.make_workload(4)
+    shared = np.full(64, 1024, np.int32)
+    out_a, part_a, (kc, vc) = _run_append(b, dev, 512, shared, 4)
+    out_s, part_s = _run(b, dev, 512, shared, 4)
+    _same_partials(part_a, part_s, b.context_lens, 512)
+    assert np.array_equal(out_a.view(np.uint32), out_s.view(np.uint32))
+    ref, kc_ref, vc_ref = O.decode_step(oracle_lib, b)
+    assert np.array_equal(kc, kc_ref), "K pool differs from the oracle's cache write"
+    assert np.array_equal(vc, vc_ref), "V pool differs from the oracle's cache write"
+    err = np.abs(out_a.astype(np.float64) - ref)
+    print(f"shared-prefix append step: max_abs={err.max():.3e}", flush=True)
+    assert err.max() <= 1e-4 and err.mean() <= 1e-6
+
+
+@pytest.mark.parametrize("samples,prefix,part", [(3, 704, 64), (4, 256, 64), (2, 1536, 512)])
+def test_shared_append_ragged_groups(dev, samples, prefix, part):
+    """Ragged groups as above.  The member cut below the prefix keeps the new
+    token of its full length: with (4, 256, 64) its last position falls in a
+    shared partition, the case where the token is only written."""
+    rng = np.random.default_rng(130 + samples + part)
+    prompts = 5
+    priv = rng.integers(0, 300, prompts * samples)
+    b = W.make_shared_prefix_batch(prompts, samples, prefix, priv, 131 + prefix)
+    lens = b.context_lens.copy()
+    lens[samples] = prefix // 2
+    ngroups = -(-b.num_seqs // samples)
+    shared = np.full(ngroups, prefix, np.int32)
+    shared[2] = 0
+    out_a, part_a, pools_a = _run_append(b, dev, part, shared, samples, lens)
+    out_s, part_s = _run(b, dev, part, shared, samples, lens)
+    _same_partials(part_a, part_s, lens, part)
+    assert np.array_equal(out_a.view(np.uint32), out_s.view(np.uint32))
+    # Pools: the same as writing every token with tv_cache_write.
+    import paged_kv_cache_tv_amd as tv
+    kc, vc = tv.new_pools(b.num_blocks, b.num_kv_heads, b.head_dim, b.block_size, dev,
+                          fill=W.BF16_NAN)
+    for k, v, sl in (b.fill_inputs(), b.step_inputs()):
+        live = sl >= 0
+        tv.cache_write(_to_dev(k[live], dev), _to_dev(v[live], dev), kc, vc,
+                       _to_dev(sl[live], dev))
+    assert np.array_equal(pools_a[0], kc.cpu().numpy().view(np.uint16))
+    assert np.array_equal(pools_a[1], vc.cpu().numpy().view(np.uint16))
