@@ -286,7 +286,8 @@ __device__ Unit plan_unit(const DecodeArgs &a, int j, int lane)
 // hold the same blocks for all members.  SHARED: one workgroup per (group,
 // K/V head, such partition) attends for every member at once -- column r of
 // the MFMAs is query head r % G of member r / G -- reading each tile once.
-// The per-sequence pass skips those partitions.
+// The per-sequence pass skips those partitions (with APPEND it still writes a
+// new token whose position lies in one, and attends nothing there).
 //
 // SPLIT wavefronts per workgroup (1 or 4): the partition's tiles are divided
 // into SPLIT equal consecutive ranges, wavefront w attends to range w with
@@ -295,14 +296,14 @@ __device__ Unit plan_unit(const DecodeArgs &a, int j, int lane)
 // across partitions.  With 4 wavefronts one workgroup occupies one slot on
 // each SIMD of its CU, so the CU's SIMDs share every partition's bytes
 // equally.
+//
+// decode_unit is the work of one workgroup; `bid` is its index in its pass.
 template <bool APPEND, bool SHARED, bool PLAN, int SPLIT>
-__global__ __launch_bounds__(64 * SPLIT)
-__attribute__((amdgpu_waves_per_eu(SPLIT > 1 ? 4 : 1, SPLIT > 1 ? 4 : 8)))
-void paged_decode_kernel(DecodeArgs a)
+__device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
 {
     constexpr int kRing = kRingFor<SPLIT>;
-    const int kvh = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
-    const int rest = (int)(blockIdx.x / (unsigned)a.num_kv_heads);
+    const int kvh = (int)(bid % (unsigned)a.num_kv_heads);
+    const int rest = (int)(bid / (unsigned)a.num_kv_heads);
     const int units = SHARED ? a.num_groups : a.num_seqs;
     int part = rest / units;
     int s = rest % units;                      // SHARED: the group; the sequence below
@@ -566,6 +567,30 @@ void paged_decode_kernel(DecodeArgs a)
     }
 }
 
+template <bool APPEND, bool SHARED, bool PLAN, int SPLIT>
+__global__ __launch_bounds__(64 * SPLIT)
+__attribute__((amdgpu_waves_per_eu(SPLIT > 1 ? 4 : 3, SPLIT > 1 ? 4 : 8)))
+void paged_decode_kernel(DecodeArgs a)
+{
+    decode_unit<APPEND, SHARED, PLAN, SPLIT>(a, blockIdx.x);
+}
+
+// A shared-prefix launch in one grid: workgroups [0, shared_groups) take the
+// group pass, the rest the per-sequence pass.  The two passes read disjoint
+// partitions and write disjoint partials, so one grid lets each fill the
+// other's tail.  shared_groups is a multiple of the K/V head count, so every
+// workgroup keeps its head's XCD.
+template <bool APPEND, int SPLIT>
+__global__ __launch_bounds__(64 * SPLIT)
+__attribute__((amdgpu_waves_per_eu(SPLIT > 1 ? 4 : 3, SPLIT > 1 ? 4 : 8)))
+void paged_decode_shared_kernel(DecodeArgs a, unsigned shared_groups)
+{
+    if (blockIdx.x < shared_groups)
+        decode_unit<false, true, false, SPLIT>(a, blockIdx.x);
+    else
+        decode_unit<APPEND, false, false, SPLIT>(a, blockIdx.x - shared_groups);
+}
+
 // What the launcher needs to know of the device: its compute units and how
 // many one-wavefront decode workgroups each holds at once (cached per device;
 // zeros if unknown).
@@ -631,15 +656,23 @@ hipError_t launch_paged_decode(const DecodeArgs &args, hipStream_t stream)
     const int64_t resident = (int64_t)dev.cus * dev.waves_per_cu;
     const bool split = resident > 0 && groups <= 2 * resident;
     if (a.shared_len) {
-        // Shared partitions first (one workgroup per group, head and partition).
+        // One workgroup per (group, head, partition) for the group pass, then
+        // one per (sequence, head, partition) for the rest, in one grid.
         const int64_t shared_groups = (int64_t)a.num_kv_heads * a.num_groups * a.num_parts;
-        if (split)
-            launch<false, true, false, 4>(a, shared_groups, stream);
+        const dim3 grid((unsigned)(shared_groups + groups));
+        if (split && a.k_new)
+            hipLaunchKernelGGL((paged_decode_shared_kernel<true, 4>), grid, dim3(256), 0, stream, a,
+                               (unsigned)shared_groups);
+        else if (split)
+            hipLaunchKernelGGL((paged_decode_shared_kernel<false, 4>), grid, dim3(256), 0, stream,
+                               a, (unsigned)shared_groups);
+        else if (a.k_new)
+            hipLaunchKernelGGL((paged_decode_shared_kernel<true, 1>), grid, dim3(64), 0, stream, a,
+                               (unsigned)shared_groups);
         else
-            launch<false, true, false, 1>(a, shared_groups, stream);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
+            hipLaunchKernelGGL((paged_decode_shared_kernel<false, 1>), grid, dim3(64), 0, stream, a,
+                               (unsigned)shared_groups);
+        return hipGetLastError();
     }
     // Balanced order: consecutive workgroups of one head cycle over
     // cus / gcd(heads, cus) compute units (32 on one XCD for 8 heads).
