@@ -297,6 +297,21 @@ def test_launch_policy_paths(dev, oracle_lib, num_seqs):
     assert np.abs(outs[0] - outs[1]).max() <= 1e-5
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (16, 4), (32, 2)])
+def test_launch_policy_head_counts(dev, oracle_lib, hq, hkv):
+    """Loose host bounds (the balanced order) and tight ones (4 wavefronts) with
+    1, 2 and 4 K/V heads: the order deals each head's workgroups over
+    cus / gcd(heads, cus) compute units, which is 256, 128 or 64 here."""
+    rng = np.random.default_rng(47 + hkv)
+    lens = rng.integers(1, 1200, size=96)
+    batch = W.make_batch(lens, 47 + hkv, num_q_heads=hq, num_kv_heads=hkv,
+                         table_width=131072 // 16)
+    ref, _, _ = O.decode_step(oracle_lib, batch)
+    for mc in (int(lens.max()), 131072):
+        got, _ = _gpu_step(batch, dev, max_context_len=mc)
+        _assert_close(got, ref, f"{hq}/{hkv} heads, max_context_len {mc}")
+
+
 # ---------------------------------------------------------------------------
 # tv_paged_attention_decode_append: the cache write folded into the partition
 # pass.  Under its precondition it must equal the three-call step bit for bit.
