@@ -229,7 +229,11 @@ void cache_write_kernel(CacheWriteArgs a)
 }
 
 // In-place rotary embedding of x [tokens][heads][head_dim], one wavefront per
-// token, with the same lane layout as the cache write above.
+// token, with the same lane layout as the cache write above.  A lane's
+// chunks (up to kRopeChunks rounds of 64) are all loaded before the first is
+// turned, so a token waits on memory once.
+constexpr int kRopeChunks = 8;
+
 __global__ __launch_bounds__(64 * kWavesPerGroup) void rope_kernel(RopeArgs a)
 {
     const int64_t tok = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
@@ -238,10 +242,36 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void rope_kernel(RopeArgs a)
     const int lane = threadIdx.x & 63;
     const int half = a.head_dim >> 1;
     const int groups = (a.num_heads * a.head_dim) >> 3;
+    uint16_t *xt = a.x + tok * a.num_heads * a.head_dim;
+    // Lane's pieces: style 0 one 16-byte chunk c; style 1 dims 4q..4q+3 of
+    // head h and their partners half further on (two 8-byte pieces).
+    auto piece_a = [&](int c) -> uint16_t * {
+        if (a.style == 0)
+            return xt + 8 * c;
+        const int h = (c << 3) / a.head_dim;
+        const int q = c % (a.head_dim >> 3);
+        return xt + h * a.head_dim + 4 * q;
+    };
+    uint4 in[kRopeChunks];
+#pragma unroll
+    for (int it = 0; it < kRopeChunks; ++it) {
+        const int c = it * 64 + lane;
+        in[it] = make_uint4(0, 0, 0, 0);
+        if (it * 64 < groups && c < groups) {
+            uint16_t *pa = piece_a(c);
+            if (a.style == 0) {
+                in[it] = *reinterpret_cast<const uint4 *>(pa);
+            } else {
+                const uint2 lo = *reinterpret_cast<const uint2 *>(pa);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(pa + half);
+                in[it] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+        }
+    }
     float pc, ps;
     rope_cos_sin(a.positions[tok], a.inv_freq[lane % half], pc, ps);
-    uint16_t *xt = a.x + tok * a.num_heads * a.head_dim;
     for (int base = 0; base < groups; base += 64) {
+        const int it = base >> 6;
         const int c = base + lane;
         const int q = c % (a.head_dim >> 3);
         float cs[4], sn[4];
@@ -252,10 +282,20 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void rope_kernel(RopeArgs a)
         }
         if (c >= groups)
             continue;
-        const int h = (c << 3) / a.head_dim;
+        uint4 kk = make_uint4(0, 0, 0, 0);
+        if (it < kRopeChunks) {
+#pragma unroll
+            for (int j = 0; j < kRopeChunks; ++j)
+                if (j == it)
+                    kk = in[j];
+        } else if (a.style == 0) {
+            kk = *reinterpret_cast<const uint4 *>(piece_a(c));
+        } else {
+            const uint2 lo = *reinterpret_cast<const uint2 *>(piece_a(c));
+            const uint2 hi = *reinterpret_cast<const uint2 *>(piece_a(c) + half);
+            kk = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
         if (a.style == 0) {
-            uint4 *p = reinterpret_cast<uint4 *>(xt) + c;
-            const uint4 kk = *p;
             const uint32_t w[4] = {kk.x, kk.y, kk.z, kk.w};
             uint32_t o[4];
 #pragma unroll
@@ -266,13 +306,9 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void rope_kernel(RopeArgs a)
                 o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ra) |
                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << 16);
             }
-            *p = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint4 *>(piece_a(c)) = make_uint4(o[0], o[1], o[2], o[3]);
         } else {
-            uint16_t *hx = xt + h * a.head_dim + 4 * q;
-            uint2 *qa = reinterpret_cast<uint2 *>(hx);
-            uint2 *qb = reinterpret_cast<uint2 *>(hx + half);
-            const uint2 pa = *qa, pb = *qb;
-            const uint32_t wa[2] = {pa.x, pa.y}, wb[2] = {pb.x, pb.y};
+            const uint32_t wa[2] = {kk.x, kk.y}, wb[2] = {kk.z, kk.w};
             uint32_t oa[2] = {0u, 0u}, ob[2] = {0u, 0u};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -284,8 +320,9 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void rope_kernel(RopeArgs a)
                 oa[i >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ra) << (16 * (i & 1));
                 ob[i >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << (16 * (i & 1));
             }
-            *qa = make_uint2(oa[0], oa[1]);
-            *qb = make_uint2(ob[0], ob[1]);
+            uint16_t *pa = piece_a(c);
+            *reinterpret_cast<uint2 *>(pa) = make_uint2(oa[0], oa[1]);
+            *reinterpret_cast<uint2 *>(pa + half) = make_uint2(ob[0], ob[1]);
         }
     }
 }
