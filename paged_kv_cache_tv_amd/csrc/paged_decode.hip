@@ -302,13 +302,15 @@ template <bool APPEND, bool SHARED, bool PLAN, int SPLIT>
 __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
 {
     constexpr int kRing = kRingFor<SPLIT>;
+    const int lane = (int)(threadIdx.x & 63);
+    const int wv = (int)(threadIdx.x >> 6);       // wavefront in the workgroup
     const int kvh = (int)(bid % (unsigned)a.num_kv_heads);
     const int rest = (int)(bid / (unsigned)a.num_kv_heads);
     const int units = SHARED ? a.num_groups : a.num_seqs;
     int part = rest / units;
     int s = rest % units;                      // SHARED: the group; the sequence below
     if (PLAN) {
-        const Unit u = plan_unit(a, rest, (int)(threadIdx.x & 63));
+        const Unit u = plan_unit(a, rest, lane);
         if (u.s < 0)
             return;
         s = u.s;
@@ -340,6 +342,17 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
             write_only = true;                 // the shared pass attends; only the cache write here
         }
     }
+    // The partition's table entries (partitions of up to 64 blocks) are
+    // loaded together with the context length, before the length says how
+    // many of them are used: entry l of the partition in lane l.  The row
+    // holds them: part * part_tiles < max_blocks since max_context_len <=
+    // max_blocks * block_size.
+    const bool table_ahead = a.part_tiles <= 64;
+    const int64_t row0 = (int64_t)s * a.max_blocks + (int64_t)part * a.part_tiles;
+    const int32_t ahead_lane =
+        table_ahead && lane < min(a.part_tiles, a.max_blocks - part * a.part_tiles)
+            ? a.block_tables[row0 + lane]
+            : 0;
     if (!SHARED) {
         n = a.context_lens[s];
         n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
@@ -350,8 +363,6 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
     const int ptok = min(n - first_tok, a.part_tiles * BS);    // tokens in this partition
     const int ntiles = (ptok + BS - 1) / BS;
 
-    const int lane = (int)(threadIdx.x & 63);
-    const int wv = (int)(threadIdx.x >> 6);       // wavefront in the workgroup
     const int r = lane & 15;
     const int g = lane >> 4;
     const float c = a.scale_log2;
@@ -473,9 +484,13 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
     const int nt = t_hi - t_lo;
     for (int c0 = 0; c0 < nt; c0 += 64) {
         const int cn = min(64, nt - c0);
-        const int32_t phys_lane = lane < cn ? bt[c0 + lane] : 0;   // one table entry per lane
+        // One table entry per lane: the entries loaded ahead (then nt <= 64,
+        // so c0 == 0 and the wavefront's tiles start at entry t_lo), or the
+        // chunk's own.
+        const int32_t phys_lane = table_ahead ? ahead_lane : (lane < cn ? bt[c0 + lane] : 0);
+        const int first = table_ahead ? t_lo : 0;
         auto block_of = [&](int k) -> int32_t {
-            return __builtin_amdgcn_readlane(phys_lane, min(k, cn - 1));
+            return __builtin_amdgcn_readlane(phys_lane, first + min(k, cn - 1));
         };
         Tile ring[kRing];
 #pragma unroll
