@@ -18,8 +18,9 @@
 //     the dispatcher deals consecutive workgroups round-robin over its
 //     compute units, each wavefront to the next SIMD; a SIMD's finishing time
 //     follows the tiles it was dealt.  With 4 wavefronts the partition's
-//     tiles are split evenly over the CU's 4 SIMDs.  With 1, large grids
-//     take a balanced order derived from the context lengths (plan_unit).
+//     tiles are split evenly over the CU's 4 SIMDs.  Grids larger than what
+//     the device holds at once take a balanced order derived from the
+//     context lengths (plan_unit).
 //   * One block of one K/V head is a 2 KiB K tile, stored as 8 chunks of
 //     [16 tokens][8 dims], plus a 2 KiB V tile [64 dims][16 tokens].  Each
 //     K load instruction reads 1 KiB contiguous (lane l: bytes 16l..16l+15 of
@@ -216,6 +217,8 @@ __device__ Unit plan_unit(const DecodeArgs &a, int j, int lane)
         const int nonlast = P > 0 ? P - 1 : 0;
         nparts[k] = P;
         last[k] = P > 0 ? tiles - nonlast * PT : 0;
+        if (k * 64 >= a.num_seqs)
+            continue;                            // no sequence in this chunk
         const int incl = wave_scan_incl(nonlast, lane);
         const int excl = incl - nonlast;
         const uint64_t m = __ballot(j >= F + excl && j < F + incl);
@@ -648,19 +651,23 @@ void launch(const DecodeArgs &a, int64_t groups, hipStream_t stream)
 
 }  // namespace
 
-// Launch policy, from the grid of one-wavefront workgroups per (sequence,
-// head, partition) that the host bounds give:
-//   * up to two rounds of what the device holds at once: 4 wavefronts per
-//     partition.  The launch then has many small workgroups, the hardware
-//     hands them out as slots free up, and each CU's 4 SIMDs share every
-//     partition's bytes, so no SIMD is left with more tiles than the others
-//     at the end (measured on batch 64 x 512-4096 tokens: 53.6 against
-//     56.6 us), and small batches get 4x the wavefronts;
-//   * beyond that (few very long sequences, or many sequences with room for
-//     long ones): one wavefront per partition, and for up to 256 sequences
-//     the balanced order of plan_unit, which moves the grid's empty
-//     partitions behind the work (batch 4 x 32k-128k tokens: 110.8 against
-//     121.9 us).
+// Launch policy, from the grid G of one-wavefront workgroups per (sequence,
+// head, partition) that the host bounds give and the number R of them the
+// device holds at once:
+//   * G <= 2R: 4 wavefronts per partition.  The launch then has many small
+//     workgroups, the hardware hands them out as slots free up, and each
+//     CU's 4 SIMDs share every partition's bytes, so no SIMD is left with
+//     more tiles than the others at the end (measured on batch 64 x
+//     512-4096 tokens: 53.6 against 56.6 us), and small batches get 4x the
+//     wavefronts;
+//   * G > 2R (few very long sequences, or many sequences with room for long
+//     ones): one wavefront per partition;
+//   * G > R and at most 256 sequences (no shared prefixes): the balanced
+//     order of plan_unit, which moves the grid's empty partitions behind the
+//     work (batch 4 x 32k-128k tokens: 110.8 against 121.9 us; batch 64 x
+//     512-4096 with 4 wavefronts: 53.6 against 54.8 us).  Below R the order's
+//     prologue is not hidden behind other workgroups' loads (batch 8: 9.3
+//     against 8.2 us), so small grids keep the plain order.
 // The shared-prefix launch takes the split its per-sequence grid would get,
 // so its partitions round exactly as the per-sequence pass's do.
 hipError_t launch_paged_decode(const DecodeArgs &args, hipStream_t stream)
@@ -692,9 +699,14 @@ hipError_t launch_paged_decode(const DecodeArgs &args, hipStream_t stream)
     // Balanced order: consecutive workgroups of one head cycle over
     // cus / gcd(heads, cus) compute units (32 on one XCD for 8 heads).
     a.plan_width = 0;
-    if (!split && !a.shared_len && a.num_seqs <= 64 * kPlanChunks && dev.cus > 0)
+    if (groups > resident && !a.shared_len && a.num_seqs <= 64 * kPlanChunks && dev.cus > 0)
         a.plan_width = dev.cus / std::gcd(a.num_kv_heads, dev.cus);
-    if (split) {
+    if (split && a.plan_width > 0) {
+        if (a.k_new)
+            launch<true, false, true, 4>(a, groups, stream);
+        else
+            launch<false, false, true, 4>(a, groups, stream);
+    } else if (split) {
         if (a.k_new)
             launch<true, false, false, 4>(a, groups, stream);
         else
