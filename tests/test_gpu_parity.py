@@ -204,6 +204,42 @@ def test_context_len_clamp_and_bad_table_entries(dev, oracle_lib):
     _assert_close(got2, ref, "clamped length")
 
 
+@pytest.mark.parametrize("num_seqs", [256, 300])
+def test_odd_device_data_large_grids(dev, oracle_lib, num_seqs):
+    """The same defined behaviour on grids past one resident round: 256
+    sequences (4 wavefronts, balanced order, whose scan reads every length)
+    and 300 (one wavefront, plain order)."""
+    import torch
+    from paged_kv_cache_tv_amd.step import DeviceBatch
+    rng = np.random.default_rng(48 + num_seqs)
+    lens = rng.integers(1, 1500, size=num_seqs)
+    lens[0] = 1500                                   # the longest: the clamp target
+    batch = W.make_batch(lens, 48 + num_seqs)
+    ref, _, _ = O.decode_step(oracle_lib, batch)
+    db = DeviceBatch(batch, dev)
+    db.fill()
+    db.write_step()
+    cl = db.context_lens.clone()
+    db.context_lens[1] = -7                          # negative length -> zero row
+    db.block_tables[2, 3] = batch.num_blocks + 11    # an entry past the pool
+    db.block_tables[2, 5] = -2                       # and a negative one
+    db.decode()
+    db.reduce()
+    got = db.out.cpu().numpy()
+    torch.cuda.synchronize()
+    assert (got[1] == 0).all()
+    assert np.isfinite(got[2]).all()
+    keep = np.ones(num_seqs, bool)
+    keep[[1, 2]] = False
+    _assert_close(got[keep], ref[keep], f"{num_seqs} sequences, untouched rows")
+    db.context_lens.copy_(cl)
+    db.block_tables.copy_(torch.from_numpy(batch.block_tables).to(dev))
+    db.context_lens[0] = 100000                      # cut to max_context_len = 1500
+    db.decode()
+    db.reduce()
+    _assert_close(db.out.cpu().numpy(), ref, f"{num_seqs} sequences, clamped length")
+
+
 def test_cache_write_skips_padding_and_out_of_pool(dev, oracle_lib):
     import torch
     import paged_kv_cache_tv_amd as tv
