@@ -205,16 +205,23 @@ tv_status tv_paged_attention_decode(float *part_acc, float *part_max, float *par
  * blocks).  The same partials as tv_paged_attention_decode; the shared
  * prefix's tiles are read once per group instead of once per sequence.
  *
- * Sequences g*group_size .. min((g+1)*group_size, num_seqs) - 1 form group g.
+ * The sequences at positions g*group_size .. min((g+1)*group_size, num_seqs)
+ * - 1 form group g, where position p holds sequence group_order[p] (a
+ * permutation of 0 .. num_seqs-1), or sequence p when group_order is NULL.
  * With sh = min(shared_len[g], context length of every member of g), the
  * partitions p < floor(sh / partition_size) of the group's members are
- * computed together from the block table of the group's first sequence.
+ * computed together from the block table of the group's first member.
  * Precondition: for those positions every member's table holds the same
  * blocks as the first member's (as after tv_bm_fork).  Then the partials are
  * those of tv_paged_attention_decode bit for bit.  shared_len[g] = 0 (or
  * group_size 1) leaves a group to the per-sequence pass.
  *
  *   shared_len   int32 [ceil(num_seqs / group_size)] (device), 4-byte aligned
+ *   group_order  int32 [num_seqs] (device) or NULL, 4-byte aligned.  An entry
+ *                outside [0, num_seqs) leaves its position out (its group
+ *                shares nothing); a sequence listed twice, or not at all, is
+ *                the caller's error (its partials are computed twice, or not
+ *                written).
  *   group_size   1 .. 16 / (num_q_heads / num_kv_heads)  (4 for groups of 4 heads)
  *   other arguments as for tv_paged_attention_decode.
  * Errors: as for tv_paged_attention_decode, plus TV_ERR_SHAPE for
@@ -225,7 +232,8 @@ tv_status tv_paged_attention_decode_shared(float *part_acc, float *part_max, flo
                                            const uint16_t *q, const uint16_t *k_cache,
                                            const uint16_t *v_cache, const int32_t *block_tables,
                                            const int32_t *context_lens, const int32_t *shared_len,
-                                           int32_t group_size, int32_t num_seqs,
+                                           const int32_t *group_order, int32_t group_size,
+                                           int32_t num_seqs,
                                            int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t block_size,
                                            int32_t max_blocks_per_seq, int64_t num_blocks,
@@ -291,17 +299,18 @@ tv_status tv_paged_attention_decode_append(float *part_acc, float *part_max, flo
  * token is still written, but the group pass has attended that slot's
  * previous contents.
  *
- *   arguments as for tv_paged_attention_decode_append, plus shared_len and
- *   group_size as for tv_paged_attention_decode_shared.
+ *   arguments as for tv_paged_attention_decode_append, plus shared_len,
+ *   group_order and group_size as for tv_paged_attention_decode_shared.
  * Supported shapes and errors: the union of both calls'.
  */
 tv_status tv_paged_attention_decode_shared_append(
     float *part_acc, float *part_max, float *part_sum, const uint16_t *q, const uint16_t *k_new,
     const uint16_t *v_new, const int64_t *slot_mapping, uint16_t *k_cache, uint16_t *v_cache,
     const int32_t *block_tables, const int32_t *context_lens, const int32_t *shared_len,
-    int32_t group_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
-    int32_t max_context_len, int32_t partition_size, float scale, void *stream);
+    const int32_t *group_order, int32_t group_size, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int64_t num_blocks, int32_t max_context_len, int32_t partition_size, float scale,
+    void *stream);
 
 /*
  * Log-sum-exp merge of the partitions ("vLLM" page, Flash Attention: the

@@ -52,13 +52,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                      i32, i32, i32, i32, i32, i32, i64, i32, i32,
                                                      f32, vp]
     lib.tv_paged_attention_decode_shared.restype = ctypes.c_int
-    lib.tv_paged_attention_decode_shared.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
-                                                     i32, i32, i32, i32, i32, i64, i32, i32,
+    lib.tv_paged_attention_decode_shared.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                                     i32, i32, i32, i32, i32, i32, i64, i32, i32,
                                                      ctypes.c_float, vp]
     lib.tv_paged_attention_decode_shared_append.restype = ctypes.c_int
     lib.tv_paged_attention_decode_shared_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                                            vp, vp, i32, i32, i32, i32, i32, i32,
-                                                            i32, i64, i32, i32, ctypes.c_float, vp]
+                                                            vp, vp, vp, i32, i32, i32, i32, i32,
+                                                            i32, i32, i64, i32, i32, ctypes.c_float,
+                                                            vp]
     lib.tv_paged_attention_reduce.restype = ctypes.c_int
     lib.tv_paged_attention_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.tv_paged_attention_prefill.restype = ctypes.c_int
@@ -285,13 +286,24 @@ def paged_attention_prefill(out, q, query_start, k_cache, v_cache, block_tables,
     _check("tv_paged_attention_prefill", st)
 
 
+def _group_order_ptr(group_order, S):
+    import torch
+    if group_order is None:
+        return None
+    _need(group_order, "group_order", dtype=torch.int32, ndim=1)
+    if group_order.shape[0] != S:
+        raise ValueError("group_order must have one entry per sequence")
+    return group_order.data_ptr()
+
+
 def paged_attention_decode_shared(part_acc, part_max, part_sum, q, k_cache, v_cache,
                                   block_tables, context_lens, shared_len, group_size: int,
                                   max_context_len: int, partition_size: int, scale: float,
-                                  stream=None) -> None:
+                                  stream=None, group_order=None) -> None:
     """tv_paged_attention_decode_shared: the partition pass with the shared
-    prefix of each group of ``group_size`` consecutive sequences read once;
-    shared_len: int32 [ceil(S / group_size)]."""
+    prefix of each group of ``group_size`` sequences read once; shared_len:
+    int32 [ceil(S / group_size)]; group_order: int32 [S] (position p holds
+    sequence group_order[p]) or None for consecutive groups."""
     import torch
     _need(q, "q", itemsize=2, ndim=3)
     _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
@@ -311,10 +323,11 @@ def paged_attention_decode_shared(part_acc, part_max, part_sum, q, k_cache, v_ca
         raise ValueError("block_tables / context_lens must have one row per sequence")
     if group_size < 1 or shared_len.shape[0] != -(-S // group_size):
         raise ValueError("shared_len must have ceil(S / group_size) entries")
+    order = _group_order_ptr(group_order, S)
     st = lib().tv_paged_attention_decode_shared(
         part_acc.data_ptr(), part_max.data_ptr(), part_sum.data_ptr(), q.data_ptr(),
         k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
-        shared_len.data_ptr(), int(group_size), S, hq, hkv, d, bs, block_tables.shape[1], nb,
+        shared_len.data_ptr(), order, int(group_size), S, hq, hkv, d, bs, block_tables.shape[1], nb,
         int(max_context_len), int(partition_size), float(scale), _stream_handle(stream, q.device))
     _check("tv_paged_attention_decode_shared", st)
 
@@ -361,9 +374,10 @@ def paged_attention_decode_shared_append(part_acc, part_max, part_sum, q, k_new,
                                          slot_mapping, k_cache, v_cache, block_tables,
                                          context_lens, shared_len, group_size: int,
                                          max_context_len: int, partition_size: int, scale: float,
-                                         stream=None) -> None:
+                                         stream=None, group_order=None) -> None:
     """tv_paged_attention_decode_shared_append: the cache write of one new
-    token per sequence and the shared-prefix partition pass (two launches)."""
+    token per sequence and the shared-prefix partition pass, in one launch;
+    group_order as for paged_attention_decode_shared."""
     import torch
     _need(q, "q", itemsize=2, ndim=3)
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
@@ -389,11 +403,12 @@ def paged_attention_decode_shared_append(part_acc, part_max, part_sum, q, k_new,
         raise ValueError("block_tables / context_lens must have one row per sequence")
     if group_size < 1 or shared_len.shape[0] != -(-S // group_size):
         raise ValueError("shared_len must have ceil(S / group_size) entries")
+    order = _group_order_ptr(group_order, S)
     st = lib().tv_paged_attention_decode_shared_append(
         part_acc.data_ptr(), part_max.data_ptr(), part_sum.data_ptr(), q.data_ptr(),
         k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
         v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
-        shared_len.data_ptr(), int(group_size), S, hq, hkv, d, bs, block_tables.shape[1], nb,
+        shared_len.data_ptr(), order, int(group_size), S, hq, hkv, d, bs, block_tables.shape[1], nb,
         int(max_context_len), int(partition_size), float(scale), _stream_handle(stream, q.device))
     _check("tv_paged_attention_decode_shared_append", st)
 

@@ -283,8 +283,10 @@ __device__ Unit plan_unit(const DecodeArgs &a, int j, int lane)
 // the block table gives for position n-1 -- attends to the new values straight
 // from registers, so no other workgroup and no earlier kernel is involved.
 //
-// Shared prefixes (a.shared_len != nullptr): sequences g*group_size ..
-// g*group_size + group_size - 1 form group g, and the partitions lying wholly
+// Shared prefixes (a.shared_len != nullptr): the sequences at positions
+// g*group_size .. g*group_size + group_size - 1 form group g (position p
+// holds sequence group_order[p], or p without an order; an entry outside
+// [0, num_seqs) leaves its position out), and the partitions lying wholly
 // inside its first shared_len[g] tokens (clamped to every member's context)
 // hold the same blocks for all members.  SHARED: one workgroup per (group,
 // K/V head, such partition) attends for every member at once -- column r of
@@ -322,21 +324,29 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
     int members = 1;
     int n = 0;
     bool write_only = false;
+    int first = 0;                             // SHARED: position of the group's first member
+    auto seq_at = [&](int p) -> int { return a.group_order ? a.group_order[p] : p; };
     if (a.shared_len) {
-        const int grp = SHARED ? s : s / a.group_size;
-        const int first = grp * a.group_size;
+        const int grp = SHARED ? s : s / a.group_size;   // s: the group, or a position
+        first = grp * a.group_size;
         const int cnt = min(a.group_size, a.num_seqs - first);
         int sh = a.shared_len[grp];
         for (int m = 0; m < cnt; ++m) {
-            int nm = a.context_lens[first + m];
+            const int sm = seq_at(first + m);
+            int nm = sm >= 0 && sm < a.num_seqs ? a.context_lens[sm] : 0;   // left out: no sharing
             nm = nm < 0 ? 0 : (nm > a.max_context_len ? a.max_context_len : nm);
             sh = min(sh, nm);
         }
         const int shared_parts = sh > 0 ? sh / (a.part_tiles * BS) : 0;
+        if (!SHARED) {
+            s = seq_at(s);                     // the position's sequence
+            if (s < 0 || s >= a.num_seqs)
+                return;
+        }
         if (SHARED) {
             if (part >= shared_parts)
                 return;
-            s = first;
+            s = seq_at(first);
             members = cnt;
             n = shared_parts * a.part_tiles * BS;
         } else if (part < shared_parts) {
@@ -372,10 +382,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
     const int G = a.group;
 
     // B operands of the score MFMAs: column r = query head kvh*G + r % G of
-    // sequence s + r / G (r < G except in the shared pass), rows = dims
-    // 8g..8g+7 (first MFMA) and 32+8g..32+8g+7 (second).
-    const int col_seq = s + r / G;
+    // the group's member r / G in the shared pass (r < members * G), of
+    // sequence s otherwise (r < G); rows = dims 8g..8g+7 (first MFMA) and
+    // 32+8g..32+8g+7 (second).
     const bool col_ok = SHARED ? r < members * G : r < G;
+    const int col_seq = SHARED ? (col_ok ? seq_at(first + r / G) : 0) : s;
     bf16x8 qb0 = {}, qb1 = {};
     if (col_ok) {
         const uint16_t *qp = a.q + ((int64_t)col_seq * a.num_kv_heads * G + (int64_t)kvh * G + r % G) * D + g * 8;

@@ -291,7 +291,8 @@ tv_status tv_paged_attention_decode_shared(float *part_acc, float *part_max, flo
                                            const uint16_t *q, const uint16_t *k_cache,
                                            const uint16_t *v_cache, const int32_t *block_tables,
                                            const int32_t *context_lens, const int32_t *shared_len,
-                                           int32_t group_size, int32_t num_seqs,
+                                           const int32_t *group_order, int32_t group_size,
+                                           int32_t num_seqs,
                                            int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t block_size,
                                            int32_t max_blocks_per_seq, int64_t num_blocks,
@@ -314,9 +315,10 @@ tv_status tv_paged_attention_decode_shared(float *part_acc, float *part_max, flo
         return TV_OK;
     if (!shared_len)
         return TV_ERR_NULL;
-    if (!aligned(shared_len, 4))
+    if (!aligned(shared_len, 4) || !aligned(group_order, 4))
         return TV_ERR_ALIGNMENT;
     a.shared_len = shared_len;
+    a.group_order = group_order;
     a.group_size = group_size;
     a.num_groups = (int32_t)ceil_div(num_seqs, group_size);
     return from_hip(tv::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
@@ -326,9 +328,9 @@ tv_status tv_paged_attention_decode_shared_append(
     float *part_acc, float *part_max, float *part_sum, const uint16_t *q, const uint16_t *k_new,
     const uint16_t *v_new, const int64_t *slot_mapping, uint16_t *k_cache, uint16_t *v_cache,
     const int32_t *block_tables, const int32_t *context_lens, const int32_t *shared_len,
-    int32_t group_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
-    int32_t max_context_len, int32_t partition_size, float scale, void *stream)
+    const int32_t *group_order, int32_t group_size, int32_t num_seqs, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int64_t num_blocks, int32_t max_context_len, int32_t partition_size, float scale, void *stream)
 {
     if (group_size < 1)
         return TV_ERR_SHAPE;
@@ -344,12 +346,13 @@ tv_status tv_paged_attention_decode_shared_append(
         return st;
     if (!shared_len || !k_new || !v_new || !slot_mapping)
         return TV_ERR_NULL;
-    if (!aligned(shared_len, 4) || !aligned(k_new, 16) || !aligned(v_new, 2) ||
-        !aligned(slot_mapping, 8))
+    if (!aligned(shared_len, 4) || !aligned(group_order, 4) || !aligned(k_new, 16) ||
+        !aligned(v_new, 2) || !aligned(slot_mapping, 8))
         return TV_ERR_ALIGNMENT;
     if (num_blocks > INT64_MAX / block_size)
         return TV_ERR_SHAPE;
     a.shared_len = shared_len;
+    a.group_order = group_order;
     a.group_size = group_size;
     a.num_groups = (int32_t)ceil_div(num_seqs, group_size);
     a.k_new = k_new;

@@ -67,6 +67,7 @@ struct DecodeArgs {
     uint16_t *v_cache_w;
     // Shared prefixes (tv_paged_attention_decode_shared): shared_len == nullptr: none.
     const int32_t *shared_len;  // [num_groups]: leading tokens shared by group g's sequences
+    const int32_t *group_order; // [num_seqs] or nullptr: position p holds sequence group_order[p]
     int32_t group_size;         // sequences per group (consecutive), 1 .. 16 / group
     int32_t num_groups;         // ceil(num_seqs / group_size)
     // Set by the launcher: > 0 selects the balanced workgroup order and gives

@@ -135,7 +135,7 @@ def test_decode_append_validation(lib):
     assert _app(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
 
 
-def _shd(lib, S=2, hq=32, hkv=8, gs=4, mctx=64, part=32, ptrs=(BAD,) * 9):
+def _shd(lib, S=2, hq=32, hkv=8, gs=4, mctx=64, part=32, ptrs=(BAD,) * 10):
     return lib.tv_paged_attention_decode_shared(*ptrs, gs, S, hq, hkv, 64, 16, 4, 8, mctx, part,
                                                 0.125, None)
 
@@ -148,14 +148,17 @@ def test_decode_shared_validation(lib):
     assert _shd(lib, S=0) == TV_OK
     assert _shd(lib, mctx=0) == TV_OK
     assert _shd(lib) == TV_ERR_ALIGNMENT                  # the decode arguments are checked first
-    ptrs = [ALIGNED] * 9
+    ptrs = [ALIGNED] * 10
     ptrs[8] = None
     assert _shd(lib, ptrs=tuple(ptrs)) == TV_ERR_NULL
     ptrs[8] = 0x1002
     assert _shd(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
+    ptrs = [ALIGNED] * 10
+    ptrs[9] = 0x1002                                      # group_order misaligned (NULL is allowed)
+    assert _shd(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
 
 
-def _sha(lib, S=2, hq=32, hkv=8, gs=4, mctx=64, part=32, ptrs=(BAD,) * 12):
+def _sha(lib, S=2, hq=32, hkv=8, gs=4, mctx=64, part=32, ptrs=(BAD,) * 13):
     return lib.tv_paged_attention_decode_shared_append(*ptrs, gs, S, hq, hkv, 64, 16, 4, 8, mctx,
                                                        part, 0.125, None)
 
@@ -171,11 +174,13 @@ def test_decode_shared_append_validation(lib):
     # The partition-pass arguments pass their checks; each of the shared and
     # append ones is then refused when NULL or misaligned (nothing launches).
     for i in (4, 5, 6, 11):                               # k_new, v_new, slot_mapping, shared_len
-        ptrs = [ALIGNED] * 12
+        ptrs = [ALIGNED] * 12 + [None]                    # group_order NULL: consecutive groups
         ptrs[i] = None
         assert _sha(lib, ptrs=tuple(ptrs)) == TV_ERR_NULL
         ptrs[i] = BAD
         assert _sha(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
+    ptrs = [ALIGNED] * 12 + [BAD]                         # group_order misaligned
+    assert _sha(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
 
 
 def _pre(lib, S=2, hq=32, hkv=8, d=64, bs=16, mb=4, nb=8, mq=40, mctx=64, scale=0.125,

@@ -190,3 +190,68 @@ def test_shared_append_ragged_groups(dev, samples, prefix, part):
                        _to_dev(sl[live], dev))
     assert np.array_equal(pools_a[0], kc.cpu().numpy().view(np.uint16))
     assert np.array_equal(pools_a[1], vc.cpu().numpy().view(np.uint16))
+
+
+@pytest.mark.parametrize("append", [False, True])
+def test_shared_groups_in_any_order(dev, append):
+    """Groups given by a member order instead of consecutive positions: the
+    shared-prefix workload with its sequences shuffled must give, sequence
+    for sequence, the partials and output of the consecutive layout bit for
+    bit (and with appends, the same pools)."""
+    import torch
+    import paged_kv_cache_tv_amd as tv
+    b = W.make_workload(4)
+    S = b.num_seqs
+    perm = np.random.default_rng(140).permutation(S)      # sequence i moves to index perm[i]
+    order = perm.astype(np.int32)                         # position i (group i // 4) -> perm[i]
+    part = 512
+    shared = np.full(S // 4, 1024, np.int32)
+
+    def run(shuffled):
+        kc, vc = tv.new_pools(b.num_blocks, b.num_kv_heads, b.head_dim, b.block_size, dev,
+                              fill=W.BF16_NAN)
+        k, v, sl = b.fill_inputs()
+        live = sl >= 0
+        tv.cache_write(_to_dev(k[live], dev), _to_dev(v[live], dev), kc, vc,
+                       _to_dev(sl[live], dev))
+        sk, sv, ss = b.step_inputs()
+        if not append:
+            live = ss >= 0
+            tv.cache_write(_to_dev(sk[live], dev), _to_dev(sv[live], dev), kc, vc,
+                           _to_dev(ss[live], dev))
+
+        def arr(x):                                       # row i of x -> row perm[i]
+            if not shuffled:
+                return x
+            y = np.empty_like(x)
+            y[perm] = x
+            return y
+        mc = int(b.context_lens.max())
+        ws = tv.new_workspace(S, b.num_q_heads, b.head_dim, mc, part, dev)
+        for t in ws:
+            t.fill_(float("nan"))
+        q, bt, cl = _to_dev(arr(b.q), dev), _to_dev(arr(b.block_tables), dev), \
+            _to_dev(arr(b.context_lens), dev)
+        go = _to_dev(order, dev) if shuffled else None
+        if append:
+            tv.paged_attention_decode_shared_append(
+                *ws, q, _to_dev(arr(sk), dev), _to_dev(arr(sv), dev),
+                _to_dev(arr(ss.astype(np.int64)), dev), kc, vc, bt, cl, _to_dev(shared, dev), 4,
+                mc, part, b.scale, group_order=go)
+        else:
+            tv.paged_attention_decode_shared(*ws, q, kc, vc, bt, cl, _to_dev(shared, dev), 4, mc,
+                                             part, b.scale, group_order=go)
+        out = torch.empty((S, b.num_q_heads, b.head_dim), dtype=torch.float32, device=dev)
+        tv.paged_attention_reduce(out, *ws, cl, mc, part)
+        torch.cuda.synchronize()
+        res = [out.cpu().numpy()] + [t.cpu().numpy() for t in ws]
+        if shuffled:
+            res = [r[perm] for r in res]                  # back to the original sequence order
+        pools = (kc.cpu().numpy().view(np.uint16), vc.cpu().numpy().view(np.uint16))
+        return res, pools
+
+    (out_c, *part_c), pools_c = run(False)
+    (out_s, *part_s), pools_s = run(True)
+    _same_partials(part_s, part_c, b.context_lens, part)
+    assert np.array_equal(out_s.view(np.uint32), out_c.view(np.uint32))
+    assert np.array_equal(pools_s[0], pools_c[0]) and np.array_equal(pools_s[1], pools_c[1])
