@@ -152,6 +152,26 @@ def test_engine_flow(dev, oracle_lib):
             tv.paged_attention_reduce(out2, *ws2, cl, mc, PART)
             torch.cuda.synchronize()
             assert torch.equal(out2.view(torch.int32), outd.view(torch.int32)), step
+        else:
+            # After a sample has ended the prompts' samples are no longer in
+            # consecutive rows: give the groups as a member order (prompt 0,
+            # prompt 2, then prompt 1's two remaining samples as a partial
+            # last group), with the new tokens appended again by the shared
+            # pass (the same bits into the same slots).
+            by_prompt = {i: [r for r, seq in enumerate(live) if seq // SAMPLES == i]
+                         for i in range(len(prompts))}
+            groups = [0, 2, 1]
+            order = np.array(sum((by_prompt[i] for i in groups), []), np.int32)
+            assert [len(by_prompt[i]) for i in groups] == [SAMPLES, SAMPLES, SAMPLES - 1]
+            shared = np.array([(prompts[i] // BS) * BS for i in groups], np.int32)
+            ws2 = tv.new_workspace(S, HQ, D, mc, PART, dev)
+            out2 = torch.empty_like(outd)
+            tv.paged_attention_decode_shared_append(
+                *ws2, qd, kd, _to_dev(v_new, dev), _to_dev(slots, dev), kc, vc, bt, cl,
+                _to_dev(shared, dev), SAMPLES, mc, PART, SCALE, group_order=_to_dev(order, dev))
+            tv.paged_attention_reduce(out2, *ws2, cl, mc, PART)
+            torch.cuda.synchronize()
+            assert torch.equal(out2.view(torch.int32), outd.view(torch.int32)), step
         for r, seq in enumerate(live):
             k, v = hist[seq]
             hist[seq] = (np.concatenate([k, k_new[r:r + 1]]), np.concatenate([v, v_new[r:r + 1]]))
