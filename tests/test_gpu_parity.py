@@ -348,6 +348,42 @@ def test_launch_policy_head_counts(dev, oracle_lib, hq, hkv):
         _assert_close(got, ref, f"{hq}/{hkv} heads, max_context_len {mc}")
 
 
+_RANDOM_CASES = [
+    # (seed, sequences, max length, partition, query heads, K/V heads, loose host bound)
+    (60, 1, 5000, 512, 32, 8, False),
+    (61, 5, 3000, 64, 16, 2, True),
+    (62, 33, 2500, 256, 32, 8, False),
+    (63, 130, 1800, 512, 8, 8, False),
+    (64, 17, 4100, 2048, 32, 4, True),
+    (65, 300, 600, 128, 32, 8, False),
+    (66, 64, 4096, 512, 32, 8, True),
+    (67, 200, 900, 512, 64, 4, False),
+]
+
+
+@pytest.mark.parametrize("case", _RANDOM_CASES, ids=[f"seed{c[0]}" for c in _RANDOM_CASES])
+def test_random_configurations(dev, oracle_lib, case):
+    """Seeded batches across the launch forms (4 wavefronts or 1, balanced or
+    plain order), partition sizes, group sizes and host bounds: the output
+    meets the bars against the oracle, the pools match its cache write bit
+    for bit, and the two-launch step equals the three-launch step bit for
+    bit."""
+    seed, S, maxlen, part, hq, hkv, loose = case
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, maxlen + 1, size=S)
+    width = 8192 if loose else None
+    batch = W.make_batch(lens, seed, num_q_heads=hq, num_kv_heads=hkv, table_width=width)
+    ref, kc_ref, vc_ref = O.decode_step(oracle_lib, batch)
+    mc = 8192 * 16 if loose else int(lens.max())
+    got, db = _gpu_step(batch, dev, partition_size=part, max_context_len=mc)
+    kc, vc = db.pools_numpy()
+    assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+    _assert_close(got, ref, f"seed {seed}: {S} x <= {maxlen} tokens, partition {part}, "
+                            f"{hq}/{hkv} heads, host bound {mc}")
+    fused, _ = _gpu_step(batch, dev, partition_size=part, max_context_len=mc, fused=True)
+    assert np.array_equal(got, fused)
+
+
 # ---------------------------------------------------------------------------
 # tv_paged_attention_decode_append: the cache write folded into the partition
 # pass.  Under its precondition it must equal the three-call step bit for bit.
