@@ -2,11 +2,13 @@
 // Attention": the running maximum / running sum rule, applied across the
 // context partitions of one sequence and query head).
 //
-// Short contexts (at most kMerge partitions): one wavefront per (sequence,
-// query head), four per workgroup.  Such a merge is latency-bound (a few
-// hundred bytes per wavefront), so it waits on memory only twice: the context
-// length, then -- issued together -- the partition maxima and sums (lane p
-// holds partition p) and the partition rows (lane d holds dimension d).
+// Short contexts (at most kMerge partitions in the workspace): one wavefront
+// per (sequence, query head), four per workgroup.  Such a merge is
+// latency-bound (a few hundred bytes per wavefront), so it waits on memory
+// once: the context length, the partition maxima and sums (lane p holds
+// partition p) and the rows of every workspace partition (lane d holds
+// dimension d) are loaded together, and the partitions past the sequence's
+// end -- never written, so any bits -- are selected away afterwards.
 //
 // Longer contexts: one 256-thread workgroup per (sequence, query head);
 // thread (group q = tid/16, column c = tid%16) accumulates the float4 column
@@ -55,22 +57,23 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void paged_reduce_kernel(Reduc
     const int lane = threadIdx.x & 63;
     const int s = (int)(sh / a.num_q_heads);
 
+    // Issue every load before using any of them.
+    const int P = a.num_parts;                     // <= kMerge here
+    const float *pm = a.part_max + sh * P;
+    const float *pl = a.part_sum + sh * P;
+    const float *pa = a.part_acc + sh * P * D;
     int n = a.context_lens[s];
-    n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
-    const int np = (n + a.partition_size - 1) / a.partition_size;
-    float *out = a.out + sh * D;
-
-    const float *pm = a.part_max + sh * a.num_parts;
-    const float *pl = a.part_sum + sh * a.num_parts;
-    const float *pa = a.part_acc + sh * a.num_parts * D;
-
-    // Issue everything the common case needs before using any of it.
     float rows[kMerge];
 #pragma unroll
     for (int j = 0; j < kMerge; ++j)
-        rows[j] = j < np ? pa[(int64_t)j * D + lane] : 0.f;
-    const float m_lane = lane < np ? pm[lane] : -INFINITY;
-    const float l_lane = lane < np ? pl[lane] : 0.f;
+        rows[j] = j < P ? pa[(int64_t)j * D + lane] : 0.f;
+    const float m_raw = lane < P ? pm[lane] : -INFINITY;
+    const float l_raw = lane < P ? pl[lane] : 0.f;
+    n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
+    const int np = (n + a.partition_size - 1) / a.partition_size;
+    float *out = a.out + sh * D;
+    const float m_lane = lane < np ? m_raw : -INFINITY;
+    const float l_lane = lane < np ? l_raw : 0.f;
 
     // Maximum over all partitions (lane p covers p, p + 64, ...).
     float m_all = m_lane;
