@@ -329,7 +329,8 @@ tv_status tv_paged_attention_decode_shared_append(
  *                 partition_size; part_acc 16-byte aligned
  *   context_lens  int32 [num_seqs]
  *
- * Supported shapes: head_dim == 64.
+ * Supported shapes: head_dim == 64, num_seqs * num_q_heads < 2^24 (one
+ * workgroup per row in the launch grid).
  * Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED, TV_ERR_ALIGNMENT,
  * TV_ERR_HIP.  num_seqs == 0 is a no-op.  With max_context_len == 0 every row
  * of out is set to zero.

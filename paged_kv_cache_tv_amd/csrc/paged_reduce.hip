@@ -10,10 +10,16 @@
 // dimension d) are loaded together, and the partitions past the sequence's
 // end -- never written, so any bits -- are selected away afterwards.
 //
-// Longer contexts: one 256-thread workgroup per (sequence, query head);
-// thread (group q = tid/16, column c = tid%16) accumulates the float4 column
-// c of partitions q, q+16, q+32, ..., eight rows in flight at a time, and the
-// 16 groups are summed through shuffles and LDS.
+// 9 to 256 partitions and few rows (s, h) -- very long contexts at a small
+// batch, where one workgroup per row would leave most of the device idle:
+// each row is split over four workgroups of four float4 columns each, and a
+// workgroup waits on memory once (every partition's column, maximum and sum
+// loaded together with the context length).
+//
+// Otherwise: one 256-thread workgroup per (sequence, query head); thread
+// (group q = tid/16, column c = tid%16) accumulates the float4 column c of
+// partitions q, q+16, q+32, ..., eight rows in flight at a time, and the 16
+// groups are summed through shuffles and LDS.
 //
 // Summation orders are fixed, so results are bitwise reproducible run to run.
 #include "tv_internal.h"
@@ -58,7 +64,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void paged_reduce_kernel(Reduc
     const int s = (int)(sh / a.num_q_heads);
 
     // Issue every load before using any of them.
-    const int P = a.num_parts;                     // <= kMerge here
+    const int P = a.num_parts;                     // <= kMerge here, so np <= kMerge
     const float *pm = a.part_max + sh * P;
     const float *pl = a.part_sum + sh * P;
     const float *pa = a.part_acc + sh * P * D;
@@ -75,37 +81,134 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void paged_reduce_kernel(Reduc
     const float m_lane = lane < np ? m_raw : -INFINITY;
     const float l_lane = lane < np ? l_raw : 0.f;
 
-    // Maximum over all partitions (lane p covers p, p + 64, ...).
-    float m_all = m_lane;
-    for (int p = 64 + lane; p < np; p += 64)
-        m_all = fmaxf(m_all, pm[p]);
-    const float M = wave_max(m_all);
+    const float M = wave_max(m_lane);
     if (M == -INFINITY) {                          // no partition / no usable token
         out[lane] = 0.f;
         return;
     }
 
     const float w_lane = m_lane == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_lane - M);
-    float den_part = w_lane * l_lane;
+    const float den_part = w_lane * l_lane;
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < kMerge; ++j)
         if (j < np)
             acc = fmaf(lane_value(w_lane, j), rows[j], acc);
-    for (int j = kMerge; j < min(np, 64); ++j)
-        acc = fmaf(lane_value(w_lane, j), pa[(int64_t)j * D + lane], acc);
-
-    // Partitions beyond the first 64 (contexts longer than 64 partitions).
-    for (int p0 = 64; p0 < np; p0 += 64) {
-        const float mp = p0 + lane < np ? pm[p0 + lane] : -INFINITY;
-        const float wp = mp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mp - M);
-        den_part = fmaf(wp, p0 + lane < np ? pl[p0 + lane] : 0.f, den_part);
-        const int cnt = min(64, np - p0);
-        for (int j = 0; j < cnt; ++j)
-            acc = fmaf(lane_value(wp, j), pa[(int64_t)(p0 + j) * D + lane], acc);
-    }
     const float den = wave_sum(den_part);
     out[lane] = acc / den;
+}
+
+// 9 .. kMid workspace partitions: every load issued at once.  The 16 float4
+// columns of a (s, h) row are split over SPLIT workgroups (blockIdx.y), so
+// that short batches still spread over the device; each workgroup holds
+// C = 16 / SPLIT columns.  Thread (group q = tid / C, column c = tid % C)
+// holds its column of partitions q, q + G, q + 2G, ... (G = 256 / C groups)
+// together with their maxima and sums, loaded alongside the context length;
+// partitions past the sequence's end are selected away.  The maximum, the
+// sum and the groups' partial rows are then combined through shuffles and
+// LDS in a fixed order.
+constexpr int kMid = 256;
+constexpr int kMidSplit = 4;
+// Rows (s, h) up to which the split form runs.  Past it the grid fills the
+// device anyway, and the wide kernel's whole-row loads (a wavefront reads
+// four contiguous 256-byte rows) and single read of the maxima and sums
+// win: at 2048 rows it is 1.9x (64 partitions) to 3x (256) faster.
+constexpr int64_t kMidRows = 256;
+
+template <int SPLIT>
+__global__ __launch_bounds__(256) void paged_reduce_mid_kernel(ReduceArgs a)
+{
+    constexpr int C = 16 / SPLIT;                  // float4 columns per workgroup
+    constexpr int G = 256 / C;                     // partition groups
+    constexpr int U = kMid / G;                    // partitions per thread
+    const int64_t sh = blockIdx.x;                 // s * Hq + h
+    const int s = (int)(sh / a.num_q_heads);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int q = tid / C;
+    const int c = tid % C;
+    const int col = (int)blockIdx.y * C + c;
+    const int P = a.num_parts;                     // kMerge < P <= kMid
+    const float *pm = a.part_max + sh * P;
+    const float *pl = a.part_sum + sh * P;
+    const float4 *pa = reinterpret_cast<const float4 *>(a.part_acc + sh * P * D);
+    float4 *out = reinterpret_cast<float4 *>(a.out + sh * D);
+
+    int n = a.context_lens[s];
+    float4 x[U];
+    float mp[U], lp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int p = q + G * u;
+        const bool in = p < P;
+        x[u] = in ? pa[(int64_t)p * 16 + col] : make_float4(0.f, 0.f, 0.f, 0.f);
+        mp[u] = in ? pm[p] : -INFINITY;
+        lp[u] = in ? pl[p] : 0.f;
+    }
+    n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
+    const int np = (n + a.partition_size - 1) / a.partition_size;
+
+    __shared__ float red[4];
+    __shared__ float4 part4[4][C];
+
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (q + G * u < np)
+            m = fmaxf(m, mp[u]);
+    m = wave_max(m);
+    if (lane == 0)
+        red[wv] = m;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    if (M == -INFINITY) {                          // no partition / no usable token
+        if (tid < C)
+            out[col] = make_float4(0.f, 0.f, 0.f, 0.f);
+        return;
+    }
+
+    float den = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const bool live = q + G * u < np && mp[u] != -INFINITY;
+        const float w = live ? __builtin_amdgcn_exp2f(mp[u] - M) : 0.f;
+        if (live) {
+            den = fmaf(w, lp[u], den);
+            acc.x = fmaf(w, x[u].x, acc.x);
+            acc.y = fmaf(w, x[u].y, acc.y);
+            acc.z = fmaf(w, x[u].z, acc.z);
+            acc.w = fmaf(w, x[u].w, acc.w);
+        }
+    }
+    // Sum the wavefront's partition groups (lanes c, c + C, c + 2C, ...).
+#pragma unroll
+    for (int mk = C; mk <= 32; mk <<= 1) {
+        den += __shfl_xor(den, mk);
+        acc.x += __shfl_xor(acc.x, mk);
+        acc.y += __shfl_xor(acc.y, mk);
+        acc.z += __shfl_xor(acc.z, mk);
+        acc.w += __shfl_xor(acc.w, mk);
+    }
+    if (lane < C)
+        part4[wv][lane] = acc;
+    if (lane == 0)
+        red[wv] = den;                             // every column's groups hold the same sums
+    __syncthreads();
+    if (tid < C) {
+        const float DEN = (red[0] + red[1]) + (red[2] + red[3]);
+        float4 t = part4[0][tid];
+#pragma unroll
+        for (int w4 = 1; w4 < 4; ++w4) {
+            t.x += part4[w4][tid].x;
+            t.y += part4[w4][tid].y;
+            t.z += part4[w4][tid].z;
+            t.w += part4[w4][tid].w;
+        }
+        out[col] = make_float4(t.x / DEN, t.y / DEN, t.z / DEN, t.w / DEN);
+    }
 }
 
 __global__ __launch_bounds__(256) void paged_reduce_wide_kernel(ReduceArgs a)
@@ -205,7 +308,12 @@ hipError_t launch_paged_reduce(const ReduceArgs &a, hipStream_t stream)
 {
     if (a.num_parts > kMerge) {
         const int64_t groups = (int64_t)a.num_seqs * a.num_q_heads;
-        hipLaunchKernelGGL(paged_reduce_wide_kernel, dim3((unsigned)groups), dim3(256), 0, stream, a);
+        if (a.num_parts <= kMid && groups <= kMidRows)
+            hipLaunchKernelGGL(paged_reduce_mid_kernel<kMidSplit>,
+                               dim3((unsigned)groups, kMidSplit), dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL(paged_reduce_wide_kernel, dim3((unsigned)groups), dim3(256), 0,
+                               stream, a);
         return hipGetLastError();
     }
     const int64_t waves = (int64_t)a.num_seqs * a.num_q_heads;

@@ -378,7 +378,7 @@ tv_status tv_paged_attention_reduce(float *out, const float *part_acc, const flo
     const int64_t parts = ceil_div(max_context_len, partition_size);
     if (!out || !context_lens || (parts > 0 && (!part_acc || !part_max || !part_sum)))
         return TV_ERR_NULL;
-    if ((int64_t)num_seqs * num_q_heads > 0x7fffffff)
+    if ((int64_t)num_seqs * num_q_heads > 0xffffff)
         return TV_ERR_UNSUPPORTED;
     if (!aligned(out, 16) || !aligned(part_acc, 16) || !aligned(part_max, 4) ||
         !aligned(part_sum, 4) || !aligned(context_lens, 4))

@@ -272,6 +272,8 @@ def test_reduce_validation(lib):
     assert _red(lib, part=0) == TV_ERR_SHAPE
     assert _red(lib, mctx=-3) == TV_ERR_SHAPE
     assert _red(lib, d=32) == TV_ERR_UNSUPPORTED
+    assert _red(lib, S=1 << 19, hq=32) == TV_ERR_UNSUPPORTED          # 2^24 rows
+    assert _red(lib, S=(1 << 19) - 1, hq=32) == TV_ERR_ALIGNMENT     # just under the limit
     assert _red(lib, S=0) == TV_OK
     assert _red(lib, ptrs=(None,) + (BAD,) * 4) == TV_ERR_NULL
     assert _red(lib, ptrs=(BAD, None, BAD, BAD, BAD)) == TV_ERR_NULL

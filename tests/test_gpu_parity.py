@@ -92,6 +92,35 @@ def test_partition_invariance(dev, oracle_lib, partition_size):
     assert np.abs(got - base).max() <= 1e-5
 
 
+_MERGE_FORMS = [
+    # (sequences, partition size, workspace partitions): 32 query heads each
+    (8, 256, 9),      # 256 rows, 9 partitions: split form
+    (8, 32, 100),     # split form
+    (8, 16, 256),     # split form, its largest partition count
+    (9, 16, 256),     # 288 rows: wide form
+    (8, 16, 257),     # 257 partitions: wide form
+]
+
+
+@pytest.mark.parametrize("case", _MERGE_FORMS, ids=[f"s{c[0]}-p{c[2]}" for c in _MERGE_FORMS])
+def test_merge_forms(dev, oracle_lib, case):
+    """The merge past eight workspace partitions takes one of two forms --
+    each row split over four workgroups (at most 256 rows, at most 256
+    partitions) or one workgroup per row -- on both sides of each limit the
+    output meets the bars against the oracle, with contexts that end in
+    every partition position (the workspace's later partitions unused)."""
+    S, part, parts = case
+    mc = part * parts
+    rng = np.random.default_rng(97 + 7 * S + parts)
+    lens = rng.integers(1, mc + 1, size=S)
+    lens[1] = mc
+    lens[2] = 1
+    batch = W.make_batch(lens, 97 + parts, table_width=-(-mc // 16))
+    ref, _, _ = O.decode_step(oracle_lib, batch)
+    got, _ = _gpu_step(batch, dev, partition_size=part, max_context_len=mc)
+    _assert_close(got, ref, f"{S} sequences, {parts} partitions of {part}")
+
+
 def test_block_permutation_and_determinism(dev, oracle_lib):
     """Moving physical blocks leaves the GPU result bit-identical; so does re-running."""
     batch = W.make_batch([70, 513, 1111, 16], 32)
