@@ -101,8 +101,8 @@ int32_t tv_num_partitions(int32_t max_context_len, int32_t partition_size);
  * Two tokens naming the same slot is a caller error: which one lands is not
  * specified.  num_tokens == 0 is a no-op (pointers may then be NULL).
  * Errors: TV_ERR_NULL, TV_ERR_SHAPE (negative count, non-positive sizes),
- * TV_ERR_UNSUPPORTED (head_dim not a multiple of 8), TV_ERR_ALIGNMENT,
- * TV_ERR_HIP.
+ * TV_ERR_UNSUPPORTED (head_dim not a multiple of 8, or num_tokens above
+ * 4 * (2^24 - 1): the launch grid), TV_ERR_ALIGNMENT, TV_ERR_HIP.
  */
 tv_status tv_cache_write(const uint16_t *k, const uint16_t *v,
                          uint16_t *k_cache, uint16_t *v_cache,
@@ -134,7 +134,8 @@ tv_status tv_cache_write(const uint16_t *k, const uint16_t *v,
  * tv_rope: x [num_tokens][num_heads][head_dim] bf16 (16-byte aligned) turned
  * in place by R_{positions[i]} (q before attention, or a new token's K before
  * tv_paged_attention_decode_append).
- * Supported: head_dim a multiple of 8, at most 128.  Errors: TV_ERR_NULL,
+ * Supported: head_dim a multiple of 8, at most 128; num_tokens at most
+ * 4 * (2^24 - 1) (the launch grid).  Errors: TV_ERR_NULL,
  * TV_ERR_SHAPE (negative counts, non-positive sizes, a style other than 0/1),
  * TV_ERR_UNSUPPORTED, TV_ERR_ALIGNMENT, TV_ERR_HIP.  num_tokens == 0 is a no-op.
  */
@@ -367,7 +368,9 @@ tv_status tv_paged_attention_reduce(float *out, const float *part_acc,
  *   max_context_len  host-side upper bound of context_lens, <= max_blocks_per_seq * block_size
  *
  * Supported shapes: head_dim == 64, block_size == 16, num_q_heads /
- * num_kv_heads in {1, 2, 4, 8, 16}.  Arithmetic: bf16 products accumulated
+ * num_kv_heads in {1, 2, 4, 8, 16}; num_kv_heads * num_seqs *
+ * ceil(max_query_len / (256 / (num_q_heads / num_kv_heads))) < 2^23 (the
+ * launch grid).  Arithmetic: bf16 products accumulated
  * in fp32, softmax weights rounded to bf16 for the product with V.
  * Odd device data as for the decode call: context lengths are clamped to
  * [0, max_context_len], table entries outside [0, num_blocks) drop their
@@ -399,7 +402,8 @@ tv_status tv_paged_attention_prefill(float *out, const uint16_t *q, const int32_
  *   num_kv_heads * head_dim * block_size must be a multiple of 8
  *
  * The destinations must be distinct and no destination may also be a source
- * of the same call; otherwise the result is unspecified.  num_pairs == 0 is a
+ * of the same call; otherwise the result is unspecified.  num_pairs < 2^24
+ * (the launch grid); num_pairs == 0 is a
  * no-op.  Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED,
  * TV_ERR_ALIGNMENT, TV_ERR_HIP.
  */

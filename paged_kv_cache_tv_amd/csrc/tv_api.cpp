@@ -58,7 +58,7 @@ tv_status tv_cache_write(const uint16_t *k, const uint16_t *v, uint16_t *k_cache
         return TV_ERR_SHAPE;
     if ((int64_t)num_kv_heads * head_dim > (1 << 24))
         return TV_ERR_UNSUPPORTED;
-    if (ceil_div(num_tokens, 4) > 0x7fffffff)
+    if (ceil_div(num_tokens, 4) > 0xffffff)            // 256-thread workgroups of 4 tokens
         return TV_ERR_UNSUPPORTED;
     if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 2) ||
         !aligned(slot_mapping, 8))
@@ -88,7 +88,7 @@ tv_status tv_cache_write_rope(const uint16_t *k, const uint16_t *v, uint16_t *k_
         return TV_ERR_SHAPE;
     if ((int64_t)num_kv_heads * head_dim > (1 << 24))
         return TV_ERR_UNSUPPORTED;
-    if (ceil_div(num_tokens, 4) > 0x7fffffff)
+    if (ceil_div(num_tokens, 4) > 0xffffff)            // 256-thread workgroups of 4 tokens
         return TV_ERR_UNSUPPORTED;
     if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 2) ||
         !aligned(slot_mapping, 8) || !aligned(positions, 4) || !aligned(inv_freq, 4))
@@ -113,7 +113,7 @@ tv_status tv_rope(uint16_t *x, const int32_t *positions, const float *inv_freq,
         return TV_ERR_NULL;
     if (head_dim % 8 != 0 || head_dim > 128 || (int64_t)num_heads * head_dim > (1 << 24))
         return TV_ERR_UNSUPPORTED;
-    if (ceil_div(num_tokens, 4) > 0x7fffffff)
+    if (ceil_div(num_tokens, 4) > 0xffffff)            // 256-thread workgroups of 4 tokens
         return TV_ERR_UNSUPPORTED;
     if (!aligned(x, 16) || !aligned(positions, 4) || !aligned(inv_freq, 4))
         return TV_ERR_ALIGNMENT;
@@ -262,7 +262,7 @@ tv_status tv_paged_attention_prefill(float *out, const uint16_t *q, const int32_
     if (!out || !q || !query_start || !k_cache || !v_cache || !block_tables || !context_lens)
         return TV_ERR_NULL;
     const int64_t rows_per_wg = 256 / group;
-    if ((int64_t)num_kv_heads * num_seqs * ceil_div(max_query_len, rows_per_wg) > 0x7fffffff)
+    if ((int64_t)num_kv_heads * num_seqs * ceil_div(max_query_len, rows_per_wg) > 0x7fffff)
         return TV_ERR_UNSUPPORTED;
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(query_start, 4) ||
         !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_tables, 4) ||
@@ -404,7 +404,7 @@ tv_status tv_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int64_t *bl
         return TV_OK;
     if (!k_cache || !v_cache || !block_pairs)
         return TV_ERR_NULL;
-    if (2 * num_pairs > 0x7fffffff)
+    if (2 * num_pairs > 0x1ffffff)                   // 128-thread workgroups
         return TV_ERR_UNSUPPORTED;
     if (num_blocks > INT64_MAX / block_elems)
         return TV_ERR_SHAPE;

@@ -72,6 +72,8 @@ def test_cache_write_validation(lib):
     assert _cw(lib, ptrs=(None, BAD, BAD, BAD, BAD)) == TV_ERR_NULL
     assert _cw(lib, ptrs=(BAD, BAD, BAD, BAD, None)) == TV_ERR_NULL
     assert _cw(lib, d=60) == TV_ERR_UNSUPPORTED
+    assert _cw(lib, T=4 * 0xffffff + 1) == TV_ERR_UNSUPPORTED    # launch grid
+    assert _cw(lib, T=4 * 0xffffff) == TV_ERR_ALIGNMENT
     assert _cw(lib) == TV_ERR_ALIGNMENT
 
 
@@ -199,6 +201,8 @@ def test_prefill_validation(lib):
     assert _pre(lib, bs=32, mb=2) == TV_ERR_UNSUPPORTED
     assert _pre(lib, hq=24) == TV_ERR_UNSUPPORTED          # group 3
     assert _pre(lib, hq=256) == TV_ERR_UNSUPPORTED         # group 32
+    assert _pre(lib, S=1 << 20, mq=64) == TV_ERR_UNSUPPORTED   # 2^23 workgroups
+    assert _pre(lib, S=(1 << 20) - 1, mq=64) == TV_ERR_ALIGNMENT
     assert _pre(lib, S=0) == TV_OK
     assert _pre(lib, mq=0) == TV_OK
     assert _pre(lib) == TV_ERR_ALIGNMENT
@@ -240,6 +244,8 @@ def test_rope_validation(lib):
     assert _rope(lib, style=-1) == TV_ERR_SHAPE
     assert _rope(lib, T=0) == TV_OK
     assert _rope(lib, d=20) == TV_ERR_UNSUPPORTED
+    assert _rope(lib, T=4 * 0xffffff + 1) == TV_ERR_UNSUPPORTED
+    assert _rope(lib, T=4 * 0xffffff) == TV_ERR_ALIGNMENT
     assert _rope(lib) == TV_ERR_ALIGNMENT
     for i in range(3):
         ptrs = [ALIGNED] * 3
@@ -258,6 +264,8 @@ def test_copy_blocks_validation(lib):
     assert _copy(lib, hkv=0) == TV_ERR_SHAPE
     assert _copy(lib, nb=0) == TV_ERR_SHAPE
     assert _copy(lib, hkv=1, d=3, bs=1) == TV_ERR_UNSUPPORTED    # 3 values per block
+    assert _copy(lib, n=1 << 24) == TV_ERR_UNSUPPORTED           # launch grid
+    assert _copy(lib, n=(1 << 24) - 1) == TV_ERR_ALIGNMENT
     assert _copy(lib, n=0, ptrs=(None,) * 3) == TV_OK           # no-op
     assert _copy(lib, ptrs=(BAD, BAD, None)) == TV_ERR_NULL
     assert _copy(lib) == TV_ERR_ALIGNMENT
