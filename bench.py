@@ -490,6 +490,19 @@ def main(argv=None):
         roof_kernel, roof_bytes, roof_ms = "paged_decode_kernel", dec_bytes, decode_ms
     roof_gbs = roof_bytes / (roof_ms * 1e-3) / 1e9
 
+    # The plain-read yardstick: tv_stream_read over as many bytes as the
+    # kernel above moves per launch, timed the same way (eviction + kernel
+    # loop minus the eviction loop).
+    sr_bytes = -(-roof_bytes // 16) * 16
+    sr_buf = torch.zeros(sr_bytes // 4, dtype=torch.int32, device=dev)
+    sr_out = torch.empty(-(-sr_bytes // tv.STREAM_CHUNK_BYTES), dtype=torch.int32, device=dev)
+    for i in range(max(1, args.warmup)):
+        flush(i)
+        tv.stream_read(sr_buf, sr_out, stream)
+    sr_ms = timed_loop(lambda i: (flush(i), tv.stream_read(sr_buf, sr_out, stream)), K) - t_flush
+    sr_gbs = sr_bytes / (sr_ms * 1e-3) / 1e9
+    del sr_buf, sr_out
+
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -537,7 +550,13 @@ def main(argv=None):
                      "frac": round(roof_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(batch.name, roof_kernel),
                      "algorithmic_bytes_per_launch": roof_bytes,
-                     "avg_launch_us": round(roof_ms * 1e3, 2)},
+                     "avg_launch_us": round(roof_ms * 1e3, 2),
+                     "frac_of_stream_read": round(roof_gbs / sr_gbs, 4)},
+        "stream_read": {"kernel": "stream_read_kernel", "bytes_per_launch": sr_bytes,
+                        "us_per_launch": round(sr_ms * 1e3, 2), "GB_per_s": round(sr_gbs, 2),
+                        "frac_of_hbm_peak": round(sr_gbs / HBM_PEAK_GBS, 4),
+                        "what": "one plain coalesced read of the same byte count as the "
+                                "roofline kernel, cold cache, same timing method"},
     }
 
     if not args.no_block_copy:

@@ -500,6 +500,24 @@ tv_status tv_bm_block_table(const tv_block_manager *bm, int32_t seq, int32_t *ro
 tv_status tv_bm_slots(const tv_block_manager *bm, int32_t seq, int32_t start, int32_t count,
                       int64_t *slots);
 
+/* ------------------------------------------------------------------------
+ * Streaming-read yardstick.  The decode path is bound by HBM reads (the K/V
+ * of every context token once per step), and its bytes per second are
+ * reported as a fraction of the 8 TB/s specification and, for context, of
+ * what a plain read of the same size achieves on the device.  This call is
+ * that plain read: buf[0 .. bytes) read once, coalesced, non-temporal.
+ *
+ *   buf        device memory, 16-byte aligned; bytes a multiple of 16
+ *   chunk_xor  uint32 [ceil(bytes / 8192)] (device), 4-byte aligned:
+ *              entry c = XOR of the 32-bit words of bytes
+ *              [8192 c, min(8192 (c + 1), bytes)), little-endian
+ *
+ * bytes == 0 is a no-op.  Errors: TV_ERR_SHAPE (bytes < 0), TV_ERR_NULL,
+ * TV_ERR_UNSUPPORTED (bytes not a multiple of 16, or 2^24 chunks or more:
+ * the launch grid), TV_ERR_ALIGNMENT, TV_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+tv_status tv_stream_read(const void *buf, int64_t bytes, uint32_t *chunk_xor, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -72,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_rope.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp]
     lib.tv_copy_blocks.restype = ctypes.c_int
     lib.tv_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, vp]
+    lib.tv_stream_read.restype = ctypes.c_int
+    lib.tv_stream_read.argtypes = [vp, i64, vp, vp]
     i32p, i64p = ctypes.POINTER(i32), ctypes.POINTER(i64)
     lib.tv_bm_create.restype = ctypes.c_int
     lib.tv_bm_create.argtypes = [i32, i32, i32, i32, ctypes.POINTER(vp)]
@@ -474,6 +476,26 @@ def copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:
                               block_pairs.shape[0], hkv, d, bs, nb,
                               _stream_handle(stream, k_cache.device))
     _check("tv_copy_blocks", st)
+
+
+STREAM_CHUNK_BYTES = 8192
+
+
+def stream_read(buf, chunk_xor, stream=None) -> None:
+    """tv_stream_read: read every byte of the contiguous device tensor `buf`
+    (its size a multiple of 16 bytes) once; chunk_xor (int32, one entry per
+    8 KiB chunk, the last possibly partial) receives each chunk's XOR of
+    32-bit words.  The plain-read yardstick for HBM-bound kernels."""
+    import torch
+    _need(buf, "buf")
+    _need(chunk_xor, "chunk_xor", dtype=torch.int32, ndim=1)
+    nbytes = buf.numel() * buf.element_size()
+    chunks = -(-nbytes // STREAM_CHUNK_BYTES)
+    if chunk_xor.numel() < chunks:
+        raise ValueError(f"chunk_xor needs {chunks} entries, has {chunk_xor.numel()}")
+    st = lib().tv_stream_read(buf.data_ptr(), nbytes, chunk_xor.data_ptr(),
+                              _stream_handle(stream, buf.device))
+    _check("tv_stream_read", st)
 
 
 class BlockManager:

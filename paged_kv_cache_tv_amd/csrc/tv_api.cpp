@@ -413,3 +413,21 @@ tv_status tv_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int64_t *bl
     tv::BlockCopyArgs a{k_cache, v_cache, block_pairs, num_pairs, num_blocks, block_elems};
     return from_hip(tv::launch_block_copy(a, static_cast<hipStream_t>(stream)));
 }
+
+tv_status tv_stream_read(const void *buf, int64_t bytes, uint32_t *chunk_xor, void *stream)
+{
+    if (bytes < 0)
+        return TV_ERR_SHAPE;
+    if (bytes % 16 != 0)
+        return TV_ERR_UNSUPPORTED;
+    if (bytes == 0)
+        return TV_OK;
+    if (!buf || !chunk_xor)
+        return TV_ERR_NULL;
+    if (ceil_div(bytes, tv::kStreamChunkBytes) > 0xffffff)   // 256-thread workgroups
+        return TV_ERR_UNSUPPORTED;
+    if (!aligned(buf, 16) || !aligned(chunk_xor, 4))
+        return TV_ERR_ALIGNMENT;
+    tv::StreamReadArgs a{buf, bytes / 16, chunk_xor};
+    return from_hip(tv::launch_stream_read(a, static_cast<hipStream_t>(stream)));
+}

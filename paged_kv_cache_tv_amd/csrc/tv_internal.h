@@ -116,11 +116,20 @@ struct BlockCopyArgs {
     int64_t block_elems;        // num_kv_heads * block_size * head_dim (a multiple of 8)
 };
 
+constexpr int64_t kStreamChunkBytes = 8192;    // bytes folded into one XOR by tv_stream_read
+
+struct StreamReadArgs {
+    const void *buf;            // 16-byte aligned
+    int64_t pieces;             // bytes / 16
+    uint32_t *chunk_xor;        // [ceil(bytes / kStreamChunkBytes)]
+};
+
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream);
 hipError_t launch_rope(const RopeArgs &a, hipStream_t stream);
 hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t stream);
 hipError_t launch_paged_prefill(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_paged_reduce(const ReduceArgs &a, hipStream_t stream);
+hipError_t launch_stream_read(const StreamReadArgs &a, hipStream_t stream);
 
 }  // namespace tv

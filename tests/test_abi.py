@@ -288,6 +288,19 @@ def test_reduce_validation(lib):
     assert _red(lib) == TV_ERR_ALIGNMENT
 
 
+def test_stream_read_validation(lib):
+    f = lib.tv_stream_read
+    assert f(BAD, -16, BAD, None) == TV_ERR_SHAPE
+    assert f(BAD, 24, BAD, None) == TV_ERR_UNSUPPORTED               # not a multiple of 16
+    assert f(None, 0, None, None) == TV_OK                            # no-op
+    assert f(None, 16, BAD, None) == TV_ERR_NULL
+    assert f(BAD, 16, None, None) == TV_ERR_NULL
+    assert f(BAD, 8192 * 0xffffff + 16, BAD, None) == TV_ERR_UNSUPPORTED   # 2^24 chunks
+    assert f(BAD, 8192 * 0xffffff, BAD, None) == TV_ERR_ALIGNMENT
+    assert f(ALIGNED, 16, ALIGNED + 2, None) == TV_ERR_ALIGNMENT
+    assert f(ALIGNED + 8, 16, ALIGNED, None) == TV_ERR_ALIGNMENT
+
+
 def test_binding_refuses_host_tensors():
     import torch
     import paged_kv_cache_tv_amd as tv
