@@ -443,6 +443,7 @@ def main(argv=None):
     t_flush_decode = timed_loop(lambda i: (flush(i), db.decode(stream)), K)
     t_flush_append = timed_loop(lambda i: (flush(i), db.decode_append(stream)), K)
     t_flush_reduce = timed_loop(lambda i: (flush(i), db.reduce(stream)), K)
+    t_flush_call = timed_loop(lambda i: (flush(i), db.call_step(stream)), K)
     if args.no_flush:
         t_flush = 0.0
     step_ms_cold = t_flush_step - t_flush
@@ -451,6 +452,7 @@ def main(argv=None):
     append_ms = t_flush_append - t_flush
     write_ms = t_flush_write - t_flush
     reduce_ms = t_flush_reduce - t_flush
+    call_ms = t_flush_call - t_flush
 
     # Hot cache: the same steps back to back with no eviction in between.
     hot_steps = max(10, K)
@@ -534,6 +536,10 @@ def main(argv=None):
         "step": "two launches: decode_append + reduce" if fused else
                 "three launches: cache_write + decode + reduce",
         "other_step_us": round(other_ms * 1e3, 2),
+        "one_call_step_us": round(call_ms * 1e3, 2),
+        "one_call_step": ("one launch (the pass divides by the sum itself)"
+                          if db.max_context_len <= db.partition_size
+                          else "two launches inside tv_paged_attention_decode_step"),
         "kernels_us": {"cache_write": round(write_ms * 1e3, 2),
                        "paged_decode": round(decode_ms * 1e3, 2),
                        "paged_decode_append": round(append_ms * 1e3, 2),

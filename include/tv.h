@@ -344,6 +344,43 @@ tv_status tv_paged_attention_reduce(float *out, const float *part_acc,
                                     void *stream);
 
 /*
+ * A whole decode step in one call: the new tokens' cache write, the partition
+ * pass and the log-sum-exp merge ("vLLM" page, Flash Attention: the running
+ * maximum / running sum rule; a single partition merges to acc / l).
+ *
+ * When ceil(max_context_len / partition_size) == 1 the partition pass divides
+ * by the sum itself and writes out: one launch, and part_acc, part_max and
+ * part_sum are not used (they may be NULL).  Otherwise it is
+ * tv_paged_attention_decode_append followed by tv_paged_attention_reduce on
+ * the same stream: two launches through the workspace.  Either way out is
+ * bitwise what those two calls give.  With max_context_len == 0 every row of
+ * out is set to zero.
+ *
+ *   out        float [num_seqs][num_q_heads][head_dim], 16-byte aligned
+ *   part_*     the workspace as for tv_paged_attention_decode (part_acc
+ *              16-byte aligned), sized for ceil(max_context_len /
+ *              partition_size) partitions; unused with one partition
+ *   other arguments, the append precondition and the odd-data behaviour as
+ *   for tv_paged_attention_decode_append
+ *
+ * Supported shapes: those of tv_paged_attention_decode_append, and
+ * num_seqs * num_q_heads < 2^24.  Errors: TV_ERR_NULL, TV_ERR_SHAPE,
+ * TV_ERR_UNSUPPORTED, TV_ERR_ALIGNMENT, TV_ERR_HIP; all argument errors are
+ * found before anything is launched.  num_seqs == 0 is a no-op.
+ */
+tv_status tv_paged_attention_decode_step(float *out, float *part_acc, float *part_max,
+                                         float *part_sum, const uint16_t *q,
+                                         const uint16_t *k_new, const uint16_t *v_new,
+                                         const int64_t *slot_mapping, uint16_t *k_cache,
+                                         uint16_t *v_cache, const int32_t *block_tables,
+                                         const int32_t *context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size,
+                                         int32_t max_blocks_per_seq, int64_t num_blocks,
+                                         int32_t max_context_len, int32_t partition_size,
+                                         float scale, void *stream);
+
+/*
  * Prefill and chunked prefill ("tiny-vLLM으로 처음부터 고성능 LLM 추론 엔진
  * 구축하기" page, section "고급 추론 개념": prefill runs the whole prompt,
  * decode only the newest token; "tiny-vllm 씹뜯맛즐 - (1)" page, section 1:

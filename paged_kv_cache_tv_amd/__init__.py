@@ -11,7 +11,7 @@ from .binding import (LIB_PATH, STREAM_CHUNK_BYTES, BlockManager, TvError, cache
                       load_library, new_pools,
                       new_workspace, num_partitions, paged_attention, paged_attention_decode,
                       paged_attention_decode_append, paged_attention_decode_shared,
-                      paged_attention_decode_shared_append,
+                      paged_attention_decode_shared_append, paged_attention_decode_step,
                       paged_attention_prefill,
                       paged_attention_reduce, stream_read)
 
@@ -20,5 +20,5 @@ __all__ = ["LIB_PATH", "STREAM_CHUNK_BYTES", "BlockManager", "TvError", "cache_w
            "load_library", "new_pools",
            "new_workspace", "num_partitions", "paged_attention", "paged_attention_decode",
            "paged_attention_decode_append", "paged_attention_decode_shared",
-           "paged_attention_decode_shared_append",
+           "paged_attention_decode_shared_append", "paged_attention_decode_step",
            "paged_attention_prefill", "paged_attention_reduce", "stream_read"]

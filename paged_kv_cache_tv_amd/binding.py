@@ -51,6 +51,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_paged_attention_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                      i32, i32, i32, i32, i32, i32, i64, i32, i32,
                                                      f32, vp]
+    lib.tv_paged_attention_decode_step.restype = ctypes.c_int
+    lib.tv_paged_attention_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                   vp, i32, i32, i32, i32, i32, i32, i64, i32,
+                                                   i32, f32, vp]
     lib.tv_paged_attention_decode_shared.restype = ctypes.c_int
     lib.tv_paged_attention_decode_shared.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                                      i32, i32, i32, i32, i32, i32, i64, i32, i32,
@@ -370,6 +374,51 @@ def paged_attention_decode_append(part_acc, part_max, part_sum, q, k_new, v_new,
         block_tables.shape[1], nb, int(max_context_len), int(partition_size), float(scale),
         _stream_handle(stream, q.device))
     _check("tv_paged_attention_decode_append", st)
+
+
+def paged_attention_decode_step(out, workspace, q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                block_tables, context_lens, max_context_len: int,
+                                partition_size: int, scale: float, stream=None) -> None:
+    """tv_paged_attention_decode_step: cache write, partition pass and merge in
+    one call -- one launch when max_context_len fits one partition (workspace
+    unused, may be None), else the append pass and the merge through
+    `workspace` = (part_acc, part_max, part_sum).  out: float32 [S, Hq, D]."""
+    import torch
+    _need(out, "out", dtype=torch.float32, ndim=3)
+    _need(q, "q", itemsize=2, ndim=3)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, itemsize=2, ndim=3)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1)
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    S, hq, d = q.shape
+    nb, hkv, bs, d2 = _pool_dims(k_cache, v_cache)
+    if d2 != d or tuple(out.shape) != (S, hq, d):
+        raise ValueError("out must be [S, Hq, D] and the caches must match q")
+    if tuple(k_new.shape) != (S, hkv, d) or tuple(v_new.shape) != (S, hkv, d) or \
+            slot_mapping.shape[0] != S:
+        raise ValueError("k_new, v_new must be [S, Hkv, D] and slot_mapping [S]")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    P = num_partitions(max_context_len, partition_size)
+    if P > 1:
+        if workspace is None:
+            raise ValueError(f"{P} partitions need the workspace")
+        part_acc, part_max, part_sum = workspace
+        for t, n in ((part_acc, "part_acc"), (part_max, "part_max"), (part_sum, "part_sum")):
+            _need(t, n, dtype=torch.float32)
+        if tuple(part_acc.shape) != (S, hq, P, d) or tuple(part_max.shape) != (S, hq, P) or \
+                tuple(part_sum.shape) != (S, hq, P):
+            raise ValueError(f"workspace must be [S, Hq, P(={P}), D] and [S, Hq, P]")
+        ptrs = (part_acc.data_ptr(), part_max.data_ptr(), part_sum.data_ptr())
+    else:
+        ptrs = (None, None, None)
+    st = lib().tv_paged_attention_decode_step(
+        out.data_ptr(), *ptrs, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+        slot_mapping.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), S, hq, hkv, d, bs, block_tables.shape[1], nb,
+        int(max_context_len), int(partition_size), float(scale), _stream_handle(stream, q.device))
+    _check("tv_paged_attention_decode_step", st)
 
 
 def paged_attention_decode_shared_append(part_acc, part_max, part_sum, q, k_new, v_new,

@@ -371,8 +371,18 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
         n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
     }
     const int first_tok = part * a.part_tiles * BS;
-    if (first_tok >= n)
+    if (first_tok >= n) {
+        if (a.normalize && threadIdx.x < 64) {
+            // An empty context with the only partition: its rows of the
+            // output are 0 (the merge of no partition).  The plain order is
+            // used here, so the unit knows its sequence.
+            float4 *o0 = reinterpret_cast<float4 *>(
+                a.part_acc + ((int64_t)s * a.num_kv_heads * a.group + (int64_t)kvh * a.group) * D);
+            for (int e = lane; e < a.group * (D / 4); e += 64)
+                o0[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
         return;
+    }
     const int ptok = min(n - first_tok, a.part_tiles * BS);    // tokens in this partition
     const int ntiles = (ptok + BS - 1) / BS;
 
@@ -585,14 +595,26 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
     if (col_ok) {
         const int hq = a.num_kv_heads * G;
         const int64_t row = ((int64_t)col_seq * hq + (int64_t)kvh * G + r % G) * a.num_parts + part;
-        if (g == 0) {
-            a.part_max[row] = m_run;
-            a.part_sum[row] = l_run;
-        }
         float *acc = a.part_acc + row * D + 4 * g;
+        if (a.normalize) {
+            // The only partition: merging it is dividing by its sum.
+            const bool none = m_run == -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<float4 *>(acc + 16 * j) = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<float4 *>(acc + 16 * j) =
+                    none ? make_float4(0.f, 0.f, 0.f, 0.f)
+                         : make_float4(o[j][0] / l_run, o[j][1] / l_run, o[j][2] / l_run,
+                                       o[j][3] / l_run);
+        } else {
+            if (g == 0) {
+                a.part_max[row] = m_run;
+                a.part_sum[row] = l_run;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<float4 *>(acc + 16 * j) =
+                    make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
+        }
     }
 }
 
@@ -708,9 +730,12 @@ hipError_t launch_paged_decode(const DecodeArgs &args, hipStream_t stream)
         return hipGetLastError();
     }
     // Balanced order: consecutive workgroups of one head cycle over
-    // cus / gcd(heads, cus) compute units (32 on one XCD for 8 heads).
+    // cus / gcd(heads, cus) compute units (32 on one XCD for 8 heads).  Not
+    // with a single, self-normalised partition: there an empty context's
+    // unit must know its sequence to write its zero rows.
     a.plan_width = 0;
-    if (groups > resident && !a.shared_len && a.num_seqs <= 64 * kPlanChunks && dev.cus > 0)
+    if (groups > resident && !a.shared_len && !a.normalize && a.num_seqs <= 64 * kPlanChunks &&
+        dev.cus > 0)
         a.plan_width = dev.cus / std::gcd(a.num_kv_heads, dev.cus);
     if (split && a.plan_width > 0) {
         if (a.k_new)

@@ -363,6 +363,62 @@ tv_status tv_paged_attention_decode_shared_append(
     return from_hip(tv::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+tv_status tv_paged_attention_decode_step(float *out, float *part_acc, float *part_max,
+                                         float *part_sum, const uint16_t *q,
+                                         const uint16_t *k_new, const uint16_t *v_new,
+                                         const int64_t *slot_mapping, uint16_t *k_cache,
+                                         uint16_t *v_cache, const int32_t *block_tables,
+                                         const int32_t *context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size,
+                                         int32_t max_blocks_per_seq, int64_t num_blocks,
+                                         int32_t max_context_len, int32_t partition_size,
+                                         float scale, void *stream)
+{
+    // One partition per (sequence, head): the merge is acc / l, written by the
+    // partition pass itself into out (the workspace is not used).
+    const bool one = partition_size > 0 && max_context_len > 0 && max_context_len <= partition_size;
+    tv::DecodeArgs a;
+    const tv_status st = check_decode(a, one ? out : part_acc, one ? out : part_max,
+                                      one ? out : part_sum, q, k_cache, v_cache, block_tables,
+                                      context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                      block_size, max_blocks_per_seq, num_blocks,
+                                      max_context_len, partition_size, scale);
+    if (st != TV_OK || num_seqs == 0)
+        return st;
+    if (a.num_parts == 0)                         // max_context_len == 0: out rows are 0
+        return tv_paged_attention_reduce(out, part_acc, part_max, part_sum, context_lens,
+                                         num_seqs, num_q_heads, head_dim, max_context_len,
+                                         partition_size, stream);
+    if (!out || !k_new || !v_new || !slot_mapping)
+        return TV_ERR_NULL;
+    if ((int64_t)num_seqs * num_q_heads > 0xffffff)
+        return TV_ERR_UNSUPPORTED;
+    if (!aligned(out, 16) || (!one && !aligned(part_acc, 16)) || !aligned(k_new, 16) ||
+        !aligned(v_new, 2) || !aligned(slot_mapping, 8))
+        return TV_ERR_ALIGNMENT;
+    if (num_blocks > INT64_MAX / block_size)
+        return TV_ERR_SHAPE;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.slot_mapping = slot_mapping;
+    a.k_cache_w = k_cache;
+    a.v_cache_w = v_cache;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (one) {
+        a.part_max = nullptr;
+        a.part_sum = nullptr;
+        a.normalize = 1;
+        return from_hip(tv::launch_paged_decode(a, hs));
+    }
+    const tv_status sd = from_hip(tv::launch_paged_decode(a, hs));
+    if (sd != TV_OK)
+        return sd;
+    tv::ReduceArgs r{out, part_acc, part_max, part_sum, context_lens, num_seqs, num_q_heads,
+                     a.num_parts, partition_size, max_context_len};
+    return from_hip(tv::launch_paged_reduce(r, hs));
+}
+
 tv_status tv_paged_attention_reduce(float *out, const float *part_acc, const float *part_max,
                                     const float *part_sum, const int32_t *context_lens,
                                     int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,

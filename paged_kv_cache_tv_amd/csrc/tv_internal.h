@@ -74,6 +74,11 @@ struct DecodeArgs {
     // how many compute units consecutive workgroups of one K/V head are dealt
     // over; 0 keeps the plain (partition, sequence, head) order.
     int32_t plan_width;
+    // 1: a single partition per (sequence, head) (num_parts == 1, no shared
+    // prefix), whose log-sum-exp merge is just acc / l: the pass writes that
+    // (0 where nothing was attended) into part_acc, which is then the output
+    // [num_seqs][num_q_heads][head_dim], and writes no max or sum.
+    int32_t normalize;
 };
 
 struct ReduceArgs {

@@ -97,6 +97,16 @@ class DeviceBatch:
         self.reduce(stream)
         return self.out
 
+    def call_step(self, stream=None):
+        """The same step through one library call (tv_paged_attention_decode_step):
+        one launch when the host bound fits one partition, else two."""
+        tv.paged_attention_decode_step(self.out, self.workspace, self.q, self.step_k, self.step_v,
+                                       self.step_slots, self.k_cache, self.v_cache,
+                                       self.block_tables, self.context_lens,
+                                       self.max_context_len, self.partition_size,
+                                       self.batch.scale, stream)
+        return self.out
+
     def pools_numpy(self):
         return (self.k_cache.cpu().numpy().view(np.uint16),
                 self.v_cache.cpu().numpy().view(np.uint16))

@@ -137,6 +137,46 @@ def test_decode_append_validation(lib):
     assert _app(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
 
 
+def _stp(lib, S=2, hq=32, hkv=8, d=64, mctx=64, part=32, ptrs=(BAD,) * 12):
+    return lib.tv_paged_attention_decode_step(*ptrs, S, hq, hkv, d, 16, 4, 8, mctx, part,
+                                              0.125, None)
+
+
+def test_decode_step_validation(lib):
+    """tv_paged_attention_decode_step: every argument error is found before a
+    launch; the workspace is needed only with more than one partition.  Each
+    case below keeps at least one argument that fails, so nothing launches."""
+    assert _stp(lib, S=-1) == TV_ERR_SHAPE
+    assert _stp(lib, part=24) == TV_ERR_SHAPE
+    assert _stp(lib, d=128) == TV_ERR_UNSUPPORTED
+    assert _stp(lib, S=0) == TV_OK
+    assert _stp(lib) == TV_ERR_ALIGNMENT
+    # max_context_len == 0: the merge alone zeroes out; out is still checked.
+    assert _stp(lib, mctx=0) == TV_ERR_ALIGNMENT
+    assert _stp(lib, mctx=0, ptrs=(None,) + (BAD,) * 11) == TV_ERR_NULL
+    # One partition (64 <= 64): no workspace needed.
+    one = [ALIGNED] * 12
+    one[1:4] = [None] * 3
+    one[0] = BAD                                          # out misaligned
+    assert _stp(lib, part=64, ptrs=tuple(one)) == TV_ERR_ALIGNMENT
+    one[0] = ALIGNED
+    one[5] = None                                         # k_new
+    assert _stp(lib, part=64, ptrs=tuple(one)) == TV_ERR_NULL
+    one[5] = ALIGNED
+    one[7] = 0x1004                                       # slot_mapping not 8-byte aligned
+    assert _stp(lib, part=64, ptrs=tuple(one)) == TV_ERR_ALIGNMENT
+    assert _stp(lib, part=64, S=1 << 19, ptrs=tuple(one)) == TV_ERR_UNSUPPORTED   # 2^24 rows
+    # Two partitions: the workspace is required, part_acc 16-byte aligned.
+    two = [ALIGNED] * 12
+    two[1] = None
+    assert _stp(lib, ptrs=tuple(two)) == TV_ERR_NULL
+    two[1] = 0x1004
+    assert _stp(lib, ptrs=tuple(two)) == TV_ERR_ALIGNMENT
+    two[1] = ALIGNED
+    two[0] = None                                         # out
+    assert _stp(lib, ptrs=tuple(two)) == TV_ERR_NULL
+
+
 def _shd(lib, S=2, hq=32, hkv=8, gs=4, mctx=64, part=32, ptrs=(BAD,) * 10):
     return lib.tv_paged_attention_decode_shared(*ptrs, gs, S, hq, hkv, 64, 16, 4, 8, mctx, part,
                                                 0.125, None)

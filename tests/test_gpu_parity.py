@@ -92,6 +92,71 @@ def test_partition_invariance(dev, oracle_lib, partition_size):
     assert np.abs(got - base).max() <= 1e-5
 
 
+# ---------------------------------------------------------------------------
+# tv_paged_attention_decode_step: the whole step in one call.  With one
+# partition the pass divides by the sum itself (one launch); the output must
+# equal the two-launch step bit for bit either way.
+# ---------------------------------------------------------------------------
+
+def _call_step(db):
+    import torch
+    db.out.fill_(float("nan"))                    # every row must be written by the call
+    got = db.call_step().clone()
+    torch.cuda.synchronize()
+    return got.cpu().numpy()
+
+
+@pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
+def test_decode_step_call_workloads(dev, oracle_lib, index):
+    """Full workloads through tv_paged_attention_decode_step (workload 1's 37
+    tokens fit one partition: a single launch): output bitwise the two-launch
+    step's, pools bit-exact against the oracle's cache write."""
+    batch = W.make_workload(index)
+    ref, kc_ref, vc_ref = _oracle_step(oracle_lib, ("workload", index), batch)
+    two, db = _gpu_step(batch, dev, fused=True)
+    got = _call_step(db)
+    assert np.array_equal(got, two), f"workload {index}: one call differs from two launches"
+    kc, vc = db.pools_numpy()
+    assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+    _assert_close(got, ref, f"workload {index}, one call")
+
+
+_ONE_PARTITION = [
+    # (seed, sequences, longest context, partition, host bound, query heads, K/V heads)
+    (70, 1, 37, 512, 37, 32, 8),
+    (71, 7, 512, 512, 512, 32, 8),      # contexts up to the whole partition
+    (72, 64, 300, 512, 512, 32, 8),     # host bound above every context
+    (73, 300, 64, 64, 64, 32, 8),       # small partitions, a large grid
+    (74, 40, 500, 512, 500, 16, 2),     # 8 query heads per K/V head
+    (75, 33, 200, 256, 256, 8, 8),      # 1 query head per K/V head
+]
+
+
+@pytest.mark.parametrize("case", _ONE_PARTITION, ids=[f"seed{c[0]}" for c in _ONE_PARTITION])
+def test_decode_step_one_partition(dev, oracle_lib, case):
+    """Host bounds that fit one partition, so the call is one launch whose
+    pass writes acc / l: output within the bars against the oracle and bitwise
+    the two-launch step's, including empty contexts (zero rows), one-token
+    contexts and every launch form (4 wavefronts or 1 per partition)."""
+    seed, S, maxlen, part, mc, hq, hkv = case
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, maxlen + 1, size=S)
+    lens[0] = maxlen
+    if S > 2:
+        lens[1], lens[2] = 0, 1
+    batch = W.make_batch(lens, seed, num_q_heads=hq, num_kv_heads=hkv, table_width=-(-mc // 16))
+    ref, kc_ref, vc_ref = O.decode_step(oracle_lib, batch)
+    two, db = _gpu_step(batch, dev, partition_size=part, max_context_len=mc, fused=True)
+    got = _call_step(db)
+    assert np.array_equal(got, two), f"seed {seed}: one launch differs from two"
+    kc, vc = db.pools_numpy()
+    assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+    _assert_close(got, ref, f"seed {seed}: {S} x <= {maxlen} tokens, host bound {mc}, "
+                            f"partition {part}, {hq}/{hkv} heads")
+    if S > 2:
+        assert not got[1].any(), "an empty context must give a zero row"
+
+
 _MERGE_FORMS = [
     # (sequences, partition size, workspace partitions): 32 query heads each
     (8, 256, 9),      # 256 rows, 9 partitions: split form
