@@ -129,6 +129,7 @@ _ONE_PARTITION = [
     (73, 300, 64, 64, 64, 32, 8),       # small partitions, a large grid
     (74, 40, 500, 512, 500, 16, 2),     # 8 query heads per K/V head
     (75, 33, 200, 256, 256, 8, 8),      # 1 query head per K/V head
+    (76, 20, 400, 512, 400, 32, 2),     # 16 query heads per K/V head (the largest group)
 ]
 
 
@@ -137,7 +138,8 @@ def test_decode_step_one_partition(dev, oracle_lib, case):
     """Host bounds that fit one partition, so the call is one launch whose
     pass writes acc / l: output within the bars against the oracle and bitwise
     the two-launch step's, including empty contexts (zero rows), one-token
-    contexts and every launch form (4 wavefronts or 1 per partition)."""
+    contexts, 1 to 16 query heads per K/V head and both launch forms (4
+    wavefronts or 1 per partition)."""
     seed, S, maxlen, part, mc, hq, hkv = case
     rng = np.random.default_rng(seed)
     lens = rng.integers(0, maxlen + 1, size=S)
