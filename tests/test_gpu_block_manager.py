@@ -46,19 +46,23 @@ def _to_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def test_copy_blocks_parity(dev, oracle_lib):
+@pytest.mark.parametrize("count", [100, 700])
+def test_copy_blocks_parity(dev, oracle_lib, count):
+    """Whole pools bit-exact after the copy, in both launch shapes (up to 512
+    pairs: 256-thread workgroups; more: 128-thread ones), with skipped pairs
+    (source = destination, out of range)."""
     import torch
     import paged_kv_cache_tv_amd as tv
-    rng = np.random.default_rng(50)
-    NB = 300
+    rng = np.random.default_rng(50 + count)
+    NB = 3 * count
     kc_ref = _bf16(rng, (NB, HKV, D // 8, BS, 8))
     vc_ref = _bf16(rng, (NB, HKV, D, BS))
-    src = rng.choice(150, size=100, replace=False)
-    dst = 150 + rng.choice(150, size=100, replace=False)
+    src = rng.choice(NB // 2, size=count, replace=False)
+    dst = NB // 2 + rng.choice(NB // 2, size=count, replace=False)
     pairs = np.stack([src, dst], 1).astype(np.int64)
     pairs = np.concatenate([pairs, [[7, 7], [NB, 3], [-1, 5], [4, NB + 9]]])   # skipped pairs
     kc, vc = _to_dev(kc_ref, dev), _to_dev(vc_ref, dev)
-    assert oracle_lib.copy_blocks(kc_ref, vc_ref, pairs) == 100
+    assert oracle_lib.copy_blocks(kc_ref, vc_ref, pairs) == count
     tv.copy_blocks(kc, vc, _to_dev(pairs, dev))
     torch.cuda.synchronize()
     assert np.array_equal(kc.cpu().numpy().view(np.uint16), kc_ref)
