@@ -231,7 +231,7 @@ def rope_rate(tv, dev, stream, flush, steps, index=3):
     pos = np.concatenate([np.arange(n, dtype=np.int32) for n in pb.query_lens])
     kd, vd, sd, pd = dev_arr(k), dev_arr(v), dev_arr(sl), dev_arr(pos)
     qd = dev_arr(pb.q)
-    f = dev_arr(tv.rope_inv_freq(b.head_dim, 500000.0))
+    f = dev_arr(W.rope_inv_freq(b.head_dim, 500000.0))
     kc, vc = tv.new_pools(b.num_blocks, b.num_kv_heads, b.head_dim, b.block_size, dev, fill=0)
     T = int(len(sl))
     kv_bytes = 2 * 2 * T * b.num_kv_heads * b.head_dim * 2 + T * 8

@@ -165,13 +165,19 @@ tv_status tv_rope(uint16_t *x, const int32_t *positions, const float *inv_freq,
  * partition_size) are not written.  tv_paged_attention_reduce turns these
  * into softmax(scale * q K^T) V.
  *
- *   part_acc      float [num_seqs][num_q_heads][P][head_dim], P = tv_num_partitions(max_context_len, partition_size)
- *   part_max      float [num_seqs][num_q_heads][P]
- *   part_sum      float [num_seqs][num_q_heads][P]
+ *   part_acc      float [num_seqs][num_q_heads][P][head_dim], P = tv_num_partitions(max_context_len, partition_size),
+ *                 16-byte aligned (written with 16-byte stores)
+ *   part_max      float [num_seqs][num_q_heads][P], 4-byte aligned
+ *   part_sum      float [num_seqs][num_q_heads][P], 4-byte aligned
  *   q             bf16  [num_seqs][num_q_heads][head_dim], 16-byte aligned
  *   k_cache, v_cache  pools as above, 16-byte aligned
- *   block_tables  int32 [num_seqs][max_blocks_per_seq]; only the first
- *                 ceil(n / block_size) entries of a row are read
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq].  Only the first
+ *                 ceil(n / block_size) entries of a row are used.  Entries
+ *                 up to min(max_blocks_per_seq, P * partition_size /
+ *                 block_size) of a row may be read (a partition's entries
+ *                 are loaded before its length is known), so the whole row
+ *                 must be readable memory; what unused entries hold does not
+ *                 matter
  *   context_lens  int32 [num_seqs]
  *   max_context_len  host-side upper bound of context_lens (sizes the launch);
  *                 must be <= max_blocks_per_seq * block_size
@@ -261,7 +267,7 @@ tv_status tv_paged_attention_decode_shared(float *part_acc, float *part_max, flo
  * the same call reads gives unspecified values for that sequence.
  *
  *   k_new         bf16 [num_seqs][num_kv_heads][head_dim], 16-byte aligned
- *   v_new         bf16 [num_seqs][num_kv_heads][head_dim], 2-byte aligned
+ *   v_new         bf16 [num_seqs][num_kv_heads][head_dim], 16-byte aligned
  *   slot_mapping  int64 [num_seqs], 8-byte aligned
  *   other arguments as for tv_paged_attention_decode (the pools writable).
  * Supported shapes and errors: as for tv_paged_attention_decode, plus

@@ -7,7 +7,7 @@ marshals torch tensors into the C calls declared in ``include/tv.h``.
 """
 
 from .binding import (LIB_PATH, STREAM_CHUNK_BYTES, BlockManager, TvError, cache_write, cache_write_rope,
-                      copy_blocks, lib, rope, rope_inv_freq,
+                      copy_blocks, lib, rope,
                       load_library, new_pools,
                       new_workspace, num_partitions, paged_attention, paged_attention_decode,
                       paged_attention_decode_append, paged_attention_decode_shared,
@@ -16,7 +16,7 @@ from .binding import (LIB_PATH, STREAM_CHUNK_BYTES, BlockManager, TvError, cache
                       paged_attention_reduce, stream_read)
 
 __all__ = ["LIB_PATH", "STREAM_CHUNK_BYTES", "BlockManager", "TvError", "cache_write", "cache_write_rope",
-           "copy_blocks", "lib", "rope", "rope_inv_freq",
+           "copy_blocks", "lib", "rope",
            "load_library", "new_pools",
            "new_workspace", "num_partitions", "paged_attention", "paged_attention_decode",
            "paged_attention_decode_append", "paged_attention_decode_shared",

@@ -220,14 +220,6 @@ def paged_attention_decode(part_acc, part_max, part_sum, q, k_cache, v_cache, bl
     _check("tv_paged_attention_decode", st)
 
 
-def rope_inv_freq(head_dim: int, base: float):
-    """Plain RoPE frequencies base^(-2k / head_dim), k < head_dim / 2, as float32
-    (host numpy; copy to the device for the calls below)."""
-    import numpy as np
-    k = np.arange(0, head_dim, 2, dtype=np.float64)
-    return (base ** (-k / head_dim)).astype(np.float32)
-
-
 def cache_write_rope(k, v, k_cache, v_cache, slot_mapping, positions, inv_freq,
                      rope_style: int = 0, stream=None) -> None:
     """tv_cache_write_rope: tv_cache_write with K turned by the rotary embedding

@@ -157,7 +157,7 @@ tv_status check_decode(tv::DecodeArgs &a, float *part_acc, float *part_max, floa
     if ((int64_t)num_kv_heads * num_seqs * parts > 0xffffff)
         return TV_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-        !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(part_acc, 4) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(part_acc, 16) ||
         !aligned(part_max, 4) || !aligned(part_sum, 4))
         return TV_ERR_ALIGNMENT;
     a.part_acc = part_acc;
@@ -222,7 +222,7 @@ tv_status tv_paged_attention_decode_append(float *part_acc, float *part_max, flo
         return st;
     if (!k_new || !v_new || !slot_mapping)
         return TV_ERR_NULL;
-    if (!aligned(k_new, 16) || !aligned(v_new, 2) || !aligned(slot_mapping, 8))
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 8))
         return TV_ERR_ALIGNMENT;
     if (num_blocks > INT64_MAX / block_size)
         return TV_ERR_SHAPE;
@@ -347,7 +347,7 @@ tv_status tv_paged_attention_decode_shared_append(
     if (!shared_len || !k_new || !v_new || !slot_mapping)
         return TV_ERR_NULL;
     if (!aligned(shared_len, 4) || !aligned(group_order, 4) || !aligned(k_new, 16) ||
-        !aligned(v_new, 2) || !aligned(slot_mapping, 8))
+        !aligned(v_new, 16) || !aligned(slot_mapping, 8))
         return TV_ERR_ALIGNMENT;
     if (num_blocks > INT64_MAX / block_size)
         return TV_ERR_SHAPE;
@@ -395,7 +395,7 @@ tv_status tv_paged_attention_decode_step(float *out, float *part_acc, float *par
     if ((int64_t)num_seqs * num_q_heads > 0xffffff)
         return TV_ERR_UNSUPPORTED;
     if (!aligned(out, 16) || (!one && !aligned(part_acc, 16)) || !aligned(k_new, 16) ||
-        !aligned(v_new, 2) || !aligned(slot_mapping, 8))
+        !aligned(v_new, 16) || !aligned(slot_mapping, 8))
         return TV_ERR_ALIGNMENT;
     if (num_blocks > INT64_MAX / block_size)
         return TV_ERR_SHAPE;

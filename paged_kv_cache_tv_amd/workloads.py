@@ -61,6 +61,16 @@ def contiguous_waste(max_length: int, num_tokens: int) -> int:
     return max_length - num_tokens
 
 
+def rope_inv_freq(head_dim: int, base: float) -> np.ndarray:
+    """The caller-supplied rotary frequency table for plain RoPE, base^(-2k /
+    head_dim) for k < head_dim / 2, as float32.  It is an input of the rotary
+    calls (both the GPU library and the oracle take it as given), built here
+    with the other inputs; a context-extension scheme would supply another
+    table.  The Llama-3 family uses base 500000."""
+    k = np.arange(0, head_dim, 2, dtype=np.float64)
+    return (base ** (-k / head_dim)).astype(np.float32)
+
+
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round finite float32 values to bf16 (nearest, ties to even); return uint16 bits."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)

@@ -135,6 +135,27 @@ def test_decode_append_validation(lib):
     ptrs = [ALIGNED] * 11
     ptrs[6] = 0x1004                                      # slot_mapping not 8-byte aligned
     assert _app(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
+    for bad_v in (0x1002, 0x1004, 0x1008):                # v_new: loaded 4 bytes per lane,
+        ptrs = [ALIGNED] * 11                             # required 16-byte aligned like k_new
+        ptrs[5] = bad_v
+        assert _app(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
+
+
+def test_partition_pass_part_acc_alignment(lib):
+    """The partition pass writes part_acc with 16-byte stores: every call that
+    takes the workspace refuses a part_acc that is only 4-byte aligned."""
+    dec = [ALIGNED] * 8
+    dec[0] = 0x1004
+    assert _dec(lib, ptrs=tuple(dec)) == TV_ERR_ALIGNMENT
+    app = [ALIGNED] * 11
+    app[0] = 0x1004
+    assert _app(lib, ptrs=tuple(app)) == TV_ERR_ALIGNMENT
+    shd = [ALIGNED] * 10
+    shd[0] = 0x1004
+    assert _shd(lib, ptrs=tuple(shd)) == TV_ERR_ALIGNMENT
+    sha = [ALIGNED] * 12 + [None]
+    sha[0] = 0x1004
+    assert _sha(lib, ptrs=tuple(sha)) == TV_ERR_ALIGNMENT
 
 
 def _stp(lib, S=2, hq=32, hkv=8, d=64, mctx=64, part=32, ptrs=(BAD,) * 12):
@@ -175,6 +196,9 @@ def test_decode_step_validation(lib):
     two[1] = ALIGNED
     two[0] = None                                         # out
     assert _stp(lib, ptrs=tuple(two)) == TV_ERR_NULL
+    two[0] = ALIGNED
+    two[6] = 0x1004                                       # v_new not 16-byte aligned
+    assert _stp(lib, ptrs=tuple(two)) == TV_ERR_ALIGNMENT
 
 
 def _shd(lib, S=2, hq=32, hkv=8, gs=4, mctx=64, part=32, ptrs=(BAD,) * 10):

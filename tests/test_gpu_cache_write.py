@@ -85,7 +85,7 @@ def test_cache_write_paths(dev, oracle_lib, aligned, rope_style, reps):
     k = W.round_to_bf16_bits(rng.standard_normal((T, HKV, D)).astype(np.float32))
     v = W.round_to_bf16_bits(rng.standard_normal((T, HKV, D)).astype(np.float32))
     pos = rng.integers(0, 70000, T).astype(np.int32)
-    f = tv.rope_inv_freq(D, 500000.0)
+    f = W.rope_inv_freq(D, 500000.0)
     kc, vc = _pools(dev, aligned)
     if rope_style is None:
         tv.cache_write(_to_dev(k, dev), _to_dev(v, dev), kc, vc, _to_dev(slots, dev))

@@ -63,7 +63,7 @@ def test_engine_flow(dev, oracle_lib):
     prompts = [45, 300, 513]
     nseq = len(prompts) * SAMPLES
     bm = tv.BlockManager(NB, BS, nseq, WIDTH)
-    f = tv.rope_inv_freq(D, 500000.0)
+    f = W.rope_inv_freq(D, 500000.0)
     fd = _to_dev(f, dev)
     kc, vc = tv.new_pools(NB, HKV, D, BS, dev, fill=W.BF16_NAN)
     kr, vr = O.Oracle.new_pools(NB, HKV, D, BS)

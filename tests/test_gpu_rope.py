@@ -79,7 +79,7 @@ def test_rope_in_place(dev, oracle_lib, style):
     x = W.round_to_bf16_bits(rng.standard_normal((T, H, D)).astype(np.float32) * 3)
     pos = np.concatenate([[0, 1, 2, 15, 16, 4095, 65535, 131071, 131072, -7],
                           rng.integers(0, 140000, T - 10)]).astype(np.int32)
-    f = tv.rope_inv_freq(D, 500000.0)
+    f = W.rope_inv_freq(D, 500000.0)
     xd = _to_dev(x, dev)
     tv.rope(xd, _to_dev(pos, dev), _to_dev(f, dev), style)
     torch.cuda.synchronize()
@@ -103,7 +103,7 @@ def test_cache_write_rope(dev, oracle_lib, style, head_dim, heads):
     slots = rng.choice(NB * BS, T, replace=False).astype(np.int64)
     slots[[3, 50, 199]] = [-1, NB * BS, -5]                 # skipped
     pos = rng.integers(0, 131072, T).astype(np.int32)
-    f = tv.rope_inv_freq(head_dim, 10000.0)
+    f = W.rope_inv_freq(head_dim, 10000.0)
     kc, vc = tv.new_pools(NB, heads, head_dim, BS, dev, fill=W.BF16_NAN)
     tv.cache_write_rope(_to_dev(k, dev), _to_dev(v, dev), kc, vc, _to_dev(slots, dev),
                         _to_dev(pos, dev), _to_dev(f, dev), style)
@@ -131,7 +131,7 @@ def test_decode_with_rope_end_to_end(dev, oracle_lib):
     import torch
     import paged_kv_cache_tv_amd as tv
     b = W.make_batch([1, 37, 300, 1025], 95)
-    f = tv.rope_inv_freq(D, 500000.0)
+    f = W.rope_inv_freq(D, 500000.0)
     fd = _to_dev(f, dev)
     kc, vc = tv.new_pools(b.num_blocks, b.num_kv_heads, D, b.block_size, dev, fill=W.BF16_NAN)
     kr, vr = O.Oracle.new_pools(b.num_blocks, b.num_kv_heads, D, b.block_size)
