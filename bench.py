@@ -323,24 +323,132 @@ def shared_prefix_rate(tv, dev, stream, flush, steps):
     return res
 
 
-def cpu_baseline(batch, target_seconds: float):
-    """Time the CPU oracle doing the same step (cache write + attention) on this host."""
+def cold_loop_ms(stream, flush, body, k):
+    """Mean ms per iteration of (eviction, body), minus the eviction alone: k
+    iterations back to back between two events on the kernels' stream."""
+    import torch
+
+    def loop(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(k):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    with_body = loop(lambda i: (flush(i), body()))
+    return with_body - loop(flush)
+
+
+def workloads_rate(tv, dev, stream, flush, steps, warmup, partition_size, have=None):
+    """The decode step on every one of the five workloads, cold, timed as the
+    headline step is (eviction-subtracted event loop): the two-launch step
+    (decode_append + reduce) and the one-call step (tv_paged_attention_decode_step:
+    one launch when the contexts fit one partition).  Workload 4 also runs its
+    parallel-sampling form (shared prefix read once per group of 4:
+    tv_paged_attention_decode_shared_append + reduce).  GB/s counts the same
+    algorithmic bytes as the headline; for workload 4 both the logical bytes
+    (every sequence's context) and the unique ones (each shared block once).
+    `have` maps a workload index to an already built (batch, DeviceBatch)."""
+    import torch
+    from paged_kv_cache_tv_amd import workloads as W
+    from paged_kv_cache_tv_amd.step import DeviceBatch
+    res = {}
+    for idx in (1, 2, 3, 4, 5):
+        if have and idx in have:
+            batch, db = have[idx]
+        else:
+            batch = W.make_workload(idx)
+            db = DeviceBatch(batch, dev, partition_size=partition_size)
+            db.fill()
+        forms = {"two_launch": lambda: db.fused_step(stream),
+                 "one_call": lambda: db.call_step(stream)}
+        shared = None
+        if idx == 4:
+            shared = torch.full((batch.num_seqs // 4,), 1024, dtype=torch.int32, device=dev)
+            pa, pm, ps = db.workspace
+
+            def grouped_step():
+                tv.paged_attention_decode_shared_append(
+                    pa, pm, ps, db.q, db.step_k, db.step_v, db.step_slots, db.k_cache,
+                    db.v_cache, db.block_tables, db.context_lens, shared, 4, db.max_context_len,
+                    db.partition_size, batch.scale, stream)
+                db.reduce(stream)
+            forms["shared_prefix_two_launch"] = grouped_step
+        for fn in forms.values():
+            for i in range(max(1, warmup)):
+                flush(i)
+                fn()
+        _, step_bytes, _ = algorithmic_bytes(batch)
+        entry = {"num_seqs": batch.num_seqs, "context_tokens": batch.total_tokens,
+                 "context_len_range": [int(batch.context_lens.min()),
+                                       int(batch.context_lens.max())],
+                 "partitions": int(-(-db.max_context_len // db.partition_size)),
+                 "step_bytes": step_bytes}
+        for name, fn in forms.items():
+            ms = cold_loop_ms(stream, flush, fn, steps)
+            e = {"step_us": round(ms * 1e3, 2),
+                 "GB_per_s": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                 "pct_of_hbm_peak": round(100.0 * step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                 "seq_tokens_per_s": round(batch.total_tokens / (ms * 1e-3), 1),
+                 "decode_tokens_per_s": round(batch.num_seqs / (ms * 1e-3), 1)}
+            if idx == 4:
+                unique = step_bytes - batch.kv_bytes_logical() + batch.kv_bytes_unique()
+                e["GB_per_s_unique"] = round(unique / (ms * 1e-3) / 1e9, 1)
+                e["pct_of_hbm_peak_unique"] = round(
+                    100.0 * unique / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
+            entry[name] = e
+        if idx == 4:
+            entry["step_bytes_unique"] = (step_bytes - batch.kv_bytes_logical()
+                                          + batch.kv_bytes_unique())
+        res[batch.name] = entry
+        if not (have and idx in have):
+            del db
+        torch.cuda.synchronize()
+    return res
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(batch, target_seconds: float, single_runs: int = 3):
+    """Time the CPU oracle doing the same step (cache write + attention) on this
+    host: repeated for about `target_seconds` with every core this process may
+    use, then `single_runs` times on one thread.  Returns (output, multi-thread
+    times, threads, single-thread times)."""
     import oracle as O
     orc = O.default()
     threads = O.cpu_count()
     kc, vc = O.build_pools(orc, batch, include_step=False)
     sk, sv, ss = batch.step_inputs()
+
+    def one(nthreads):
+        t0 = time.perf_counter()
+        orc.cache_write(sk, sv, kc, vc, ss)
+        o = orc.paged_attention(batch.q, kc, vc, batch.block_tables, batch.context_lens,
+                                batch.scale, nthreads)
+        return o, time.perf_counter() - t0
+
     times, out = [], None
     t_start = time.perf_counter()
     while True:
-        t0 = time.perf_counter()
-        orc.cache_write(sk, sv, kc, vc, ss)
-        out = orc.paged_attention(batch.q, kc, vc, batch.block_tables, batch.context_lens,
-                                  batch.scale, threads)
-        times.append(time.perf_counter() - t0)
+        out, t = one(threads)
+        times.append(t)
         if time.perf_counter() - t_start >= target_seconds and len(times) >= 1:
             break
-    return out, times, threads
+    single = [one(1)[1] for _ in range(single_runs)]
+    return out, times, threads, single
 
 
 def main(argv=None):
@@ -357,6 +465,8 @@ def main(argv=None):
                     help="skip the prefill attention measurement")
     ap.add_argument("--no-block-copy", action="store_true",
                     help="skip the copy-on-write block copy measurement")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the step on all five workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-flush", action="store_true", help="skip the cold-cache flush")
     ap.add_argument("--lib", default=None, help="load libtv from this path instead of the package")
@@ -565,6 +675,9 @@ def main(argv=None):
                                 "roofline kernel, cold cache, same timing method"},
     }
 
+    if not args.no_workloads:
+        result["workloads"] = workloads_rate(tv, dev, stream, flush, K, args.warmup,
+                                             args.partition_size, {args.workload: (batch, db)})
     if not args.no_block_copy:
         result["block_copy"] = block_copy_rate(tv, dev, stream, flush, K)
         result["block_manager"] = block_manager_rate(tv, K)
@@ -574,14 +687,21 @@ def main(argv=None):
         result["shared_prefix"] = shared_prefix_rate(tv, dev, stream, flush, K)
 
     if not args.no_cpu_baseline:
-        ref, times, threads = cpu_baseline(batch, args.cpu_seconds)
+        ref, times, threads, single = cpu_baseline(batch, args.cpu_seconds)
         t = float(np.median(times))
+        t1 = float(np.median(single))
         result["cpu_baseline"] = {
             "value": round(step_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "median_step_s": round(t, 4),
+            "single_thread": {"value": round(step_bytes / t1 / 1e9, 4), "unit": "GB/s",
+                              "cores": 1, "median_step_s": round(t1, 4), "runs": len(single)},
             "sample": f"the full step of {batch.name} (cache write of {batch.num_seqs} tokens + "
-                      f"attention over {batch.total_tokens} context tokens, fp64), repeated "
-                      f"{len(times)}x for {sum(times):.1f}s; median step {t:.3f}s",
+                      f"attention over {batch.total_tokens} context tokens; the oracle computes "
+                      f"in fp64), repeated {len(times)}x for {sum(times):.1f}s on {threads} "
+                      f"threads (median step {t:.3f}s), then {len(single)}x on one thread "
+                      f"(median {t1:.3f}s)",
         }
         err = np.abs(out.astype(np.float64) - ref)
         result["parity"] = {"max_abs": float(err.max()), "mean_abs": float(err.mean())}
