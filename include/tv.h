@@ -67,7 +67,9 @@ typedef enum tv_status {
     TV_ERR_UNSUPPORTED = 3,  /* valid shape that this build does not implement */
     TV_ERR_HIP = 4,          /* the HIP runtime reported an error when launching */
     TV_ERR_ALIGNMENT = 5,    /* a pointer is not aligned as required */
-    TV_ERR_NO_BLOCKS = 6     /* block manager: no free block left (or host memory exhausted) */
+    TV_ERR_NO_BLOCKS = 6,    /* block manager: no free block left (or host memory exhausted) */
+    TV_ERR_SCRATCH = 7       /* the call's workspace exceeds the fixed scratch array
+                                (tv_paged_attention_decode_step_noalloc) */
 } tv_status;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -385,6 +387,39 @@ tv_status tv_paged_attention_decode_step(float *out, float *part_acc, float *par
                                          int32_t max_blocks_per_seq, int64_t num_blocks,
                                          int32_t max_context_len, int32_t partition_size,
                                          float scale, void *stream);
+
+/*
+ * The decode step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Computes exactly what tv_paged_attention_decode_step computes (out is
+ * bitwise the same) and takes the same arguments minus the workspace: the
+ * partition workspace lives in a fixed device array of
+ * TV_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from the
+ * first such call on that GPU until the process ends.  The call allocates
+ * nothing and frees nothing.
+ *
+ * Limit: with P = ceil(max_context_len / partition_size) > 1 the workspace is
+ * num_seqs * num_q_heads * P * (head_dim + 2) * 4 bytes and must not exceed
+ * TV_NOALLOC_SCRATCH_BYTES (16 MiB: e.g. 64 sequences x 32 heads x 8
+ * partitions of 512 tokens takes 4.3 MB, 4 x 32 x 256 partitions 8.7 MB);
+ * beyond it the call returns TV_ERR_SCRATCH before anything is launched.
+ * With P <= 1 no workspace is used and there is no limit.
+ *
+ * Every call on one GPU shares that GPU's array and may leave anything in
+ * it; nothing in it needs clearing between calls.  Calls that overlap on one
+ * GPU (two streams, or two host threads without ordering) race on the array
+ * and give unspecified results: order them on one stream.
+ *
+ * Errors: those of tv_paged_attention_decode_step, plus TV_ERR_SCRATCH.
+ */
+#define TV_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+tv_status tv_paged_attention_decode_step_noalloc(
+    float *out, const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+    const int64_t *slot_mapping, uint16_t *k_cache, uint16_t *v_cache,
+    const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+    int32_t partition_size, float scale, void *stream);
 
 /*
  * Prefill and chunked prefill ("tiny-vLLM으로 처음부터 고성능 LLM 추론 엔진

@@ -12,6 +12,7 @@ from .binding import (LIB_PATH, STREAM_CHUNK_BYTES, BlockManager, TvError, cache
                       new_workspace, num_partitions, paged_attention, paged_attention_decode,
                       paged_attention_decode_append, paged_attention_decode_shared,
                       paged_attention_decode_shared_append, paged_attention_decode_step,
+                      paged_attention_decode_step_noalloc,
                       paged_attention_prefill,
                       paged_attention_reduce, stream_read)
 
@@ -21,4 +22,5 @@ __all__ = ["LIB_PATH", "STREAM_CHUNK_BYTES", "BlockManager", "TvError", "cache_w
            "new_workspace", "num_partitions", "paged_attention", "paged_attention_decode",
            "paged_attention_decode_append", "paged_attention_decode_shared",
            "paged_attention_decode_shared_append", "paged_attention_decode_step",
+           "paged_attention_decode_step_noalloc",
            "paged_attention_prefill", "paged_attention_reduce", "stream_read"]

@@ -20,7 +20,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtv.so")
 
 TV_OK = 0
 STATUS_NAMES = {0: "TV_OK", 1: "TV_ERR_NULL", 2: "TV_ERR_SHAPE", 3: "TV_ERR_UNSUPPORTED",
-                4: "TV_ERR_HIP", 5: "TV_ERR_ALIGNMENT", 6: "TV_ERR_NO_BLOCKS"}
+                4: "TV_ERR_HIP", 5: "TV_ERR_ALIGNMENT", 6: "TV_ERR_NO_BLOCKS",
+                7: "TV_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024     # TV_NOALLOC_SCRATCH_BYTES
 
 
 class TvError(RuntimeError):
@@ -55,6 +57,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_paged_attention_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                    vp, i32, i32, i32, i32, i32, i32, i64, i32,
                                                    i32, f32, vp]
+    lib.tv_paged_attention_decode_step_noalloc.restype = ctypes.c_int
+    lib.tv_paged_attention_decode_step_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                                           i32, i32, i32, i32, i32, i64, i32, i32,
+                                                           f32, vp]
     lib.tv_paged_attention_decode_shared.restype = ctypes.c_int
     lib.tv_paged_attention_decode_shared.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                                      i32, i32, i32, i32, i32, i32, i64, i32, i32,
@@ -411,6 +417,38 @@ def paged_attention_decode_step(out, workspace, q, k_new, v_new, slot_mapping, k
         context_lens.data_ptr(), S, hq, hkv, d, bs, block_tables.shape[1], nb,
         int(max_context_len), int(partition_size), float(scale), _stream_handle(stream, q.device))
     _check("tv_paged_attention_decode_step", st)
+
+
+def paged_attention_decode_step_noalloc(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                        block_tables, context_lens, max_context_len: int,
+                                        partition_size: int, scale: float, stream=None) -> None:
+    """tv_paged_attention_decode_step_noalloc: the whole decode step with the
+    partition workspace in the library's fixed per-GPU array (nothing is
+    allocated by the call; workspaces above NOALLOC_SCRATCH_BYTES raise
+    TvError TV_ERR_SCRATCH)."""
+    import torch
+    _need(out, "out", dtype=torch.float32, ndim=3)
+    _need(q, "q", itemsize=2, ndim=3)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, itemsize=2, ndim=3)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1)
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    S, hq, d = q.shape
+    nb, hkv, bs, d2 = _pool_dims(k_cache, v_cache)
+    if d2 != d or tuple(out.shape) != (S, hq, d):
+        raise ValueError("out must be [S, Hq, D] and the caches must match q")
+    if tuple(k_new.shape) != (S, hkv, d) or tuple(v_new.shape) != (S, hkv, d) or \
+            slot_mapping.shape[0] != S:
+        raise ValueError("k_new, v_new must be [S, Hkv, D] and slot_mapping [S]")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    st = lib().tv_paged_attention_decode_step_noalloc(
+        out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+        slot_mapping.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), S, hq, hkv, d, bs, block_tables.shape[1], nb,
+        int(max_context_len), int(partition_size), float(scale), _stream_handle(stream, q.device))
+    _check("tv_paged_attention_decode_step_noalloc", st)
 
 
 def paged_attention_decode_shared_append(part_acc, part_max, part_sum, q, k_new, v_new,

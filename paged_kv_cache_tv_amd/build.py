@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtv.so")
 
 SOURCES = ["cache_write.hip", "paged_decode.hip", "paged_reduce.hip", "block_copy.hip",
-           "paged_prefill.hip", "stream_read.hip", "tv_api.cpp",
+           "paged_prefill.hip", "stream_read.hip", "noalloc.hip", "tv_api.cpp",
            "block_manager.cpp"]
 ARCH = "gfx950"
 # Packed-FP32 VALU forms are switched off for all device code.

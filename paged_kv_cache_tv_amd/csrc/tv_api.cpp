@@ -28,6 +28,7 @@ const char *tv_status_string(tv_status status)
     case TV_ERR_HIP: return "TV_ERR_HIP: HIP runtime error";
     case TV_ERR_ALIGNMENT: return "TV_ERR_ALIGNMENT: misaligned pointer";
     case TV_ERR_NO_BLOCKS: return "TV_ERR_NO_BLOCKS: no free block (or no host memory)";
+    case TV_ERR_SCRATCH: return "TV_ERR_SCRATCH: workspace larger than the fixed scratch array";
     }
     return "unknown tv_status";
 }

@@ -373,3 +373,26 @@ def test_binding_refuses_host_tensors():
         tv.cache_write(x, x, torch.zeros((2, 8, 8, 16, 8), dtype=torch.int16),
                        torch.zeros((2, 8, 64, 16), dtype=torch.int16),
                        torch.zeros(1, dtype=torch.int64))
+
+
+def test_decode_step_noalloc_refuses_oversized_workspace(lib):
+    """tv_paged_attention_decode_step_noalloc: a workspace above the fixed
+    scratch array (16 MiB) is refused before anything touches the GPU; the
+    refusal needs no device, so it runs here.  Below the limit the call
+    checks its arguments as tv_paged_attention_decode_step does."""
+    TV_ERR_SCRATCH = 7
+    fn = lib.tv_paged_attention_decode_step_noalloc
+
+    def call(S, mctx, part, ptrs=(ALIGNED,) * 9, hq=32, d=64):
+        return fn(*ptrs, S, hq, 8, d, 16, max(1, mctx // 16), 1 << 20, mctx, part, 0.125, None)
+
+    # 64 x 32 x 248 x 66 x 4 B = 16.76 MB > 16 MiB; 64 x 32 x 8 x 66 x 4 B = 4.3 MB fits.
+    assert call(64, 248 * 16, 16) == TV_ERR_SCRATCH
+    assert call(1 << 20, 1 << 20, 512) == TV_ERR_SCRATCH       # no overflow in the size
+    assert call((1 << 31) - 1, (1 << 31) - 1, 16, hq=(1 << 31) - 1) == TV_ERR_SCRATCH
+    # One partition needs no workspace: no limit; the step's own checks then
+    # report the misaligned pointers (nothing launches).
+    assert call(1 << 20, 512, 512, ptrs=(BAD,) * 9) == TV_ERR_ALIGNMENT
+    assert call(-1, 4096, 512) == TV_ERR_SHAPE
+    assert call(0, 4096, 512) == TV_OK
+    assert lib.tv_status_string(TV_ERR_SCRATCH).startswith(b"TV_ERR_SCRATCH")
