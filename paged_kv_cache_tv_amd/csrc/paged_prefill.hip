@@ -18,25 +18,43 @@
 //     heaviest tiles of every sequence first.
 //   * Keys go in chunks of 64 (4 blocks).  All 512 threads load a chunk's K
 //     and V tiles (16 KiB) into registers one chunk ahead and store them to
-//     LDS, double-buffered, with one barrier per chunk.  Each wavefront then
-//     reads MFMA operands from LDS: K tiles verbatim (every 1 KiB operand
-//     read contiguous), V rearranged so that one 16-byte read is a whole PV
-//     operand and 16 consecutive dims fall on distinct banks.
+//     LDS, double-buffered, with one barrier per chunk.  K tiles are stored
+//     verbatim (every 1 KiB operand read contiguous).  V is stored in PV
+//     operand order: one 16-byte slot per (dimension, token group) holding 4
+//     tokens of the dimension from each of two blocks, the slots of one
+//     operand read in lane order.  Each thread loads its slot's two 8-byte
+//     halves from the two blocks and stores the slot with one 16-byte write,
+//     so every LDS store and every operand read covers 1 KiB contiguous, which
+//     gfx950 serves without bank conflicts.
 //   * Each wavefront owns 32 rows (2 tiles of 16 MFMA columns); the register
 //     budget is cut to 128 so that four wavefronts share each SIMD, which
-//     hides the latency of the LDS reads, the cross-lane maximum and the
-//     MFMA results.  Scores
+//     hides the latency of the LDS reads and the MFMA results.  Scores
 //     S^T[16 keys][16 rows] = K . Q^T take two v_mfma_f32_16x16x32_bf16 per
 //     tile (dims 0-31, 32-63).  Lane (q = lane/16, c = lane%16) then holds
 //     keys 4q..4q+3 of every 16-key tile for row c, and two such tiles form
 //     the lane's 8 k-slots of the B operand of O^T += V^T . P^T
 //     (v_mfma_f32_16x16x32_bf16 over 32 keys), with V^T read from LDS in the
-//     same key order.  P is rounded to bf16 for that product; the running
-//     sum uses the fp32 values.
-//   * exp is 2^x (v_exp_f32) with scale * log2(e) folded into one multiply-add
-//     per score.  Masked scores (future positions, keys past the context,
-//     blocks outside the pool) become -inf, and V of keys past the context or
-//     in dropped blocks is zeroed in LDS, because stale slots may hold NaN.
+//     same key order.
+//   * Softmax in base-2 units (v_exp_f32), scale * log2(e) folded into one
+//     multiply-add per score.  The weights are rounded to bf16 for the PV
+//     product, and the running sum adds those same rounded weights
+//     (v_dot2c_f32_bf16 against (1, 1)), so each row's output is exactly a
+//     weighted mean of V rows.  The row maximum uses v_maximum3_f32 and the
+//     gfx950 lane-swap instructions across the 4 lane groups (no LDS).
+//   * The running maximum is a reference value that only moves when needed.
+//     The weights of each 32 keys are first taken against the reference as
+//     it stands; only if a row has no reference yet, or a lane's 8 weights
+//     sum to more than 2^8 (kLaneSumLimit; an overflow to inf also fails the
+//     test), is the row maximum of those keys computed, the reference
+//     moved up to it, the row's output and sum rescaled, and the weights taken
+//     again.  Weights therefore never exceed 2^8, well inside bf16 and fp32
+//     range, and the result is the same softmax (the reference cancels in the
+//     final division).  With well-scaled scores the reference is set by a
+//     row's first keys, and later keys skip both the row maximum and the
+//     rescale of 16 accumulators per row tile.
+//   * Masked scores (future positions, keys past the context, blocks outside
+//     the pool) become -inf, and V of keys past the context or in dropped
+//     blocks is zeroed in LDS, because stale slots may hold NaN.
 #include "tv_internal.h"
 
 #include <math.h>
@@ -45,6 +63,7 @@ namespace tv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -59,6 +78,9 @@ constexpr int kChunkBlocks = 4;                  // blocks per key chunk
 constexpr int kChunkKeys = kChunkBlocks * BS;    // 64
 constexpr int kTileBytes = BS * D * 2;           // one (block, K/V head) tile: 2 KiB
 constexpr int kBufBytes = 2 * kChunkBlocks * kTileBytes;   // K then V of one chunk: 16 KiB
+constexpr float kLaneSumLimit = 256.0f;          // a lane's weights of 32 keys may sum to this
+static_assert(kThreads == kChunkBlocks * 128, "one 16-byte K piece per thread per chunk");
+static_assert(kThreads == (kChunkBlocks / 2) * D * 4, "one 16-byte V slot per thread per chunk");
 
 __device__ __forceinline__ unsigned zero_from(unsigned w, int lim, int e)
 {
@@ -66,6 +88,47 @@ __device__ __forceinline__ unsigned zero_from(unsigned w, int lim, int e)
     const unsigned lo = e >= lim ? 0u : (w & 0xFFFFu);
     const unsigned hi = e + 1 >= lim ? 0u : (w & 0xFFFF0000u);
     return lo | hi;
+}
+
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// The pair (x[l], x[l ^ 32]) (swap32) or (x[l], x[l ^ 16]) (swap16), in some
+// order, from v_permlane32_swap / v_permlane16_swap.  The results are copied
+// out of the returned vector before the bit casts: a bit cast of a vector
+// element reads the vector's first element here.
+__device__ __forceinline__ void swap32(float x, float &a, float &b)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    a = __builtin_bit_cast(float, r0);
+    b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ void swap16(float x, float &a, float &b)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    a = __builtin_bit_cast(float, r0);
+    b = __builtin_bit_cast(float, r1);
+}
+
+// Maximum and sum over the lanes l, l^16, l^32, l^48 (the 4 lane groups
+// holding one row's keys), without LDS.
+__device__ __forceinline__ float group_max(float x)
+{
+    float a, b;
+    swap32(x, a, b);
+    swap16(max2(a, b), a, b);
+    return max2(a, b);
+}
+
+__device__ __forceinline__ float group_sum(float x)
+{
+    float a, b;
+    swap32(x, a, b);
+    swap16(a + b, a, b);
+    return a + b;
 }
 
 template <int G>
@@ -132,83 +195,87 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
         qop[rt][1] = __builtin_bit_cast(bf16x8, x1);
     }
 
-    // Chunk loading: a chunk is 4 blocks x (K tile, V tile) x 128 pieces of
-    // 16 bytes.  Piece p = tid + kThreads * u (u < kLoads) is byte 16 (p & 127)
-    // of the K (bit 7 of p clear) or V tile of block p / 256.
-    constexpr int kLoads = kChunkBlocks * 256 / kThreads;
-    static_assert(kLoads * kThreads == kChunkBlocks * 256, "pieces per thread");
-    const bool is_v = (tid >> 7) & 1;
-    const int piece = tid & 127;
-    const char *pool = reinterpret_cast<const char *>(is_v ? a.v_cache : a.k_cache);
+    // Chunk loading.  K: thread tid moves 16-byte piece tid & 127 of block
+    // kb = tid >> 7's tile.  V: thread tid takes block pair vp = tid >> 8 and
+    // slot u = tid & 255 = (dt, g, c): tokens 4g .. 4g + 3 of dimension
+    // d = 16 dt + c from each block of the pair (8 bytes each), stored as the
+    // 16-byte slot u of the pair's region.  That is exactly the operand lane
+    // (c + 16 g) of the PV product for dimension tile dt reads, so both the
+    // stores and the operand reads cover 1 KiB contiguous per instruction
+    // (conflict-free on gfx950; strided 16-byte reads are not).  kb and vp
+    // are the same for the whole wavefront, so the table entries, validity
+    // and tile addresses are scalar values.
+    const int kb = __builtin_amdgcn_readfirstlane(tid >> 7);
+    const int vp = __builtin_amdgcn_readfirstlane(tid >> 8);
+    const int vg = (tid >> 4) & 3;
+    const int vd = ((tid >> 6) & 3) * 16 + (tid & 15);
+    const uint32_t k_off = 16u * (uint32_t)(tid & 127);                 // bytes in a K tile
+    const uint32_t v_off = (uint32_t)(vd * (2 * BS) + 8 * vg);          // bytes in a V tile
+    const int k_st = kb * kTileBytes + 16 * (tid & 127);
+    const int v_st = kChunkBlocks * kTileBytes + vp * 4096 + 16 * (tid & 255);
     const int32_t *table = a.block_tables + (int64_t)s * a.max_blocks;
-    // V piece = dimension piece / 2, tokens 8 (piece & 1) .. + 8 of its block.
-    const int v_tok0 = 8 * (piece & 1);
+    // Entries outside [0, num_blocks) drop their block: one unsigned compare
+    // against the pool size (capped where it exceeds every int32 entry).
+    const uint32_t nb_cap = a.num_blocks > 0x7fffffff ? 0x80000000u : (uint32_t)a.num_blocks;
+    const char *kheads = reinterpret_cast<const char *>(a.k_cache) + (int64_t)kvh * kTileBytes;
+    const char *vheads = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * kTileBytes;
+    const int64_t block_stride = (int64_t)a.num_kv_heads * kTileBytes;
 
-    u32x4 pre[kLoads];
+    u32x4 kpre;
+    u32x2 vpre0, vpre1;
     unsigned valid_next = 0;
+    auto entry = [&](int b) -> int32_t { return b * BS < n ? table[b] : -1; };
     auto load_chunk = [&](int c) {
+        const int b0 = c * kChunkBlocks;
         valid_next = 0;
 #pragma unroll
-        for (int j = 0; j < kChunkBlocks; ++j) {
-            const int b = c * kChunkBlocks + j;
-            const int32_t phys = b * BS < n ? table[b] : -1;
-            valid_next |= (phys >= 0 && (int64_t)phys < a.num_blocks ? 1u : 0u) << j;
-        }
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u) {
-            const int j = (tid + kThreads * u) >> 8;
-            const int b = c * kChunkBlocks + j;
-            const u32x4 zero = {0u, 0u, 0u, 0u};
-            pre[u] = zero;
-            if ((valid_next >> j) & 1u)
-                pre[u] = *reinterpret_cast<const u32x4 *>(
-                    pool + ((int64_t)table[b] * a.num_kv_heads + kvh) * kTileBytes + 16 * piece);
-        }
+        for (int j = 0; j < kChunkBlocks; ++j)
+            valid_next |= ((uint32_t)entry(b0 + j) < nb_cap ? 1u : 0u) << j;
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
+        const u32x2 z2 = {0u, 0u};
+        const int32_t pk = entry(b0 + kb);
+        const int32_t pa = entry(b0 + 2 * vp);
+        const int32_t pb = entry(b0 + 2 * vp + 1);
+        kpre = (uint32_t)pk < nb_cap
+                   ? *reinterpret_cast<const u32x4 *>(kheads + pk * block_stride + k_off)
+                   : z4;
+        vpre0 = (uint32_t)pa < nb_cap
+                    ? *reinterpret_cast<const u32x2 *>(vheads + pa * block_stride + v_off)
+                    : z2;
+        vpre1 = (uint32_t)pb < nb_cap
+                    ? *reinterpret_cast<const u32x2 *>(vheads + pb * block_stride + v_off)
+                    : z2;
     };
     auto store_chunk = [&](int c, char *buf) {
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u) {
-            const int j = (tid + kThreads * u) >> 8;
-            u32x4 x = pre[u];
-            if (is_v) {
-                // Keys at or past the context end: V = 0 (the slot may hold NaN).
-                const int lim = n - ((c * kChunkBlocks + j) * BS + v_tok0);
-                if (lim < 8) {
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        x[w] = zero_from(x[w], lim, 2 * w);
-                }
-            }
-            if (is_v) {
-                // V of a chunk in LDS: [block pair kp][dim d][slot][block of the
-                // pair], 8 bytes (4 tokens) each, so that one 16-byte read gives
-                // the PV operand of 4 tokens of both blocks.  Token group g of
-                // dim d sits in slot g ^ f(d % 16), f(c) = (c ^ (c >> 2)) & 3,
-                // which keeps the operand reads of 16 consecutive dims on
-                // distinct banks.
-                const int d = piece >> 1, g0 = 2 * (piece & 1);
-                const int f = (d ^ (d >> 2)) & 3;
-                char *row = buf + kChunkBlocks * kTileBytes + (j >> 1) * 4096 + d * 64 + 8 * (j & 1);
-                const u32x2 lo = {x[0], x[1]}, hi = {x[2], x[3]};
-                *reinterpret_cast<u32x2 *>(row + 16 * (g0 ^ f)) = lo;
-                *reinterpret_cast<u32x2 *>(row + 16 * ((g0 + 1) ^ f)) = hi;
-            } else {
-                *reinterpret_cast<u32x4 *>(buf + j * kTileBytes + 16 * piece) = x;
-            }
+        *reinterpret_cast<u32x4 *>(buf + k_st) = kpre;
+        u32x2 x0 = vpre0, x1 = vpre1;
+        if (c * kChunkKeys + kChunkKeys > n) {
+            // The chunk holding the context end: V of keys at or past it is
+            // 0 (the slot may hold NaN).
+            const int lim0 = n - ((c * kChunkBlocks + 2 * vp) * BS + 4 * vg);
+            const int lim1 = lim0 - BS;
+            x0[0] = zero_from(x0[0], lim0, 0);
+            x0[1] = zero_from(x0[1], lim0, 2);
+            x1[0] = zero_from(x1[0], lim1, 0);
+            x1[1] = zero_from(x1[1], lim1, 2);
         }
+        const u32x4 slot = {x0[0], x0[1], x1[0], x1[1]};
+        *reinterpret_cast<u32x4 *>(buf + v_st) = slot;
     };
 
     f32x4 o[kRowTiles][4];
-    float m_run[kRowTiles], l_run[kRowTiles];
+    float m_ref[kRowTiles], m_use[kRowTiles], l_run[kRowTiles];   // base-2 units
 #pragma unroll
     for (int rt = 0; rt < kRowTiles; ++rt) {
-        m_run[rt] = -INFINITY;
+        m_ref[rt] = -INFINITY;                               // reference maximum (base-2 units)
+        m_use[rt] = 0.f;                                     // the same, 0 while no key is seen
         l_run[rt] = 0.f;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
             o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const float cs = a.scale_log2;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     if (nchunks > 0)
         load_chunk(0);
@@ -222,93 +289,112 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
         if (c * kChunkKeys > wave_last_pos)
             continue;                                        // this wave's rows are done
 
-        // Scores.
-        f32x4 sc[kRowTiles][4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            const char *kb = buf + kt * kTileBytes + 16 * lane;
-            const bf16x8 k0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kb));
-            const bf16x8 k1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kb + 1024));
-#pragma unroll
-            for (int rt = 0; rt < kRowTiles; ++rt) {
-                f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[rt][0], z, 0, 0, 0);
-                sc[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[rt][1], z, 0, 0, 0);
-            }
-        }
-
-        // Mask keys after a row's position and keys of dropped blocks.
+        // The chunk in two halves of 32 keys (block pair kp = blocks 2 kp and
+        // 2 kp + 1): scores, softmax weights, then their PV product, so only
+        // half a chunk of scores and weights is live at a time.
         const int key0 = c * kChunkKeys + 4 * lq;           // this lane's key of slot (kt 0, j 0)
-        if (c * kChunkKeys + kChunkKeys - 1 > wave_first_pos || valid != 0xFu) {
+        const bool mask = c * kChunkKeys + kChunkKeys - 1 > wave_first_pos || valid != 0xFu;
+        const char *vb = buf + kChunkBlocks * kTileBytes + 16 * lane;
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+            // Scores of key tiles 2 kp + h.
+            f32x4 sc[kRowTiles][2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const char *kbuf = buf + (2 * kp + h) * kTileBytes + 16 * lane;
+                const bf16x8 k0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kbuf));
+                const bf16x8 k1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kbuf + 1024));
+#pragma unroll
+                for (int rt = 0; rt < kRowTiles; ++rt) {
+                    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[rt][0], z, 0, 0, 0);
+                    sc[rt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[rt][1], z, 0, 0, 0);
+                }
+            }
+
+            // Mask keys after a row's position and keys of dropped blocks.
+            if (mask) {
+#pragma unroll
+                for (int rt = 0; rt < kRowTiles; ++rt) {
+                    const int thr = pos[rt] - key0;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (16 * (2 * kp + h) + j > thr || !((valid >> (2 * kp + h)) & 1u))
+                                sc[rt][h][j] = -INFINITY;
+                }
+            }
+
+            // Softmax weights.  They are first taken against the row's
+            // reference maximum as it stands.  Only when some row of the
+            // wavefront has no reference yet, or some lane's 8 weights sum
+            // to more than 2^8 (also true for an overflow to inf), is the
+            // row maximum of these keys computed, the reference moved up to
+            // it (rescaling the output and sum), and the weights taken again
+            // -- then each is at most 1.
+            u32x4 pw[kRowTiles];                              // bf16 pairs of P
 #pragma unroll
             for (int rt = 0; rt < kRowTiles; ++rt) {
-                const int thr = pos[rt] - key0;
+                auto weights = [&](float mu) {
+                    float csum = 0.f;
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
+                    for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (16 * kt + j > thr || !((valid >> kt) & 1u))
-                            sc[rt][kt][j] = -INFINITY;
+                        for (int j = 0; j < 4; j += 2) {
+                            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[rt][h][j], cs, -mu));
+                            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[rt][h][j + 1], cs, -mu));
+                            const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+                            csum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, csum, false);
+                            pw[rt][2 * h + j / 2] = __builtin_bit_cast(unsigned, pp);
+                        }
+                    return csum;
+                };
+                float csum = 0.f;
+                bool fresh = __builtin_amdgcn_ballot_w64(m_ref[rt] == -INFINITY) != 0;
+                if (!fresh) {
+                    csum = weights(m_use[rt]);
+                    fresh = __builtin_amdgcn_ballot_w64(!(csum <= kLaneSumLimit)) != 0;
+                }
+                if (fresh) {
+                    float mx = max2(max2(sc[rt][0][0], sc[rt][0][1]), sc[rt][0][2]);
+                    mx = max2(max2(mx, sc[rt][0][3]), sc[rt][1][0]);
+                    mx = max2(max2(mx, sc[rt][1][1]), sc[rt][1][2]);
+                    mx = max2(mx, sc[rt][1][3]);
+                    const float mc = group_max(mx) * cs;    // the row maximum of these keys
+                    const float m_new = max2(m_ref[rt], mc);
+                    const float alpha = m_new > m_ref[rt] ? __builtin_amdgcn_exp2f(m_ref[rt] - m_new) : 1.f;
+                    m_ref[rt] = m_new;
+                    m_use[rt] = m_new == -INFINITY ? 0.f : m_new;
+                    l_run[rt] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+                        o[rt][dt] *= alpha;
+                    csum = weights(m_use[rt]);
+                }
+                l_run[rt] += csum;
             }
-        }
 
-        // Online softmax per row tile, then P (bf16) into the PV product.
-        bf16x8 pb[kRowTiles][2];
-#pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) {
-            float mx = sc[rt][0][0];
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    mx = fmaxf(mx, sc[rt][kt][j]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[rt], mx * cs);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;   // rows with no key yet
-            const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_use);
-            m_run[rt] = m_new;
-            float lsum = 0.f;
-#pragma unroll
-            for (int kp = 0; kp < 2; ++kp) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float p = __builtin_amdgcn_exp2f(fmaf(sc[rt][2 * kp + h][j], cs, -m_use));
-                        lsum += p;
-                        pb[rt][kp][4 * h + j] = (__bf16)p;
-                    }
-            }
-            l_run[rt] = fmaf(l_run[rt], alpha, lsum);
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-                o[rt][dt] *= alpha;
-        }
-
-        // O^T[dims][rows] += V^T . P^T: V^T lane (dim 16 dt + col, keys of k-slots
-        // 8 lq .. 8 lq + 7) = V[2 kp][dim][4 lq .. 4 lq + 3], V[2 kp + 1][dim][4 lq ..].
-        const char *vb = buf + kChunkBlocks * kTileBytes + col * 64 +
-                         16 * (lq ^ ((col ^ (col >> 2)) & 3));
-#pragma unroll
-        for (int kp = 0; kp < 2; ++kp)
+            // O^T[dims][rows] += V^T . P^T: V^T lane (dim 16 dt + col, keys of
+            // k-slots 8 lq .. 8 lq + 7) = V[2 kp][dim][4 lq .. 4 lq + 3],
+            // V[2 kp + 1][dim][4 lq ..], which is slot lane of the pair's
+            // dimension tile dt.
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
                 const bf16x8 vop = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4 *>(vb + kp * 4096 + dt * 16 * 64));
+                    bf16x8, *reinterpret_cast<const u32x4 *>(vb + kp * 4096 + dt * 1024));
 #pragma unroll
                 for (int rt = 0; rt < kRowTiles; ++rt)
-                    o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[rt][kp], o[rt][dt],
-                                                                        0, 0, 0);
+                    o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        vop, __builtin_bit_cast(bf16x8, pw[rt]), o[rt][dt], 0, 0, 0);
             }
+        }
     }
 
     // Normalise and store: lane holds dims 16 dt + 4 lq .. + 3 of its row.
 #pragma unroll
     for (int rt = 0; rt < kRowTiles; ++rt) {
-        float l = l_run[rt];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = group_sum(l_run[rt]);
         if (!row_ok[rt])
             continue;
         const float inv = l > 0.f ? 1.f / l : 0.f;

@@ -212,6 +212,30 @@ def test_prefill_dropped_blocks(dev, oracle_lib):
         _check(got[r0:r0 + m], ref, f"sequence {s} without block {dropped}", _vmax(pb))
 
 
+@pytest.mark.parametrize("factor", [8.0, 64.0])
+def test_prefill_score_jumps(dev, oracle_lib, factor):
+    """Keys whose scores jump far above everything before them, deep into
+    the context: K at every 97th position is multiplied by `factor` (a power
+    of two, so exact in bf16), and at every 211th by -`factor`.  With 64 a
+    weight taken against the earlier maximum would overflow to inf, so each
+    such key must move the row's reference maximum (and rescale what was
+    accumulated) before its weights enter the sums."""
+    pb = W.make_prefill_batch([0, 300, 0], [700, 400, 129], 80 + int(factor))
+    b = pb.base
+    k = W.bf16_bits_to_float32(b.kv_k)
+    for s in range(b.num_seqs):
+        rows = b.token_rows[s]
+        n = len(rows)
+        k[rows[96:n:97]] *= factor
+        k[rows[210:n:211]] *= -factor
+    b.kv_k[...] = W.round_to_bf16_bits(k)
+    got = _run_gpu(pb, dev, *_gpu_pools(pb, dev))
+    kc, vc = _oracle_pools(oracle_lib, pb)
+    ref = oracle_lib.paged_prefill(pb.q, pb.query_start, kc, vc, b.block_tables,
+                                   pb.context_lens, b.scale)
+    _check(got, ref, f"score jumps x{factor:g}", _vmax(pb))
+
+
 def test_prefill_deterministic_and_block_permutation(dev):
     import torch
     import paged_kv_cache_tv_amd as tv
