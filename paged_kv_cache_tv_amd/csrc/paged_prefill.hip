@@ -16,9 +16,11 @@
 //     every head of the group.  Launch index: K/V head fastest (one XCD per
 //     head, so the tiles of one (sequence, head) share an L2), and the last,
 //     heaviest tiles of every sequence first.
-//   * Keys go in chunks of 64 (4 blocks).  All 512 threads load a chunk's K
-//     and V tiles (16 KiB) into registers one chunk ahead and store them to
-//     LDS, double-buffered, with one barrier per chunk.  K tiles are stored
+//   * Keys go in chunks of 128 (8 blocks).  All 512 threads load a chunk's K
+//     and V tiles (32 KiB) into registers one chunk ahead and store them to
+//     LDS, double-buffered, with one barrier per chunk; each wavefront then
+//     works through the chunk in 32-key halves and stops at the first half
+//     past its last row.  K tiles are stored
 //     verbatim (every 1 KiB operand read contiguous).  V is stored in PV
 //     operand order: one 16-byte slot per (dimension, token group) holding 4
 //     tokens of the dimension from each of two blocks, the slots of one
@@ -74,13 +76,18 @@ constexpr int kWaves = 8;                        // wavefronts per workgroup
 constexpr int kRowTiles = 2;                     // 16-column MFMA tiles per wavefront
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWavesPerSimd = 4;                 // occupancy the register budget is cut for
-constexpr int kChunkBlocks = 4;                  // blocks per key chunk
-constexpr int kChunkKeys = kChunkBlocks * BS;    // 64
+constexpr int kChunkBlocks = 8;                  // blocks per key chunk
+constexpr int kChunkKeys = kChunkBlocks * BS;    // 128
+constexpr int kPairs = kChunkBlocks / 2;         // 32-key halves of a chunk, one block pair each
+constexpr int kLoads = kChunkBlocks * 128 / kThreads;   // 16-byte K pieces (and V slots) per thread
 constexpr int kTileBytes = BS * D * 2;           // one (block, K/V head) tile: 2 KiB
 constexpr int kBufBytes = 2 * kChunkBlocks * kTileBytes;   // K then V of one chunk: 16 KiB
 constexpr float kLaneSumLimit = 256.0f;          // a lane's weights of 32 keys may sum to this
-static_assert(kThreads == kChunkBlocks * 128, "one 16-byte K piece per thread per chunk");
-static_assert(kThreads == (kChunkBlocks / 2) * D * 4, "one 16-byte V slot per thread per chunk");
+static_assert(kLoads * kThreads == kChunkBlocks * 128, "whole 16-byte K pieces per thread");
+static_assert(kLoads * kThreads == kPairs * D * 4, "whole 16-byte V slots per thread");
+static_assert(kThreads % 256 == 0, "a V slot's block pair is the same for a whole wavefront");
+constexpr int kKStep = kThreads / 128;           // blocks whose K pieces one load round covers
+constexpr int kVStep = kThreads / 256;           // block pairs whose V slots one round covers
 
 __device__ __forceinline__ unsigned zero_from(unsigned w, int lim, int e)
 {
@@ -154,7 +161,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
     n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar row ranges
     const int lane = tid & 63;
     const int col = lane & 15;
     const int lq = lane >> 4;
@@ -195,16 +202,17 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
         qop[rt][1] = __builtin_bit_cast(bf16x8, x1);
     }
 
-    // Chunk loading.  K: thread tid moves 16-byte piece tid & 127 of block
-    // kb = tid >> 7's tile.  V: thread tid takes block pair vp = tid >> 8 and
-    // slot u = tid & 255 = (dt, g, c): tokens 4g .. 4g + 3 of dimension
-    // d = 16 dt + c from each block of the pair (8 bytes each), stored as the
-    // 16-byte slot u of the pair's region.  That is exactly the operand lane
-    // (c + 16 g) of the PV product for dimension tile dt reads, so both the
-    // stores and the operand reads cover 1 KiB contiguous per instruction
-    // (conflict-free on gfx950; strided 16-byte reads are not).  kb and vp
-    // are the same for the whole wavefront, so the table entries, validity
-    // and tile addresses are scalar values.
+    // Chunk loading.  K: thread tid moves the 16-byte pieces tid & 127 of the
+    // tiles of blocks kb + kKStep u (kb = tid >> 7, u < kLoads).  V: thread
+    // tid takes slot tid & 255 = (dt, g, c) of block pairs vp + kVStep u
+    // (vp = tid >> 8):
+    // tokens 4g .. 4g + 3 of dimension d = 16 dt + c from each block of the
+    // pair (8 bytes each), stored as one 16-byte slot.  That is exactly the
+    // operand lane (c + 16 g) of the PV product for dimension tile dt reads,
+    // so both the stores and the operand reads cover 1 KiB contiguous per
+    // instruction (conflict-free on gfx950; strided 16-byte reads are not).
+    // kb and vp are the same for the whole wavefront, so the table entries,
+    // validity and tile addresses are scalar values.
     const int kb = __builtin_amdgcn_readfirstlane(tid >> 7);
     const int vp = __builtin_amdgcn_readfirstlane(tid >> 8);
     const int vg = (tid >> 4) & 3;
@@ -221,8 +229,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
     const char *vheads = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * kTileBytes;
     const int64_t block_stride = (int64_t)a.num_kv_heads * kTileBytes;
 
-    u32x4 kpre;
-    u32x2 vpre0, vpre1;
+    u32x4 kpre[kLoads];
+    u32x2 vpre0[kLoads], vpre1[kLoads];
     unsigned valid_next = 0;
     auto entry = [&](int b) -> int32_t { return b * BS < n ? table[b] : -1; };
     auto load_chunk = [&](int c) {
@@ -233,34 +241,40 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
             valid_next |= ((uint32_t)entry(b0 + j) < nb_cap ? 1u : 0u) << j;
         const u32x4 z4 = {0u, 0u, 0u, 0u};
         const u32x2 z2 = {0u, 0u};
-        const int32_t pk = entry(b0 + kb);
-        const int32_t pa = entry(b0 + 2 * vp);
-        const int32_t pb = entry(b0 + 2 * vp + 1);
-        kpre = (uint32_t)pk < nb_cap
-                   ? *reinterpret_cast<const u32x4 *>(kheads + pk * block_stride + k_off)
-                   : z4;
-        vpre0 = (uint32_t)pa < nb_cap
-                    ? *reinterpret_cast<const u32x2 *>(vheads + pa * block_stride + v_off)
-                    : z2;
-        vpre1 = (uint32_t)pb < nb_cap
-                    ? *reinterpret_cast<const u32x2 *>(vheads + pb * block_stride + v_off)
-                    : z2;
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int32_t pk = entry(b0 + kb + kKStep * u);
+            const int32_t pa = entry(b0 + 2 * (vp + kVStep * u));
+            const int32_t pb = entry(b0 + 2 * (vp + kVStep * u) + 1);
+            kpre[u] = (uint32_t)pk < nb_cap
+                          ? *reinterpret_cast<const u32x4 *>(kheads + pk * block_stride + k_off)
+                          : z4;
+            vpre0[u] = (uint32_t)pa < nb_cap
+                           ? *reinterpret_cast<const u32x2 *>(vheads + pa * block_stride + v_off)
+                           : z2;
+            vpre1[u] = (uint32_t)pb < nb_cap
+                           ? *reinterpret_cast<const u32x2 *>(vheads + pb * block_stride + v_off)
+                           : z2;
+        }
     };
     auto store_chunk = [&](int c, char *buf) {
-        *reinterpret_cast<u32x4 *>(buf + k_st) = kpre;
-        u32x2 x0 = vpre0, x1 = vpre1;
-        if (c * kChunkKeys + kChunkKeys > n) {
-            // The chunk holding the context end: V of keys at or past it is
-            // 0 (the slot may hold NaN).
-            const int lim0 = n - ((c * kChunkBlocks + 2 * vp) * BS + 4 * vg);
-            const int lim1 = lim0 - BS;
-            x0[0] = zero_from(x0[0], lim0, 0);
-            x0[1] = zero_from(x0[1], lim0, 2);
-            x1[0] = zero_from(x1[0], lim1, 0);
-            x1[1] = zero_from(x1[1], lim1, 2);
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            *reinterpret_cast<u32x4 *>(buf + k_st + kKStep * u * kTileBytes) = kpre[u];
+            u32x2 x0 = vpre0[u], x1 = vpre1[u];
+            if (c * kChunkKeys + kChunkKeys > n) {
+                // The chunk holding the context end: V of keys at or past it
+                // is 0 (the slot may hold NaN).
+                const int lim0 = n - ((c * kChunkBlocks + 2 * (vp + kVStep * u)) * BS + 4 * vg);
+                const int lim1 = lim0 - BS;
+                x0[0] = zero_from(x0[0], lim0, 0);
+                x0[1] = zero_from(x0[1], lim0, 2);
+                x1[0] = zero_from(x1[0], lim1, 0);
+                x1[1] = zero_from(x1[1], lim1, 2);
+            }
+            const u32x4 slot = {x0[0], x0[1], x1[0], x1[1]};
+            *reinterpret_cast<u32x4 *>(buf + v_st + kVStep * u * 4096) = slot;
         }
-        const u32x4 slot = {x0[0], x0[1], x1[0], x1[1]};
-        *reinterpret_cast<u32x4 *>(buf + v_st) = slot;
     };
 
     f32x4 o[kRowTiles][4];
@@ -289,14 +303,17 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
         if (c * kChunkKeys > wave_last_pos)
             continue;                                        // this wave's rows are done
 
-        // The chunk in two halves of 32 keys (block pair kp = blocks 2 kp and
+        // The chunk in halves of 32 keys (block pair kp = blocks 2 kp and
         // 2 kp + 1): scores, softmax weights, then their PV product, so only
-        // half a chunk of scores and weights is live at a time.
+        // 32 keys of scores and weights are live at a time.
         const int key0 = c * kChunkKeys + 4 * lq;           // this lane's key of slot (kt 0, j 0)
-        const bool mask = c * kChunkKeys + kChunkKeys - 1 > wave_first_pos || valid != 0xFu;
         const char *vb = buf + kChunkBlocks * kTileBytes + 16 * lane;
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
+        for (int kp = 0; kp < kPairs; ++kp) {
+            if (c * kChunkKeys + 32 * kp > wave_last_pos)
+                break;                                       // keys past this wave's rows
+            const bool mask = c * kChunkKeys + 32 * kp + 31 > wave_first_pos ||
+                              ((valid >> (2 * kp)) & 3u) != 3u;
             // Scores of key tiles 2 kp + h.
             f32x4 sc[kRowTiles][2];
 #pragma unroll
