@@ -356,18 +356,32 @@ tv_status tv_paged_attention_reduce(float *out, const float *part_acc,
  * pass and the log-sum-exp merge ("vLLM" page, Flash Attention: the running
  * maximum / running sum rule; a single partition merges to acc / l).
  *
- * When ceil(max_context_len / partition_size) == 1 the partition pass divides
- * by the sum itself and writes out: one launch, and part_acc, part_max and
- * part_sum are not used (they may be NULL).  Otherwise it is
- * tv_paged_attention_decode_append followed by tv_paged_attention_reduce on
- * the same stream: two launches through the workspace.  Either way out is
- * bitwise what those two calls give.  With max_context_len == 0 every row of
- * out is set to zero.
+ * With P = ceil(max_context_len / partition_size) the call takes one of
+ * three forms; all compute the same softmax(q K^T * scale) V per row, and the
+ * form depends only on the shapes, never on the data, so a call is
+ * deterministic:
+ *   P == 1: the partition pass divides by the sum itself and writes out; one
+ *     launch; out is bitwise what tv_paged_attention_decode_append followed
+ *     by tv_paged_attention_reduce gives.
+ *   2 <= P <= 8, num_seqs <= 512 and num_seqs * num_kv_heads within one
+ *     resident wave of workgroups on the device: one launch with one
+ *     workgroup per (sequence, K/V head); each sequence's context is cut
+ *     into 8 equal consecutive ranges (each at most partition_size tokens),
+ *     one per wavefront, and the 8 partial results are merged in on-chip
+ *     memory by the same log-sum-exp rule.  The ranges differ from the
+ *     partition_size partitions of the two-call form, so out equals that
+ *     form's result up to fp32 rounding (a few ulp), not bitwise.
+ *   otherwise: tv_paged_attention_decode_append followed by
+ *     tv_paged_attention_reduce on the same stream, two launches through the
+ *     workspace; out is bitwise what those two calls give.
+ * With max_context_len == 0 every row of out is set to zero.
  *
  *   out        float [num_seqs][num_q_heads][head_dim], 16-byte aligned
  *   part_*     the workspace as for tv_paged_attention_decode (part_acc
- *              16-byte aligned), sized for ceil(max_context_len /
- *              partition_size) partitions; unused with one partition
+ *              16-byte aligned), sized for P partitions; unused (may be NULL)
+ *              with one partition; in the one-launch form for 2 <= P <= 8 it
+ *              is neither read nor written, but must still be non-NULL and
+ *              aligned as stated
  *   other arguments, the append precondition and the odd-data behaviour as
  *   for tv_paged_attention_decode_append
  *
@@ -392,7 +406,7 @@ tv_status tv_paged_attention_decode_step(float *out, float *part_acc, float *par
  * The decode step for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Computes exactly what tv_paged_attention_decode_step computes (out is
- * bitwise the same) and takes the same arguments minus the workspace: the
+ * bitwise the same: the same form is taken for the same shapes) and takes the same arguments minus the workspace: the
  * partition workspace lives in a fixed device array of
  * TV_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from the
  * first such call on that GPU until the process ends.  The call allocates

@@ -75,6 +75,11 @@ constexpr int kTileBytes = BS * D * 2;   // one (block, K/V head) tile: 1024 bf1
 // tokens: 52.7 against 54.6 us).
 template <int SPLIT>
 constexpr int kRingFor = SPLIT > 1 ? 2 : 4;
+// The whole-sequence form: one workgroup per (sequence, K/V head), wavefront
+// p streaming partition p (so at most kSeqWaves partitions), two workgroups
+// per compute unit (4 wavefronts per SIMD, registers capped at 128).
+constexpr int kSeqWaves = 8;
+constexpr int kSeqRing = 2;
 
 struct Tile {
     bf16x8 k0, k1;       // K[token r][8g .. 8g+8), K[token r][32+8g .. 32+8g+8)
@@ -277,6 +282,64 @@ __device__ Unit plan_unit(const DecodeArgs &a, int j, int lane)
     return u;
 }
 
+// The sequence that workgroup k of a K/V head takes in the whole-sequence
+// form: the sequences ordered by tile count (largest first; ties: lower
+// sequence first) and laid along a path that runs forward over the
+// a.plan_width compute units one workgroup of the head is dealt to in turn,
+// then backward in the next round, so that the compute unit that gets a long
+// sequence's workgroup gets a short one's next.  num_seqs <= 64 * kPlanChunks.
+__device__ int seq_unit(const DecodeArgs &a, int k, int lane)
+{
+    const int S = a.num_seqs;
+    const int C = a.plan_width;
+    if (S <= C)
+        return k;                                // one workgroup of the head per compute unit
+    int tiles[kPlanChunks];
+#pragma unroll
+    for (int kk = 0; kk < kPlanChunks; ++kk) {
+        const int s = kk * 64 + lane;
+        int n = s < S ? a.context_lens[s] : 0;
+        n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
+        tiles[kk] = s < S ? (n + BS - 1) / BS : -1;   // -1: no sequence
+    }
+    const int r = k / C, c = k - r * C;
+    const int round_end = min(S, (r + 1) * C) - r * C;         // workgroups in this round
+    const int t = r * C + ((r & 1) ? round_end - 1 - c : c);
+    auto count_ge = [&](int b) {
+        int cnt = 0;
+#pragma unroll
+        for (int kk = 0; kk < kPlanChunks; ++kk)
+            if (kk * 64 < S)                     // only the chunks that hold sequences
+                cnt += (int)__popcll(__ballot(tiles[kk] >= b));
+        return cnt;
+    };
+    // The t-th largest tile count b, then the right sequence among those of b.
+    int blo = 0, bhi = (a.max_context_len + BS - 1) / BS;
+    while (blo < bhi) {
+        const int mid = (blo + bhi + 1) >> 1;
+        if (count_ge(mid) > t)
+            blo = mid;
+        else
+            bhi = mid - 1;
+    }
+    int rank = t - count_ge(blo + 1);
+    int s = 0;
+#pragma unroll
+    for (int kk = 0; kk < kPlanChunks; ++kk) {
+        if (kk * 64 >= S)
+            break;
+        uint64_t m = __ballot(tiles[kk] == blo);
+        const int cnt = (int)__popcll(m);
+        if (rank >= 0 && rank < cnt) {
+            for (int i = 0; i < rank; ++i)
+                m &= m - 1;                      // drop the lowest set lanes
+            s = kk * 64 + (int)__builtin_ctzll(m);
+        }
+        rank -= cnt;
+    }
+    return s;
+}
+
 // APPEND: sequence s also brings a new token (k_new, v_new) for slot
 // slot_mapping[s].  The workgroup holding the sequence's last partition writes
 // the token's K/V of its head into the pools, and -- when that slot is the one
@@ -303,10 +366,16 @@ __device__ Unit plan_unit(const DecodeArgs &a, int j, int lane)
 // equally.
 //
 // decode_unit is the work of one workgroup; `bid` is its index in its pass.
-template <bool APPEND, bool SHARED, bool PLAN, int SPLIT>
+//
+// SEQ (the whole-sequence form, SPLIT == kSeqWaves): the workgroup holds all
+// of one (sequence, K/V head) and wavefront w attends to partition w, a whole
+// 512-token partition of its own; the partitions' triples are merged in LDS
+// exactly as the split ranges above are, and wavefront 0 writes out = acc / l
+// (part_acc then holds the output, with one partition in its layout).
+template <bool APPEND, bool SHARED, bool PLAN, int SPLIT, bool SEQ = false>
 __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
 {
-    constexpr int kRing = kRingFor<SPLIT>;
+    constexpr int kRing = SEQ ? kSeqRing : kRingFor<SPLIT>;
     const int lane = (int)(threadIdx.x & 63);
     const int wv = (int)(threadIdx.x >> 6);       // wavefront in the workgroup
     const int kvh = (int)(bid % (unsigned)a.num_kv_heads);
@@ -314,6 +383,17 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
     const int units = SHARED ? a.num_groups : a.num_seqs;
     int part = rest / units;
     int s = rest % units;                      // SHARED: the group; the sequence below
+    int ptiles = a.part_tiles;                 // tiles per unit
+    if (SEQ) {
+        // The sequence's tiles in kSeqWaves equal consecutive ranges, one per
+        // wavefront (at most part_tiles each, as the launch requires
+        // max_context_len <= kSeqWaves * partition_size).
+        s = seq_unit(a, rest, lane);
+        part = wv;
+        int ns = a.context_lens[s];
+        ns = ns < 0 ? 0 : (ns > a.max_context_len ? a.max_context_len : ns);
+        ptiles = max(1, ((ns + BS - 1) / BS + kSeqWaves - 1) / kSeqWaves);
+    }
     if (PLAN) {
         const Unit u = plan_unit(a, rest, lane);
         if (u.s < 0)
@@ -360,18 +440,18 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
     // many of them are used: entry l of the partition in lane l.  The row
     // holds them: part * part_tiles < max_blocks since max_context_len <=
     // max_blocks * block_size.
-    const bool table_ahead = a.part_tiles <= 64;
-    const int64_t row0 = (int64_t)s * a.max_blocks + (int64_t)part * a.part_tiles;
+    const bool table_ahead = ptiles <= 64;
+    const int64_t row0 = (int64_t)s * a.max_blocks + (int64_t)part * ptiles;
     const int32_t ahead_lane =
-        table_ahead && lane < min(a.part_tiles, a.max_blocks - part * a.part_tiles)
+        table_ahead && lane < min(ptiles, a.max_blocks - part * ptiles)
             ? a.block_tables[row0 + lane]
             : 0;
     if (!SHARED) {
         n = a.context_lens[s];
         n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
     }
-    const int first_tok = part * a.part_tiles * BS;
-    if (first_tok >= n) {
+    const int first_tok = part * ptiles * BS;
+    if (!SEQ && first_tok >= n) {
         if (a.normalize && threadIdx.x < 64) {
             // An empty context with the only partition: its rows of the
             // output are 0 (the merge of no partition).  The plain order is
@@ -383,7 +463,8 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
         }
         return;
     }
-    const int ptok = min(n - first_tok, a.part_tiles * BS);    // tokens in this partition
+    // Tokens in this partition (SEQ: 0 for a wavefront past the sequence's end).
+    const int ptok = max(0, min(n - first_tok, ptiles * BS));
     const int ntiles = (ptok + BS - 1) / BS;
 
     const int r = lane & 15;
@@ -406,7 +487,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
 
     // This wavefront's tiles of the partition: [t_lo, t_hi).
     int t_lo = 0, t_hi = ntiles;
-    if (SPLIT > 1) {
+    if (SPLIT > 1 && !SEQ) {
         const int per = (ntiles + SPLIT - 1) / SPLIT;
         t_lo = min(ntiles, wv * per);
         t_hi = min(ntiles, t_lo + per);
@@ -462,8 +543,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
     for (int j = 0; j < 4; ++j)
         o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int32_t *bt = a.block_tables + (int64_t)s * a.max_blocks + (int64_t)part * a.part_tiles +
-                        t_lo;
+    const int32_t *bt = a.block_tables + (int64_t)s * a.max_blocks + (int64_t)part * ptiles + t_lo;
     const char *kpool = reinterpret_cast<const char *>(a.k_cache) + (int64_t)kvh * kTileBytes;
     const char *vpool = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * kTileBytes;
     const int64_t tile_stride = (int64_t)a.num_kv_heads * kTileBytes;
@@ -626,6 +706,15 @@ void paged_decode_kernel(DecodeArgs a)
     decode_unit<APPEND, SHARED, PLAN, SPLIT>(a, blockIdx.x);
 }
 
+// The whole-sequence form: one workgroup of kSeqWaves wavefronts per
+// (sequence, K/V head), two per compute unit.
+template <bool APPEND>
+__global__ __launch_bounds__(64 * kSeqWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void paged_decode_seq_kernel(DecodeArgs a)
+{
+    decode_unit<APPEND, false, false, kSeqWaves, true>(a, blockIdx.x);
+}
+
 // A shared-prefix launch in one grid: workgroups [0, shared_groups) take the
 // group pass, the rest the per-sequence pass.  The two passes read disjoint
 // partitions and write disjoint partials, so one grid lets each fill the
@@ -675,6 +764,29 @@ DeviceShape device_shape()
     return {cus, per_cu};
 }
 
+// Workgroups of the whole-sequence kernel one compute unit holds at once
+// (cached per device; 0 if unknown).
+int seq_wgs_per_cu()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 0;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(paged_decode_seq_kernel<true>), 64 * kSeqWaves,
+            0) != hipSuccess)
+        return 0;
+    if (dev < 64)
+        cache[dev].store(per_cu, std::memory_order_relaxed);
+    return per_cu;
+}
+
 template <bool APPEND, bool SHARED, bool PLAN, int SPLIT>
 void launch(const DecodeArgs &a, int64_t groups, hipStream_t stream)
 {
@@ -703,6 +815,39 @@ void launch(const DecodeArgs &a, int64_t groups, hipStream_t stream)
 //     against 8.2 us), so small grids keep the plain order.
 // The shared-prefix launch takes the split its per-sequence grid would get,
 // so its partitions round exactly as the per-sequence pass's do.
+// The whole-sequence form serves a step whose contexts span 2 .. kSeqWaves
+// partitions of at most 64 blocks, with every (sequence, K/V head) workgroup
+// resident at once (at most wgs_per_cu * CUs of them: one round, so that the
+// order of seq_unit pairs long and short sequences on each compute unit) and
+// at most 64 * kPlanChunks sequences.
+bool paged_decode_seq_fits(const DecodeArgs &a)
+{
+    if (a.shared_len || a.num_parts < 2 || a.num_parts > kSeqWaves || a.part_tiles > 64 ||
+        a.num_seqs > 64 * kPlanChunks)
+        return false;
+    const DeviceShape dev = device_shape();
+    const int per_cu = seq_wgs_per_cu();
+    return dev.cus > 0 && per_cu > 0 &&
+           (int64_t)a.num_seqs * a.num_kv_heads <= (int64_t)per_cu * dev.cus;
+}
+
+// The whole decode step in one launch (a.part_acc = out); requires
+// paged_decode_seq_fits(a).
+hipError_t launch_paged_decode_seq(const DecodeArgs &args, hipStream_t stream)
+{
+    DecodeArgs a = args;
+    const DeviceShape dev = device_shape();
+    a.plan_width = dev.cus / std::gcd(a.num_kv_heads, dev.cus);
+    a.num_parts = 1;                         // out's layout: one "partition" per (sequence, head)
+    a.normalize = 1;
+    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads));
+    if (a.k_new)
+        hipLaunchKernelGGL(paged_decode_seq_kernel<true>, grid, dim3(64 * kSeqWaves), 0, stream, a);
+    else
+        hipLaunchKernelGGL(paged_decode_seq_kernel<false>, grid, dim3(64 * kSeqWaves), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_paged_decode(const DecodeArgs &args, hipStream_t stream)
 {
     DecodeArgs a = args;

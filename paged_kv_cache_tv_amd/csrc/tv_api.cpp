@@ -412,6 +412,15 @@ tv_status tv_paged_attention_decode_step(float *out, float *part_acc, float *par
         a.normalize = 1;
         return from_hip(tv::launch_paged_decode(a, hs));
     }
+    if (tv::paged_decode_seq_fits(a)) {
+        // Every (sequence, K/V head) in one resident workgroup whose
+        // wavefronts take one partition each and merge in LDS: one launch,
+        // the workspace unused.
+        a.part_acc = out;
+        a.part_max = nullptr;
+        a.part_sum = nullptr;
+        return from_hip(tv::launch_paged_decode_seq(a, hs));
+    }
     const tv_status sd = from_hip(tv::launch_paged_decode(a, hs));
     if (sd != TV_OK)
         return sd;

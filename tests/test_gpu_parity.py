@@ -106,19 +106,73 @@ def _call_step(db):
     return got.cpu().numpy()
 
 
+# Workloads the one call serves in the whole-sequence form (2 to 8 partitions,
+# every (sequence, K/V head) workgroup resident at once): 8 x U[128, 1024] and
+# 64 x U[512, 4096].  Workload 1 fits one partition; workloads 4 (2048
+# (sequence, head) pairs) and 5 (256 partitions) take the two launches.
+_WHOLE_SEQUENCE_WORKLOADS = (2, 3)
+
+
 @pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
 def test_decode_step_call_workloads(dev, oracle_lib, index):
-    """Full workloads through tv_paged_attention_decode_step (workload 1's 37
-    tokens fit one partition: a single launch): output bitwise the two-launch
-    step's, pools bit-exact against the oracle's cache write."""
+    """Full workloads through tv_paged_attention_decode_step: pools bit-exact
+    against the oracle's cache write, output within the bars and run-to-run
+    identical.  Where the call takes the one-partition launch or the two
+    launches, the output is the two-launch step's bit for bit; in the
+    whole-sequence form each context is split into 8 equal ranges instead of
+    the workspace's 512-token partitions (none longer than a partition), so
+    the two agree to rounding (2e-6)."""
     batch = W.make_workload(index)
     ref, kc_ref, vc_ref = _oracle_step(oracle_lib, ("workload", index), batch)
     two, db = _gpu_step(batch, dev, fused=True)
     got = _call_step(db)
-    assert np.array_equal(got, two), f"workload {index}: one call differs from two launches"
+    assert np.array_equal(got, _call_step(db)), f"workload {index}: two calls differ"
+    if index in _WHOLE_SEQUENCE_WORKLOADS:
+        assert np.abs(got - two).max() <= 2e-6, f"workload {index}: one call far from two launches"
+    else:
+        assert np.array_equal(got, two), f"workload {index}: one call differs from two launches"
     kc, vc = db.pools_numpy()
     assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
     _assert_close(got, ref, f"workload {index}, one call")
+
+
+_WHOLE_SEQUENCE_CASES = [
+    # (seed, lengths or (count, low, high), query heads, K/V heads, partition, host bound)
+    (80, [0, 1, 2, 15, 16, 17, 511, 512, 513, 1023, 1024, 1025, 4095, 4096], 32, 8, 512, None),
+    (81, (64, 513, 4096), 32, 8, 512, 4096),         # loose host bound: 8 partitions
+    (82, (200, 1, 600), 16, 2, 128, 1000),           # 400 (sequence, head) pairs, 8 partitions
+    (83, (256, 0, 300), 8, 1, 64, 500),              # 256 sequences, one K/V head
+    (84, (9, 1, 2048), 16, 1, 512, None),            # the largest group (16 query heads)
+    (85, (40, 1, 1000), 8, 8, 256, None),            # one query head per K/V head
+    (86, (3, 3000, 4000), 32, 8, 1024, None),        # 4 partitions of 1024
+]
+
+
+@pytest.mark.parametrize("case", _WHOLE_SEQUENCE_CASES, ids=[f"seed{c[0]}" for c in _WHOLE_SEQUENCE_CASES])
+def test_decode_step_whole_sequence_form(dev, oracle_lib, case):
+    """The one-launch whole-sequence form across its range: empty and
+    one-token contexts, lengths at tile and partition edges, group sizes 1 to
+    16, partition sizes 64 to 1024, up to 256 sequences and 512 (sequence,
+    head) workgroups: pools bit-exact against the oracle's, output within the
+    bars, run-to-run identical, and within rounding of the two-launch step."""
+    seed, lens, hq, hkv, part, bound = case
+    if isinstance(lens, tuple):
+        n_seq, lo, hi = lens
+        lens = np.random.default_rng(seed).integers(lo, hi, size=n_seq, endpoint=True)
+    lens = np.asarray(lens)
+    mc = int(lens.max()) if bound is None else bound
+    assert 2 <= -(-mc // part) <= 8 and len(lens) * hkv <= 512
+    batch = W.make_batch(lens, seed, num_q_heads=hq, num_kv_heads=hkv, table_width=mc // 16 + 1)
+    ref, kc_ref, vc_ref = O.decode_step(oracle_lib, batch)
+    two, db = _gpu_step(batch, dev, partition_size=part, max_context_len=mc, fused=True)
+    got = _call_step(db)
+    assert np.array_equal(got, _call_step(db)), "two calls differ"
+    assert np.abs(got - two).max() <= 2e-6, "one call far from the two-launch step"
+    assert not got[lens == 0].any(), "empty contexts must give zero rows"
+    kc, vc = db.pools_numpy()
+    assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+    _assert_close(got, ref, f"whole-sequence form, {len(lens)} sequences, {hq}/{hkv} heads, "
+                            f"partition {part}, host bound {mc}")
 
 
 _ONE_PARTITION = [

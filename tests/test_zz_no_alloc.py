@@ -58,25 +58,30 @@ def _check(ref, got, oracle_out, what):
 
 
 def test_noalloc_step_matches_existing_call_twice(dev, oracle_lib):
-    """Two calls in a row: batch 64 x U[512, 4096] (8 partitions), then the
-    smaller batch 8 x U[128, 1024] (2 partitions), then one 37-token
-    sequence (one partition: no workspace)."""
+    """Calls in a row whose steps go through the workspace (partition pass,
+    then the merge kernel): batch 64 x U[512, 4096] in 16 partitions of 256
+    tokens (4.3 MB of the array), then the smaller batch 8 x U[128, 1024] in
+    16 partitions of 64 (0.5 MB), then one 37-token sequence (one partition:
+    no workspace).  The 512-token partitions of the first two workloads take
+    the one-launch whole-sequence form, which needs no workspace at all: run
+    last, it must match too."""
     import oracle as O
     from paged_kv_cache_tv_amd.step import DeviceBatch
-    for idx in (3, 2, 1):
+    for idx, part in ((3, 256), (2, 64), (1, 512), (3, 512), (2, 512)):
         batch = W.make_workload(idx)
-        print(f"workload {idx}: {batch.name}", flush=True)
-        db = DeviceBatch(batch, dev)
+        print(f"workload {idx}: {batch.name}, partition {part}", flush=True)
+        db = DeviceBatch(batch, dev, partition_size=part)
         db.fill()
         ref, got = _pair(db, dev)
         want, _, _ = O.decode_step(oracle_lib, batch)
-        _check(ref, got, want, batch.name)
+        _check(ref, got, want, f"{batch.name} partition {part}")
         del db
 
 
 def test_noalloc_partition_sizes(dev, oracle_lib):
     """The same batch under partition sizes that change the workspace's shape
-    (and so where each row lands in the array): 16, 64 and 512 tokens."""
+    (and so where each row lands in the array): 16 and 64 tokens, and 512
+    (the one-launch form, no workspace)."""
     import oracle as O
     from paged_kv_cache_tv_amd.step import DeviceBatch
     batch = W.make_workload(2)
