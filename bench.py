@@ -4,11 +4,14 @@
 
 One step = the whole path for one attention layer of a decode step: cache
 write of the batch's new tokens, partition pass and merge.  By default the
-step is two launches -- tv_paged_attention_decode_append (cache write folded
-into the partition pass) and tv_paged_attention_reduce; ``--step separate``
-times the three-launch form (tv_cache_write, tv_paged_attention_decode,
-tv_paged_attention_reduce), which is also reported alongside.  The
-default workload is batch 64 with ragged contexts drawn from U[512, 4096]
+step is one library call, tv_paged_attention_decode_step; on the default
+workload it is one launch (one workgroup per (sequence, K/V head): cache
+write, attention over the whole context and the merge in one kernel).
+``--step fused`` times the two-launch form (tv_paged_attention_decode_append,
+cache write folded into the partition pass, then tv_paged_attention_reduce)
+and ``--step separate`` the three-launch form (tv_cache_write,
+tv_paged_attention_decode, tv_paged_attention_reduce); both are also
+reported alongside.  The default workload is batch 64 with ragged contexts drawn from U[512, 4096]
 (32 query heads, 8 K/V heads, head_dim 64, bf16, 16-token blocks, 512-token
 partitions), built from a fixed seed.
 
@@ -66,12 +69,12 @@ def source_digest(path: str) -> str:
     return hashlib.sha256(text.encode("utf-8")).hexdigest()
 
 
-def measured_traffic(workload_name: str, kernel: str):
+def measured_traffic(workload_name: str, kernel: str, path=None):
     """HBM bytes per launch of ``kernel`` from the committed counter record, or
     None when there is no record for this kernel and workload or the kernel
     source changed since."""
     try:
-        with open(TRAFFIC_RECORD) as f:
+        with open(path or TRAFFIC_RECORD) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -81,6 +84,98 @@ def measured_traffic(workload_name: str, kernel: str):
         return None
     w = rec.get("workloads", {}).get(workload_name)
     return None if w is None else w.get("hbm_bytes_per_launch")
+
+
+# rocprofv3 kernel-name fragments of the kernels a traffic record can cover,
+# by the name bench.py reports in roofline.kernel.
+TRAFFIC_KERNELS = {"paged_decode_seq_kernel<append>": "paged_decode_seq_kernel<true>",
+                   "paged_decode_kernel<append>": "paged_decode_kernel<true, false, true"}
+
+
+def _counter_rows(path, counter):
+    """{rocprof kernel name: [counter value per dispatch]} from one
+    --pmc pass's *_counter_collection.csv files under ``path``."""
+    import csv
+    import glob
+    out = {}
+    files = sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {path}")
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def write_traffic_record(prof_dir, workload, partition_size, out_path=None):
+    """Turn four rocprofv3 passes into TRAFFIC_RECORD: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) of the step's dominant kernel on
+    ``workload``, each scaled by what the same counter reads for a plain 1 GiB
+    device copy (``--copy-calibration``).  The passes, each its own run:
+
+      rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -- python bench.py --steps 3
+          --warmup 1 --no-cpu-baseline --no-prefill --no-block-copy --no-workloads
+      rocprofv3 --pmc WRITE_SIZE ... -d DIR/write -- (the same bench command)
+      rocprofv3 --pmc FETCH_SIZE ... -d DIR/copy_fetch -- python bench.py --copy-calibration
+      rocprofv3 --pmc WRITE_SIZE ... -d DIR/copy_write -- python bench.py --copy-calibration
+    """
+    import statistics as st
+    from paged_kv_cache_tv_amd import workloads as W
+    batch = W.make_workload(workload)
+    fetch = _counter_rows(os.path.join(prof_dir, "fetch"), "FETCH_SIZE")
+    write = _counter_rows(os.path.join(prof_dir, "write"), "WRITE_SIZE")
+    copy_f = _counter_rows(os.path.join(prof_dir, "copy_fetch"), "FETCH_SIZE")
+    copy_w = _counter_rows(os.path.join(prof_dir, "copy_write"), "WRITE_SIZE")
+
+    def copy_kib(rows):            # the 1 GiB copies are the largest dispatches
+        vals = sorted(v for vs in rows.values() for v in vs)
+        return st.median(vals[-5:])
+
+    f1, w1 = copy_kib(copy_f), copy_kib(copy_w)
+    fetch_scale = COPY_CALIBRATION_BYTES / 1024 / f1
+    write_scale = COPY_CALIBRATION_BYTES / 1024 / w1
+    for kernel, frag in TRAFFIC_KERNELS.items():
+        names = [n for n in fetch if frag in n]
+        if names:
+            break
+    else:
+        raise ValueError("no decode kernel in the FETCH_SIZE pass")
+    full = names[0]
+    fv, wv = st.mean(fetch[full]), st.mean(write[full])
+    rb, wb = int(fv * 1024 * fetch_scale), int(wv * 1024 * write_scale)
+    dec_bytes, step_bytes, write_bytes = algorithmic_bytes(batch)
+    algo = step_bytes if kernel == "paged_decode_seq_kernel<append>" else dec_bytes + write_bytes
+    rec = {
+        "kernel": kernel,
+        "rocprof_kernel_name": full,
+        "kernel_source": os.path.relpath(DECODE_SOURCE, ROOT),
+        "kernel_source_sha256": source_digest(DECODE_SOURCE),
+        "note": "HBM bytes per launch of the decode step's dominant kernel = FETCH_SIZE * "
+                "fetch_scale + WRITE_SIZE * write_scale (KiB -> bytes); the scales come from a "
+                "plain 1 GiB device copy under the same counters.  bench.py reports this as "
+                "roofline.traffic only while the kernel source, comments and blank space "
+                "removed, still has this hash (bench.source_digest).  Written by "
+                "python bench.py --traffic-from DIR --workload N.",
+        "copy_calibration": {"bytes": COPY_CALIBRATION_BYTES, "FETCH_SIZE_KiB": round(f1, 1),
+                             "WRITE_SIZE_KiB": round(w1, 1), "fetch_scale": round(fetch_scale, 4),
+                             "write_scale": round(write_scale, 4)},
+        "workloads": {batch.name: {
+            "partition_size": partition_size,
+            "FETCH_SIZE_KiB_per_launch": round(fv, 1),
+            "WRITE_SIZE_KiB_per_launch": round(wv, 1),
+            "hbm_read_bytes_per_launch": rb,
+            "hbm_write_bytes_per_launch": wb,
+            "hbm_bytes_per_launch": rb + wb,
+            "dispatches_averaged": len(fetch[full]),
+            "algorithmic_bytes_per_launch": algo,
+            "traffic_over_algorithmic": round((rb + wb) / algo, 4)}},
+    }
+    with open(out_path or TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
 
 
 def algorithmic_bytes(batch):
@@ -160,7 +255,8 @@ def prefill_rate(tv, dev, stream, flush, steps, index=3):
     `index` (default: 8 prompts of 2048 tokens, full prefill).  The prompts'
     K/V are written into fresh pools with tv_cache_write first; each timed
     launch follows a cache eviction and is bracketed by its own pair of
-    events.  FLOPs counted: 2 x 2 x head_dim per (query head, query, key)
+    events; the figure is the median launch (mean, min and max beside it).
+    FLOPs counted: 2 x 2 x head_dim per (query head, query, key)
     pair the causal mask keeps (QK^T and PV)."""
     import numpy as np
     import torch
@@ -197,13 +293,19 @@ def prefill_rate(tv, dev, stream, flush, steps, index=3):
         launch()
         e1.record(stream)
     torch.cuda.synchronize()
-    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+    each = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    ms = float(np.median(each))
     flops = pb.causal_flops()
     tflops = flops / (ms * 1e-3) / 1e12
     finite = bool(torch.isfinite(out).all().item())
     del kc, vc, out
     return {"workload": pb.name, "kernel": "paged_prefill_kernel<4>", "rows": pb.num_rows,
             "flops_per_launch": flops, "us_per_launch": round(ms * 1e3, 2),
+            "us_per_launch_stats": {"median": round(ms * 1e3, 2),
+                                    "mean": round(float(each.mean()) * 1e3, 2),
+                                    "min": round(float(each.min()) * 1e3, 2),
+                                    "max": round(float(each.max()) * 1e3, 2),
+                                    "launches": int(len(each))},
             "TFLOP_per_s": round(tflops, 1), "output_finite": finite,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -458,8 +560,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--partition-size", type=int, default=512)
-    ap.add_argument("--step", choices=["fused", "separate"], default="fused",
-                    help="two launches (write folded into the partition pass) or three")
+    ap.add_argument("--step", choices=["call", "fused", "separate"], default="call",
+                    help="one library call (tv_paged_attention_decode_step), two launches "
+                         "(write folded into the partition pass) or three")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill attention measurement")
@@ -472,7 +575,15 @@ def main(argv=None):
     ap.add_argument("--lib", default=None, help="load libtv from this path instead of the package")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain device-to-device copies of 1 GiB (counter calibration)")
+    ap.add_argument("--traffic-from", metavar="DIR", default=None,
+                    help="write the traffic record from rocprofv3 FETCH_SIZE / WRITE_SIZE passes "
+                         "under DIR (fetch/, write/, copy_fetch/, copy_write/) and exit")
     args = ap.parse_args(argv)
+
+    if args.traffic_from:
+        rec = write_traffic_record(args.traffic_from, args.workload, args.partition_size)
+        print(json.dumps(rec), flush=True)
+        return 0
 
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the decode step is "
@@ -520,13 +631,17 @@ def main(argv=None):
         if not args.no_flush:
             flush_buf.sum()
 
-    fused = args.step == "fused"
-    run_step = (lambda: db.fused_step(stream)) if fused else (lambda: db.step(stream))
-    other_step = (lambda: db.step(stream)) if fused else (lambda: db.fused_step(stream))
+    form = tv.decode_step_form(batch.num_seqs, batch.num_q_heads, batch.num_kv_heads,
+                               batch.head_dim, batch.block_size, db.max_context_len,
+                               db.partition_size)
+    steps = {"call": lambda: db.call_step(stream),
+             "fused": lambda: db.fused_step(stream),
+             "separate": lambda: db.step(stream)}
+    run_step = steps[args.step]
     for i in range(args.warmup):
-        flush(i)
-        run_step()
-        other_step()
+        for f in steps.values():
+            flush(i)
+            f()
     torch.cuda.synchronize()
 
     def timed_loop(body, k):
@@ -548,32 +663,33 @@ def main(argv=None):
     t_flush_step = timed_loop(lambda i: (flush(i), run_step()), K)
     wall = time.perf_counter() - wall0
     t_flush = timed_loop(flush, K)
-    t_flush_other = timed_loop(lambda i: (flush(i), other_step()), K)
+    t_flush_forms = {name: timed_loop(lambda i, f=f: (flush(i), f()), K)
+                     for name, f in steps.items()}
     t_flush_write = timed_loop(lambda i: (flush(i), db.write_step(stream)), K)
     t_flush_decode = timed_loop(lambda i: (flush(i), db.decode(stream)), K)
     t_flush_append = timed_loop(lambda i: (flush(i), db.decode_append(stream)), K)
     t_flush_reduce = timed_loop(lambda i: (flush(i), db.reduce(stream)), K)
-    t_flush_call = timed_loop(lambda i: (flush(i), db.call_step(stream)), K)
     if args.no_flush:
         t_flush = 0.0
     step_ms_cold = t_flush_step - t_flush
-    other_ms = t_flush_other - t_flush
+    forms_ms = {name: t - t_flush for name, t in t_flush_forms.items()}
     decode_ms = t_flush_decode - t_flush
     append_ms = t_flush_append - t_flush
     write_ms = t_flush_write - t_flush
     reduce_ms = t_flush_reduce - t_flush
-    call_ms = t_flush_call - t_flush
+    call_ms = forms_ms["call"]
 
     # Hot cache: the same steps back to back with no eviction in between.
     hot_steps = max(10, K)
     hot_ms = timed_loop(lambda i: run_step(), hot_steps)
-    hot_decode_ms = timed_loop(lambda i: (db.decode_append(stream) if fused else db.decode(stream)),
-                               hot_steps)
+    hot_decode_ms = timed_loop(lambda i: (db.decode(stream) if args.step == "separate"
+                                          else db.decode_append(stream)), hot_steps)
 
     # Isolated launches: events around every kernel of every step (adds the
-    # event/dispatch latency of each boundary; reported for reference).
-    kernels = ([db.decode_append, db.reduce] if fused
-               else [db.write_step, db.decode, db.reduce])
+    # event/dispatch latency of each boundary; reported for reference).  The
+    # one call is bracketed whole.
+    kernels = {"call": [db.call_step], "fused": [db.decode_append, db.reduce],
+               "separate": [db.write_step, db.decode, db.reduce]}[args.step]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
           for _ in range(K)]
     torch.cuda.synchronize()
@@ -585,7 +701,7 @@ def main(argv=None):
             kern(stream)
             e[j + 1].record(stream)
     torch.cuda.synchronize()
-    main = 0 if fused else 1                      # the partition pass among the launches
+    main = 1 if args.step == "separate" else 0   # the partition pass among the launches
     iso_step = np.array([e[0].elapsed_time(e[-1]) for e in ev])
     iso_decode = np.array([e[main].elapsed_time(e[main + 1]) for e in ev])
 
@@ -596,10 +712,16 @@ def main(argv=None):
     dec_bytes, step_bytes, write_bytes = algorithmic_bytes(batch)
     ms = float(step_ms_cold)
     value = step_bytes / (ms * 1e-3) / 1e9
-    if fused:
-        roof_kernel, roof_bytes, roof_ms = "paged_decode_kernel<append>", dec_bytes + write_bytes, append_ms
-    else:
+    # The dominant kernel of the timed step, with the algorithmic bytes it
+    # moves per launch.
+    if args.step == "call" and form == 2:
+        roof_kernel, roof_bytes, roof_ms = "paged_decode_seq_kernel<append>", step_bytes, ms
+    elif args.step == "call" and form == 1:
+        roof_kernel, roof_bytes, roof_ms = "paged_decode_kernel<append>", step_bytes, ms
+    elif args.step == "separate":
         roof_kernel, roof_bytes, roof_ms = "paged_decode_kernel", dec_bytes, decode_ms
+    else:
+        roof_kernel, roof_bytes, roof_ms = "paged_decode_kernel<append>", dec_bytes + write_bytes, append_ms
     roof_gbs = roof_bytes / (roof_ms * 1e-3) / 1e9
 
     # The plain-read yardstick: tv_stream_read over as many bytes as the
@@ -643,13 +765,13 @@ def main(argv=None):
         "seq_tokens_per_s": round(batch.total_tokens / (ms * 1e-3), 1),
         "decode_tokens_per_s": round(batch.num_seqs / (ms * 1e-3), 1),
         "step_bytes": step_bytes,
-        "step": "two launches: decode_append + reduce" if fused else
-                "three launches: cache_write + decode + reduce",
-        "other_step_us": round(other_ms * 1e3, 2),
-        "one_call_step_us": round(call_ms * 1e3, 2),
-        "one_call_step": ("one launch (the pass divides by the sum itself)"
-                          if db.max_context_len <= db.partition_size
-                          else "two launches inside tv_paged_attention_decode_step"),
+        "step": {"call": "one call, tv_paged_attention_decode_step: "
+                         + tv.DECODE_STEP_FORMS.get(form, str(form)),
+                 "fused": "two launches: decode_append + reduce",
+                 "separate": "three launches: cache_write + decode + reduce"}[args.step],
+        "steps_us": {"one_call": round(forms_ms["call"] * 1e3, 2),
+                     "two_launch": round(forms_ms["fused"] * 1e3, 2),
+                     "three_launch": round(forms_ms["separate"] * 1e3, 2)},
         "kernels_us": {"cache_write": round(write_ms * 1e3, 2),
                        "paged_decode": round(decode_ms * 1e3, 2),
                        "paged_decode_append": round(append_ms * 1e3, 2),

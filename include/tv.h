@@ -403,6 +403,25 @@ tv_status tv_paged_attention_decode_step(float *out, float *part_acc, float *par
                                          float scale, void *stream);
 
 /*
+ * Which form tv_paged_attention_decode_step (and its _noalloc variant) takes
+ * for these shapes on the current device, with
+ * P = ceil(max_context_len / partition_size):
+ *   0  nothing is launched (num_seqs == 0 or max_context_len == 0)
+ *   1  one launch, one partition (P == 1)
+ *   2  one launch, one workgroup per (sequence, K/V head) (2 <= P <= 8 and
+ *      the grid fits one resident wave of workgroups)
+ *   3  two launches through the workspace
+ *  -1  the step would reject these shapes (TV_ERR_SHAPE or
+ *      TV_ERR_UNSUPPORTED)
+ * Host-only; reads the current device's compute-unit count and occupancy
+ * (the first call on a device queries the runtime).  Launches nothing.
+ */
+int32_t tv_paged_attention_decode_step_form(int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t block_size, int32_t max_context_len,
+                                            int32_t partition_size);
+
+/*
  * The decode step for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Computes exactly what tv_paged_attention_decode_step computes (out is

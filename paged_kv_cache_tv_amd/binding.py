@@ -44,6 +44,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_status_string.argtypes = [ctypes.c_int]
     lib.tv_num_partitions.restype = i32
     lib.tv_num_partitions.argtypes = [i32, i32]
+    lib.tv_paged_attention_decode_step_form.restype = i32
+    lib.tv_paged_attention_decode_step_form.argtypes = [i32] * 7
     lib.tv_cache_write.restype = ctypes.c_int
     lib.tv_cache_write.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, vp]
     lib.tv_paged_attention_decode.restype = ctypes.c_int
@@ -152,6 +154,20 @@ def _need(t, name, *, itemsize=None, dtype=None, ndim=None):
 
 def num_partitions(max_context_len: int, partition_size: int) -> int:
     return int(lib().tv_num_partitions(int(max_context_len), int(partition_size)))
+
+
+DECODE_STEP_FORMS = {0: "nothing launched", 1: "one launch, one partition",
+                     2: "one launch, one workgroup per (sequence, K/V head)",
+                     3: "two launches through the workspace"}
+
+
+def decode_step_form(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                     block_size: int, max_context_len: int, partition_size: int) -> int:
+    """Form code of tv_paged_attention_decode_step for these shapes on the
+    current device (0-3, or -1 for shapes the step rejects)."""
+    return int(lib().tv_paged_attention_decode_step_form(
+        int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
+        int(max_context_len), int(partition_size)))
 
 
 def _pool_dims(k_cache, v_cache):

@@ -414,8 +414,8 @@ tv_status tv_paged_attention_decode_step(float *out, float *part_acc, float *par
     }
     if (tv::paged_decode_seq_fits(a)) {
         // Every (sequence, K/V head) in one resident workgroup whose
-        // wavefronts take one partition each and merge in LDS: one launch,
-        // the workspace unused.
+        // wavefronts take one equal range of the context each and merge in
+        // LDS: one launch, the workspace unused.
         a.part_acc = out;
         a.part_max = nullptr;
         a.part_sum = nullptr;
@@ -427,6 +427,32 @@ tv_status tv_paged_attention_decode_step(float *out, float *part_acc, float *par
     tv::ReduceArgs r{out, part_acc, part_max, part_sum, context_lens, num_seqs, num_q_heads,
                      a.num_parts, partition_size, max_context_len};
     return from_hip(tv::launch_paged_reduce(r, hs));
+}
+
+int32_t tv_paged_attention_decode_step_form(int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t block_size, int32_t max_context_len,
+                                            int32_t partition_size)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || max_context_len < 0 || partition_size <= 0 ||
+        num_q_heads % num_kv_heads != 0 || partition_size % block_size != 0)
+        return -1;
+    if (head_dim != tv::kHeadDim || block_size != tv::kBlockSize ||
+        num_q_heads / num_kv_heads > tv::kMaxGroup)
+        return -1;
+    if (num_seqs == 0 || max_context_len == 0)
+        return 0;
+    if (max_context_len <= partition_size)
+        return 1;
+    tv::DecodeArgs a{};
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.num_parts = (int32_t)ceil_div(max_context_len, partition_size);
+    a.part_tiles = partition_size / block_size;
+    a.max_context_len = max_context_len;
+    return tv::paged_decode_seq_fits(a) ? 2 : 3;
 }
 
 tv_status tv_paged_attention_reduce(float *out, const float *part_acc, const float *part_max,

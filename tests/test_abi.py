@@ -59,6 +59,22 @@ def test_num_partitions(lib):
     assert lib.tv_num_partitions(100, 0) == -1
 
 
+def test_decode_step_form_host_cases(lib):
+    """The forms decided without the device: rejected shapes, nothing to launch,
+    one partition.  (Forms 2 and 3 read the device and are covered on the GPU.)"""
+    f = lib.tv_paged_attention_decode_step_form
+    assert f(64, 32, 8, 64, 16, 512, 512) == 1
+    assert f(64, 32, 8, 64, 16, 37, 512) == 1
+    assert f(0, 32, 8, 64, 16, 4096, 512) == 0
+    assert f(64, 32, 8, 64, 16, 0, 512) == 0
+    assert f(64, 32, 8, 128, 16, 4096, 512) == -1      # head_dim other than 64
+    assert f(64, 32, 8, 64, 32, 4096, 512) == -1       # block size other than 16
+    assert f(64, 30, 8, 64, 16, 4096, 512) == -1       # query heads not a multiple
+    assert f(64, 32, 8, 64, 16, 4096, 500) == -1       # partition not whole blocks
+    assert f(-1, 32, 8, 64, 16, 4096, 512) == -1
+    assert f(64, 32, 8, 64, 16, -1, 512) == -1
+
+
 def _cw(lib, T=4, hkv=8, d=64, bs=16, nb=8, ptrs=(BAD,) * 5):
     return lib.tv_cache_write(*ptrs, T, hkv, d, bs, nb, None)
 

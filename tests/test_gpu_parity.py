@@ -106,11 +106,12 @@ def _call_step(db):
     return got.cpu().numpy()
 
 
-# Workloads the one call serves in the whole-sequence form (2 to 8 partitions,
-# every (sequence, K/V head) workgroup resident at once): 8 x U[128, 1024] and
-# 64 x U[512, 4096].  Workload 1 fits one partition; workloads 4 (2048
-# (sequence, head) pairs) and 5 (256 partitions) take the two launches.
-_WHOLE_SEQUENCE_WORKLOADS = (2, 3)
+# The form tv_paged_attention_decode_step takes per workload on MI355X: the
+# whole-sequence launch (2 to 8 partitions, every (sequence, K/V head)
+# workgroup resident at once) for 8 x U[128, 1024] and 64 x U[512, 4096]; one
+# partition for workload 1; two launches for workloads 4 (2048 (sequence, head)
+# pairs) and 5 (256 partitions).
+_STEP_FORM = {1: 1, 2: 2, 3: 2, 4: 3, 5: 3}
 
 
 @pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
@@ -125,9 +126,14 @@ def test_decode_step_call_workloads(dev, oracle_lib, index):
     batch = W.make_workload(index)
     ref, kc_ref, vc_ref = _oracle_step(oracle_lib, ("workload", index), batch)
     two, db = _gpu_step(batch, dev, fused=True)
+    import paged_kv_cache_tv_amd as tv
+    form = tv.decode_step_form(batch.num_seqs, batch.num_q_heads, batch.num_kv_heads,
+                               batch.head_dim, batch.block_size, db.max_context_len,
+                               db.partition_size)
+    assert form == _STEP_FORM[index], f"workload {index}: step form {form}"
     got = _call_step(db)
     assert np.array_equal(got, _call_step(db)), f"workload {index}: two calls differ"
-    if index in _WHOLE_SEQUENCE_WORKLOADS:
+    if form == 2:
         assert np.abs(got - two).max() <= 2e-6, f"workload {index}: one call far from two launches"
     else:
         assert np.array_equal(got, two), f"workload {index}: one call differs from two launches"
@@ -165,6 +171,8 @@ def test_decode_step_whole_sequence_form(dev, oracle_lib, case):
     batch = W.make_batch(lens, seed, num_q_heads=hq, num_kv_heads=hkv, table_width=mc // 16 + 1)
     ref, kc_ref, vc_ref = O.decode_step(oracle_lib, batch)
     two, db = _gpu_step(batch, dev, partition_size=part, max_context_len=mc, fused=True)
+    import paged_kv_cache_tv_amd as tv
+    assert tv.decode_step_form(len(lens), hq, hkv, 64, 16, mc, part) == 2
     got = _call_step(db)
     assert np.array_equal(got, _call_step(db)), "two calls differ"
     assert np.abs(got - two).max() <= 2e-6, "one call far from the two-launch step"
