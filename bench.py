@@ -193,32 +193,34 @@ def algorithmic_bytes(batch):
     return decode, decode + reduce_out + write, write
 
 
-def block_copy_rate(tv, dev, stream, flush, steps, pairs=2048):
-    """Copy-on-write copies on a pool of their own: `pairs` blocks (all 8 K/V
-    heads of 16 tokens x 64 dims in both pools, 32 KiB per block) copied to
-    fresh blocks.  Each launch follows a cache eviction and is bracketed by its
-    own pair of events on the kernel's stream; the figure is the mean over
-    `steps` launches.  Bytes counted: each block read once and written once."""
+def block_copy_rate(tv, dev, stream, flush, steps, sizes=(32, 64, 512, 2048)):
+    """Copy-on-write copies on a pool of their own: for each count in `sizes`,
+    that many blocks (all 8 K/V heads of 16 tokens x 64 dims in both pools,
+    32 KiB per block) copied to fresh blocks, one launch per step.  Timed
+    like the decode step: (eviction, launch) pairs back to back between two
+    events on the kernel's stream, minus the eviction loop.  Up to 512 pairs
+    the launch uses the 256-thread shape (a decode step's copies), above it
+    the 128-thread one.  Bytes counted: each block read once and written
+    once.  The top-level fields are those of the largest count."""
     import torch
-    kc, vc = tv.new_pools(2 * pairs, 8, 64, 16, dev, fill=0)
-    pr = torch.stack([torch.arange(pairs), pairs + torch.arange(pairs)], 1).to(torch.int64).to(dev)
-    tv.copy_blocks(kc, vc, pr, stream)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i, (a, b) in enumerate(ev):
-        flush(i)
-        a.record(stream)
+    top = max(sizes)
+    kc, vc = tv.new_pools(2 * top, 8, 64, 16, dev, fill=0)
+    out = {}
+    for pairs in sizes:
+        pr = torch.stack([torch.arange(pairs), top + torch.arange(pairs)], 1).to(torch.int64).to(dev)
         tv.copy_blocks(kc, vc, pr, stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
-    moved = pairs * 2 * (2 * 8 * 16 * 64 * 2)           # read + write, K and V pools
-    gbs = moved / (ms * 1e-3) / 1e9
+        ms = cold_loop_ms(stream, flush, lambda: tv.copy_blocks(kc, vc, pr, stream), steps)
+        moved = pairs * 2 * (2 * 8 * 16 * 64 * 2)           # read + write, K and V pools
+        gbs = moved / (ms * 1e-3) / 1e9
+        out[pairs] = {"kernel": "block_copy_kernel<256, 4>" if pairs <= 512
+                      else "block_copy_kernel<128, 8>",
+                      "pairs": pairs, "bytes_per_launch": moved,
+                      "us_per_launch": round(ms * 1e3, 2), "GB_per_s": round(gbs, 2),
+                      "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
     del kc, vc
-    return {"kernel": "block_copy_kernel", "pairs": pairs, "bytes_per_launch": moved,
-            "us_per_launch": round(ms * 1e3, 2), "GB_per_s": round(gbs, 2),
-            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    res = dict(out[top])
+    res["sizes"] = {str(p): {k: v for k, v in r.items() if k != "pairs"} for p, r in out.items()}
+    return res
 
 
 def block_manager_rate(tv, steps, prompts=64, samples=4, prefix=1024, seed=7):
@@ -316,7 +318,8 @@ def rope_rate(tv, dev, stream, flush, steps, index=3):
     """Rotary embedding on the prefill workload `index` (8 prompts x 2048
     tokens): the K/V cache write of all prompt tokens plain (tv_cache_write)
     and with K rotated (tv_cache_write_rope), and q rotated in place
-    (tv_rope).  Each launch follows a cache eviction and has its own events.
+    (tv_rope).  Each launch follows a cache eviction; timed like the decode
+    step (eviction + launch loop between two events, minus the eviction loop).
     Bytes counted: K and V read and written (cache writes), q read and
     written (tv_rope), plus slots and positions."""
     import numpy as np
@@ -347,16 +350,7 @@ def rope_rate(tv, dev, stream, flush, steps, index=3):
     res = {"workload": pb.name, "tokens": T}
     for name, (fn, nbytes) in cases.items():
         fn()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        torch.cuda.synchronize()
-        for i, (e0, e1) in enumerate(ev):
-            flush(i)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+        ms = cold_loop_ms(stream, flush, fn, steps)
         gbs = nbytes / (ms * 1e-3) / 1e9
         res[name] = {"bytes_per_launch": nbytes, "us_per_launch": round(ms * 1e3, 2),
                      "GB_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
@@ -369,8 +363,8 @@ def shared_prefix_rate(tv, dev, stream, flush, steps):
     samples, 1024 shared tokens): per sequence (tv_paged_attention_decode)
     against groups of 4 (tv_paged_attention_decode_shared), and the whole
     two-launch step each way (tv_paged_attention_decode_append or
-    tv_paged_attention_decode_shared_append, then the merge); cold, events
-    around each.  Bytes: the K/V each path must read at least -- logical
+    tv_paged_attention_decode_shared_append, then the merge); cold, timed
+    like the decode step.  Bytes: the K/V each path must read at least -- logical
     (every sequence's context) and unique (shared blocks once)."""
     import torch
     from paged_kv_cache_tv_amd import workloads as W
@@ -409,17 +403,7 @@ def shared_prefix_rate(tv, dev, stream, flush, steps):
     for name, fn in (("per_sequence", plain), ("shared", grouped),
                      ("per_sequence_step", plain_step), ("shared_step", grouped_step)):
         fn()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        torch.cuda.synchronize()
-        for i, (e0, e1) in enumerate(ev):
-            flush(i)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
-        res[name + "_us"] = round(ms * 1e3, 2)
+        res[name + "_us"] = round(cold_loop_ms(stream, flush, fn, steps) * 1e3, 2)
     res["unique_GB_per_s_shared"] = round(b.kv_bytes_unique() / (res["shared_us"] * 1e-6) / 1e9, 1)
     del db
     return res

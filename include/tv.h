@@ -261,10 +261,15 @@ tv_status tv_paged_attention_decode_shared(float *part_acc, float *part_max, flo
  * n == 0) appends nothing for s.  The partials are then those of
  * tv_paged_attention_decode over the pools after the writes.
  *
- * Precondition (the usual one for a decode step): slot_mapping[s] is negative
- * or is the slot the block table gives for position n - 1 of sequence s, and
- * no other sequence of the call reads that slot.  Then the result equals the
- * two-call sequence bit for bit.  A slot elsewhere is still written, but
+ * Precondition (the usual one for a decode step, where the block a sequence
+ * appends to is its own): slot_mapping[s] is negative or is the slot the
+ * block table gives for position n - 1 of sequence s, no other sequence of
+ * the call reads that slot, and no other sequence of the call appends into
+ * the same block.  Then the result equals the two-call sequence bit for bit.
+ * The token is written by storing back the whole 16-token tile of its block
+ * and head as this call read it, with the new token in place; another
+ * sequence appending into the same block in the same call may therefore
+ * lose its token.  A slot elsewhere is still written (its row alone), but
  * position n - 1 is read from the pool, and a slot that another sequence of
  * the same call reads gives unspecified values for that sequence.
  *
@@ -291,8 +296,9 @@ tv_status tv_paged_attention_decode_append(float *part_acc, float *part_max, flo
  * Shared-prefix partition pass with the cache write folded in: the same
  * results as tv_cache_write of one new token per sequence (as in
  * tv_paged_attention_decode_append) followed by
- * tv_paged_attention_decode_shared, in two launches on `stream` (the group
- * pass, then the per-sequence pass that also writes the tokens).  The
+ * tv_paged_attention_decode_shared, in one launch on `stream` (the group
+ * pass's workgroups first, then the per-sequence ones, which also write the
+ * tokens).  The
  * parallel-sampling decode step ("vLLM" page, section "가상 메모리 방식의
  * 해결": samples share their prompt's blocks; each sample's new token goes
  * to a block of its own).

@@ -432,7 +432,15 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
         } else if (part < shared_parts) {
             if (!APPEND)
                 return;                        // computed by the shared pass
-            write_only = true;                 // the shared pass attends; only the cache write here
+            // The shared pass attends this partition; the unit is left only
+            // the cache write of a new token at position n-1, if that lies
+            // here (it does not when the precondition holds).
+            int ns = a.context_lens[s];
+            ns = ns < 0 ? 0 : (ns > a.max_context_len ? a.max_context_len : ns);
+            const int p0 = part * a.part_tiles * BS;
+            if (ns - 1 < p0 || ns - 1 >= p0 + a.part_tiles * BS)
+                return;
+            write_only = true;
         }
     }
     // The partition's table entries (partitions of up to 64 blocks) are
@@ -512,6 +520,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
                                                        2 * (lane & 31));
     }
     int sub_off = -1;                     // token of the last tile replaced (-1: none)
+    bool row_done = false;                // the new row went out with its whole tile
 
     // The cache write of the new token, this head, from the row staged in LDS.
     auto store_new_row = [&]() {
@@ -572,6 +581,20 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
                             u.v[j][i] = (short)s_new[D + 16 * j + r];
             }
             attend_tile<true>(u, qb0, qb1, ptok - tile * BS - 4 * g, c, m_run, l_run, o);
+            // The cache write: the whole tile goes back with the new token in
+            // place (every other position rewritten with the bits just read),
+            // as coalesced 16- and 8-byte stores instead of the row's 8 chunk
+            // and 64 column stores, none of which fills a 32-byte sector.
+            char *kw = reinterpret_cast<char *>(a.k_cache_w) + (int64_t)b * tile_stride +
+                       (int64_t)kvh * kTileBytes;
+            char *vw = reinterpret_cast<char *>(a.v_cache_w) + (int64_t)b * tile_stride +
+                       (int64_t)kvh * kTileBytes;
+            *reinterpret_cast<u32x4 *>(kw + koff) = __builtin_bit_cast(u32x4, u.k0);
+            *reinterpret_cast<u32x4 *>(kw + 1024 + koff) = __builtin_bit_cast(u32x4, u.k1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<u32x2 *>(vw + voff + 512 * j) = __builtin_bit_cast(u32x2, u.v[j]);
+            row_done = true;
             return;
         }
         if ((tile + 1) * BS <= ptok)
@@ -628,7 +651,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs &a, unsigned bid)
         }
     }
 
-    if (APPEND && wslot >= 0)
+    if (APPEND && wslot >= 0 && !row_done)
         store_new_row();
 
     if (SPLIT > 1) {
@@ -720,7 +743,7 @@ void paged_decode_seq_kernel(DecodeArgs a)
 // partitions and write disjoint partials, so one grid lets each fill the
 // other's tail.  shared_groups is a multiple of the K/V head count, so every
 // workgroup keeps its head's XCD.
-template <bool APPEND, int SPLIT>
+template <bool APPEND, int SPLIT, bool PLAN>
 __global__ __launch_bounds__(64 * SPLIT)
 __attribute__((amdgpu_waves_per_eu(SPLIT > 1 ? 4 : 3, SPLIT > 1 ? 4 : 8)))
 void paged_decode_shared_kernel(DecodeArgs a, unsigned shared_groups)
@@ -728,7 +751,7 @@ void paged_decode_shared_kernel(DecodeArgs a, unsigned shared_groups)
     if (blockIdx.x < shared_groups)
         decode_unit<false, true, false, SPLIT>(a, blockIdx.x);
     else
-        decode_unit<APPEND, false, false, SPLIT>(a, blockIdx.x - shared_groups);
+        decode_unit<APPEND, false, PLAN, SPLIT>(a, blockIdx.x - shared_groups);
 }
 
 // What the launcher needs to know of the device: its compute units and how
@@ -857,21 +880,33 @@ hipError_t launch_paged_decode(const DecodeArgs &args, hipStream_t stream)
     const bool split = resident > 0 && groups <= 2 * resident;
     if (a.shared_len) {
         // One workgroup per (group, head, partition) for the group pass, then
-        // one per (sequence, head, partition) for the rest, in one grid.
+        // one per (sequence, head, partition) for the rest, in one grid; the
+        // rest in the balanced order when the sequences are in their own
+        // order (no group_order) and the grid is larger than the device holds.
         const int64_t shared_groups = (int64_t)a.num_kv_heads * a.num_groups * a.num_parts;
         const dim3 grid((unsigned)(shared_groups + groups));
+        a.plan_width = 0;
+        if (groups > resident && !a.group_order && a.num_seqs <= 64 * kPlanChunks && dev.cus > 0)
+            a.plan_width = dev.cus / std::gcd(a.num_kv_heads, dev.cus);
+        const unsigned sg = (unsigned)shared_groups;
         if (split && a.k_new)
-            hipLaunchKernelGGL((paged_decode_shared_kernel<true, 4>), grid, dim3(256), 0, stream, a,
-                               (unsigned)shared_groups);
+            hipLaunchKernelGGL((paged_decode_shared_kernel<true, 4, false>), grid, dim3(256), 0,
+                               stream, a, sg);
         else if (split)
-            hipLaunchKernelGGL((paged_decode_shared_kernel<false, 4>), grid, dim3(256), 0, stream,
-                               a, (unsigned)shared_groups);
+            hipLaunchKernelGGL((paged_decode_shared_kernel<false, 4, false>), grid, dim3(256), 0,
+                               stream, a, sg);
+        else if (a.k_new && a.plan_width > 0)
+            hipLaunchKernelGGL((paged_decode_shared_kernel<true, 1, true>), grid, dim3(64), 0,
+                               stream, a, sg);
+        else if (a.plan_width > 0)
+            hipLaunchKernelGGL((paged_decode_shared_kernel<false, 1, true>), grid, dim3(64), 0,
+                               stream, a, sg);
         else if (a.k_new)
-            hipLaunchKernelGGL((paged_decode_shared_kernel<true, 1>), grid, dim3(64), 0, stream, a,
-                               (unsigned)shared_groups);
+            hipLaunchKernelGGL((paged_decode_shared_kernel<true, 1, false>), grid, dim3(64), 0,
+                               stream, a, sg);
         else
-            hipLaunchKernelGGL((paged_decode_shared_kernel<false, 1>), grid, dim3(64), 0, stream, a,
-                               (unsigned)shared_groups);
+            hipLaunchKernelGGL((paged_decode_shared_kernel<false, 1, false>), grid, dim3(64), 0,
+                               stream, a, sg);
         return hipGetLastError();
     }
     // Balanced order: consecutive workgroups of one head cycle over
