@@ -365,7 +365,9 @@ def shared_prefix_rate(tv, dev, stream, flush, steps):
     two-launch step each way (tv_paged_attention_decode_append or
     tv_paged_attention_decode_shared_append, then the merge); cold, timed
     like the decode step.  Bytes: the K/V each path must read at least -- logical
-    (every sequence's context) and unique (shared blocks once)."""
+    (every sequence's context) and unique (shared blocks once).  `shared_step`
+    is the step through the one call (tv_paged_attention_decode_shared_step),
+    `shared_two_launch_step` the shared append and the merge."""
     import torch
     from paged_kv_cache_tv_amd import workloads as W
     from paged_kv_cache_tv_amd.step import DeviceBatch
@@ -398,13 +400,31 @@ def shared_prefix_rate(tv, dev, stream, flush, steps):
     def plain_step():
         db.fused_step(stream)
 
+    out = torch.empty_like(db.out)
+
+    def one_call_step():
+        # The same step through tv_paged_attention_decode_shared_step.
+        tv.paged_attention_decode_shared_step(out, db.workspace, db.q, db.step_k, db.step_v,
+                                              db.step_slots, db.k_cache, db.v_cache,
+                                              db.block_tables, db.context_lens, shared, 4,
+                                              db.max_context_len, db.partition_size, b.scale,
+                                              stream)
+
+    form = tv.decode_shared_step_form(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                      b.block_size, db.max_context_len, db.partition_size, 4)
     res = {"workload": b.name, "group_size": 4, "shared_tokens": 1024,
-           "kv_bytes_logical": b.kv_bytes_logical(), "kv_bytes_unique": b.kv_bytes_unique()}
+           "kv_bytes_logical": b.kv_bytes_logical(), "kv_bytes_unique": b.kv_bytes_unique(),
+           "shared_step": "one call, tv_paged_attention_decode_shared_step: " +
+                          {1: "one launch, one workgroup per (group, K/V head)",
+                           2: "two launches through the workspace"}.get(form, str(form))}
     for name, fn in (("per_sequence", plain), ("shared", grouped),
-                     ("per_sequence_step", plain_step), ("shared_step", grouped_step)):
+                     ("per_sequence_step", plain_step), ("shared_two_launch_step", grouped_step),
+                     ("shared_step", one_call_step)):
         fn()
         res[name + "_us"] = round(cold_loop_ms(stream, flush, fn, steps) * 1e3, 2)
     res["unique_GB_per_s_shared"] = round(b.kv_bytes_unique() / (res["shared_us"] * 1e-6) / 1e9, 1)
+    res["unique_GB_per_s_shared_step"] = round(
+        b.kv_bytes_unique() / (res["shared_step_us"] * 1e-6) / 1e9, 1)
     del db
     return res
 
@@ -432,9 +452,10 @@ def workloads_rate(tv, dev, stream, flush, steps, warmup, partition_size, have=N
     """The decode step on every one of the five workloads, cold, timed as the
     headline step is (eviction-subtracted event loop): the two-launch step
     (decode_append + reduce) and the one-call step (tv_paged_attention_decode_step:
-    one launch when the contexts fit one partition).  Workload 4 also runs its
-    parallel-sampling form (shared prefix read once per group of 4:
-    tv_paged_attention_decode_shared_append + reduce).  GB/s counts the same
+    the form tv_paged_attention_decode_step_form reports).  Workload 4 also
+    runs its parallel-sampling form (shared prefix read once per group of 4):
+    tv_paged_attention_decode_shared_append + reduce, and the one call
+    tv_paged_attention_decode_shared_step.  GB/s counts the same
     algorithmic bytes as the headline; for workload 4 both the logical bytes
     (every sequence's context) and the unique ones (each shared block once).
     `have` maps a workload index to an already built (batch, DeviceBatch)."""
@@ -463,6 +484,14 @@ def workloads_rate(tv, dev, stream, flush, steps, warmup, partition_size, have=N
                     db.partition_size, batch.scale, stream)
                 db.reduce(stream)
             forms["shared_prefix_two_launch"] = grouped_step
+            sh_out = torch.empty_like(db.out)
+
+            def grouped_call():
+                tv.paged_attention_decode_shared_step(
+                    sh_out, db.workspace, db.q, db.step_k, db.step_v, db.step_slots, db.k_cache,
+                    db.v_cache, db.block_tables, db.context_lens, shared, 4, db.max_context_len,
+                    db.partition_size, batch.scale, stream)
+            forms["shared_prefix_one_call"] = grouped_call
         for fn in forms.values():
             for i in range(max(1, warmup)):
                 flush(i)

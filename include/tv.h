@@ -328,6 +328,64 @@ tv_status tv_paged_attention_decode_shared_append(
     void *stream);
 
 /*
+ * The parallel-sampling decode step in one call ("vLLM" page, section "가상
+ * 메모리 방식의 해결": the samples of one prompt share its blocks, and each
+ * sample's new token goes to a block of its own; section "Flash Attention":
+ * the running maximum / running sum rule): the cache write of one new token
+ * per sequence, shared-prefix attention and the log-sum-exp merge, writing
+ * out = softmax(q K^T * scale) V per (sequence, query head) as
+ * tv_paged_attention_decode_shared_append followed by
+ * tv_paged_attention_reduce would.
+ *
+ * Forms (from the shapes alone, never the data; a call is deterministic):
+ *   group_size <= 4, no group_order, and every (group, K/V head) workgroup
+ *   resident at once on the device (num_groups * num_kv_heads <= 2 * 256 on
+ *   MI355X): one launch with one 8-wavefront workgroup per (group, K/V
+ *   head).  The group's shared tiles (its shared length cut as for
+ *   tv_paged_attention_decode_shared) are read once with every member's
+ *   query heads, each member's other tiles with its own; each of these
+ *   ranges is cut into 8 equal consecutive parts, one per wavefront, and
+ *   the parts merge in on-chip memory.  The workspace is neither read nor
+ *   written (it must still be non-NULL and aligned), and out equals the
+ *   two-call result up to fp32 rounding (the parts are not its 512-token
+ *   partitions).
+ *   otherwise: tv_paged_attention_decode_shared_append, then
+ *   tv_paged_attention_reduce, on `stream`; out bitwise the two calls'.
+ * With max_context_len == 0 every row of out is set to zero.
+ *
+ *   out   float [num_seqs][num_q_heads][head_dim], 16-byte aligned
+ *   other arguments, preconditions and odd-data behaviour as for
+ *   tv_paged_attention_decode_shared_append (the workspace sized for
+ *   ceil(max_context_len / partition_size) partitions).
+ * Supported shapes: those of tv_paged_attention_decode_shared_append, and
+ * num_seqs * num_q_heads < 2^24.  Errors: TV_ERR_NULL, TV_ERR_SHAPE,
+ * TV_ERR_UNSUPPORTED, TV_ERR_ALIGNMENT, TV_ERR_HIP; all argument errors are
+ * found before anything is launched.  num_seqs == 0 is a no-op.
+ */
+tv_status tv_paged_attention_decode_shared_step(
+    float *out, float *part_acc, float *part_max, float *part_sum, const uint16_t *q,
+    const uint16_t *k_new, const uint16_t *v_new, const int64_t *slot_mapping, uint16_t *k_cache,
+    uint16_t *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+    const int32_t *shared_len, const int32_t *group_order, int32_t group_size, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+    int32_t partition_size, float scale, void *stream);
+
+/*
+ * Which form tv_paged_attention_decode_shared_step takes for these shapes on
+ * the current device: 0 nothing is launched (num_seqs == 0 or
+ * max_context_len == 0), 1 one launch (one workgroup per (group, K/V head)),
+ * 2 two launches through the workspace, -1 the step would reject these
+ * shapes.  has_group_order: nonzero if a group_order array is passed.
+ * Host-only; reads the current device's compute-unit count and occupancy.
+ */
+int32_t tv_paged_attention_decode_shared_step_form(int32_t num_seqs, int32_t num_q_heads,
+                                                   int32_t num_kv_heads, int32_t head_dim,
+                                                   int32_t block_size, int32_t max_context_len,
+                                                   int32_t partition_size, int32_t group_size,
+                                                   int32_t has_group_order);
+
+/*
  * Log-sum-exp merge of the partitions ("vLLM" page, Flash Attention: the
  * running maximum / running sum rule applied across partitions).
  *

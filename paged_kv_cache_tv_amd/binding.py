@@ -46,6 +46,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_num_partitions.argtypes = [i32, i32]
     lib.tv_paged_attention_decode_step_form.restype = i32
     lib.tv_paged_attention_decode_step_form.argtypes = [i32] * 7
+    lib.tv_paged_attention_decode_shared_step_form.restype = i32
+    lib.tv_paged_attention_decode_shared_step_form.argtypes = [i32] * 9
     lib.tv_cache_write.restype = ctypes.c_int
     lib.tv_cache_write.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, vp]
     lib.tv_paged_attention_decode.restype = ctypes.c_int
@@ -72,6 +74,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                             vp, vp, vp, i32, i32, i32, i32, i32,
                                                             i32, i32, i64, i32, i32, ctypes.c_float,
                                                             vp]
+    lib.tv_paged_attention_decode_shared_step.restype = ctypes.c_int
+    lib.tv_paged_attention_decode_shared_step.argtypes = [vp] * 14 + [i32] * 7 + [i64, i32, i32,
+                                                                                ctypes.c_float, vp]
     lib.tv_paged_attention_reduce.restype = ctypes.c_int
     lib.tv_paged_attention_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.tv_paged_attention_prefill.restype = ctypes.c_int
@@ -168,6 +173,16 @@ def decode_step_form(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_di
     return int(lib().tv_paged_attention_decode_step_form(
         int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
         int(max_context_len), int(partition_size)))
+
+
+def decode_shared_step_form(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                            block_size: int, max_context_len: int, partition_size: int,
+                            group_size: int, has_group_order: bool = False) -> int:
+    """Form code of tv_paged_attention_decode_shared_step for these shapes on
+    the current device (0 nothing, 1 one launch, 2 two launches, -1 rejected)."""
+    return int(lib().tv_paged_attention_decode_shared_step_form(
+        int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
+        int(max_context_len), int(partition_size), int(group_size), int(bool(has_group_order))))
 
 
 def _pool_dims(k_cache, v_cache):
@@ -465,6 +480,52 @@ def paged_attention_decode_step_noalloc(out, q, k_new, v_new, slot_mapping, k_ca
         context_lens.data_ptr(), S, hq, hkv, d, bs, block_tables.shape[1], nb,
         int(max_context_len), int(partition_size), float(scale), _stream_handle(stream, q.device))
     _check("tv_paged_attention_decode_step_noalloc", st)
+
+
+def paged_attention_decode_shared_step(out, workspace, q, k_new, v_new, slot_mapping, k_cache,
+                                       v_cache, block_tables, context_lens, shared_len,
+                                       group_size: int, max_context_len: int, partition_size: int,
+                                       scale: float, stream=None, group_order=None) -> None:
+    """tv_paged_attention_decode_shared_step: the parallel-sampling decode step
+    (appends, shared-prefix attention, merge) in one call, into out [S, Hq, D];
+    workspace = (part_acc, part_max, part_sum) as for paged_attention_decode."""
+    import torch
+    part_acc, part_max, part_sum = workspace
+    _need(out, "out", dtype=torch.float32, ndim=3)
+    _need(q, "q", itemsize=2, ndim=3)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, itemsize=2, ndim=3)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1)
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    _need(shared_len, "shared_len", dtype=torch.int32, ndim=1)
+    for t, n in ((part_acc, "part_acc"), (part_max, "part_max"), (part_sum, "part_sum")):
+        _need(t, n, dtype=torch.float32)
+    S, hq, d = q.shape
+    nb, hkv, bs, d2 = _pool_dims(k_cache, v_cache)
+    if d2 != d:
+        raise ValueError("cache shapes do not match q")
+    if tuple(out.shape) != (S, hq, d):
+        raise ValueError("out must be [S, Hq, D]")
+    if tuple(k_new.shape) != (S, hkv, d) or tuple(v_new.shape) != (S, hkv, d) or \
+            slot_mapping.shape[0] != S:
+        raise ValueError("k_new, v_new must be [S, Hkv, D] and slot_mapping [S]")
+    P = num_partitions(max_context_len, partition_size)
+    if tuple(part_acc.shape) != (S, hq, P, d) or tuple(part_max.shape) != (S, hq, P) or \
+            tuple(part_sum.shape) != (S, hq, P):
+        raise ValueError(f"workspace must be [S, Hq, P(={P}), D] and [S, Hq, P]")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    if group_size < 1 or shared_len.shape[0] != -(-S // group_size):
+        raise ValueError("shared_len must have ceil(S / group_size) entries")
+    order = _group_order_ptr(group_order, S)
+    st = lib().tv_paged_attention_decode_shared_step(
+        out.data_ptr(), part_acc.data_ptr(), part_max.data_ptr(), part_sum.data_ptr(),
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(),
+        k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
+        shared_len.data_ptr(), order, int(group_size), S, hq, hkv, d, bs, block_tables.shape[1],
+        nb, int(max_context_len), int(partition_size), float(scale), _stream_handle(stream, q.device))
+    _check("tv_paged_attention_decode_shared_step", st)
 
 
 def paged_attention_decode_shared_append(part_acc, part_max, part_sum, q, k_new, v_new,

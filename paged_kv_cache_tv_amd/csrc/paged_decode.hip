@@ -288,33 +288,26 @@ __device__ Unit plan_unit(const DecodeArgs &a, int j, int lane)
 // a.plan_width compute units one workgroup of the head is dealt to in turn,
 // then backward in the next round, so that the compute unit that gets a long
 // sequence's workgroup gets a short one's next.  num_seqs <= 64 * kPlanChunks.
-__device__ int seq_unit(const DecodeArgs &a, int k, int lane)
+// Workgroup k's unit in the pairing order: units (lanes' entries of `cost`,
+// unit u = kk * 64 + lane, -1 past the count) ranked by cost, largest first,
+// and dealt over C compute units forward in one round and backward in the
+// next, so that a CU that got a large unit in one round gets a small one in
+// the next.  `bound` is at least every cost.
+__device__ int ranked_unit(const int (&cost)[kPlanChunks], int count, int bound, int C, int k)
 {
-    const int S = a.num_seqs;
-    const int C = a.plan_width;
-    if (S <= C)
-        return k;                                // one workgroup of the head per compute unit
-    int tiles[kPlanChunks];
-#pragma unroll
-    for (int kk = 0; kk < kPlanChunks; ++kk) {
-        const int s = kk * 64 + lane;
-        int n = s < S ? a.context_lens[s] : 0;
-        n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
-        tiles[kk] = s < S ? (n + BS - 1) / BS : -1;   // -1: no sequence
-    }
     const int r = k / C, c = k - r * C;
-    const int round_end = min(S, (r + 1) * C) - r * C;         // workgroups in this round
+    const int round_end = min(count, (r + 1) * C) - r * C;     // workgroups in this round
     const int t = r * C + ((r & 1) ? round_end - 1 - c : c);
     auto count_ge = [&](int b) {
         int cnt = 0;
 #pragma unroll
         for (int kk = 0; kk < kPlanChunks; ++kk)
-            if (kk * 64 < S)                     // only the chunks that hold sequences
-                cnt += (int)__popcll(__ballot(tiles[kk] >= b));
+            if (kk * 64 < count)                 // only the chunks that hold units
+                cnt += (int)__popcll(__ballot(cost[kk] >= b));
         return cnt;
     };
-    // The t-th largest tile count b, then the right sequence among those of b.
-    int blo = 0, bhi = (a.max_context_len + BS - 1) / BS;
+    // The t-th largest cost b, then the right unit among those of cost b.
+    int blo = 0, bhi = bound;
     while (blo < bhi) {
         const int mid = (blo + bhi + 1) >> 1;
         if (count_ge(mid) > t)
@@ -323,21 +316,41 @@ __device__ int seq_unit(const DecodeArgs &a, int k, int lane)
             bhi = mid - 1;
     }
     int rank = t - count_ge(blo + 1);
-    int s = 0;
+    int u = 0;
 #pragma unroll
     for (int kk = 0; kk < kPlanChunks; ++kk) {
-        if (kk * 64 >= S)
+        if (kk * 64 >= count)
             break;
-        uint64_t m = __ballot(tiles[kk] == blo);
+        uint64_t m = __ballot(cost[kk] == blo);
         const int cnt = (int)__popcll(m);
         if (rank >= 0 && rank < cnt) {
             for (int i = 0; i < rank; ++i)
                 m &= m - 1;                      // drop the lowest set lanes
-            s = kk * 64 + (int)__builtin_ctzll(m);
+            u = kk * 64 + (int)__builtin_ctzll(m);
         }
         rank -= cnt;
     }
-    return s;
+    return u;
+}
+
+// The sequence of whole-sequence workgroup k of a head: sequences ranked by
+// tile count in the pairing order when they outnumber the head's compute
+// units, else in their own order (one workgroup of the head per CU).
+__device__ int seq_unit(const DecodeArgs &a, int k, int lane)
+{
+    const int S = a.num_seqs;
+    const int C = a.plan_width;
+    if (S <= C)
+        return k;
+    int tiles[kPlanChunks];
+#pragma unroll
+    for (int kk = 0; kk < kPlanChunks; ++kk) {
+        const int s = kk * 64 + lane;
+        int n = s < S ? a.context_lens[s] : 0;
+        n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
+        tiles[kk] = s < S ? (n + BS - 1) / BS : -1;   // -1: no sequence
+    }
+    return ranked_unit(tiles, S, (a.max_context_len + BS - 1) / BS, C, k);
 }
 
 // APPEND: sequence s also brings a new token (k_new, v_new) for slot
@@ -738,6 +751,430 @@ void paged_decode_seq_kernel(DecodeArgs a)
     decode_unit<APPEND, false, false, kSeqWaves, true>(a, blockIdx.x);
 }
 
+// The whole-group form of the shared-prefix decode step: one workgroup of
+// kGroupWaves wavefronts per (group, K/V head), the cache write of every
+// member's new token folded in and the log-sum-exp merge done in LDS, so
+// the step is one launch with no workspace ("vLLM" page, section "가상 메모리
+// 방식의 해결": the samples of one prompt share its blocks; section "Flash
+// Attention": pieces of a softmax merge by the running maximum / sum rule).
+//   * The group's shared tiles (its shared length cut to whole partitions, as
+//     in the group pass) are read once, with every member's query heads as
+//     MFMA columns (column r: member r / G, head r % G), and each member's
+//     private tiles with the same columns, of which only the member's own are
+//     kept.  The group's tiles -- the shared ones, then each member's own --
+//     form one sequence, cut into kGroupWaves equal consecutive parts, one
+//     per wavefront; a part may span several ranges, streamed back to back
+//     through one ring.  Groups are dealt to compute units in the pairing
+//     order (group_unit), so a CU's two workgroups carry a large and a
+//     small group.
+//   * A wavefront folds each range's tiles into one running state in
+//     registers; at the end of a range that state is merged into the
+//     wavefront's accumulated state, kept in LDS: for every column after the
+//     shared range, for the member's own columns only after a member's range
+//     (the other columns, the member's K/V against other members' queries,
+//     are dropped).
+//   * The wavefront holding a member's last tile writes that member's new
+//     token, substituting it in registers and storing the whole tile back,
+//     as the append pass does; a slot elsewhere gets its row alone at the end.
+//   * The kGroupWaves states merge in LDS in wavefront order and the rows are
+//     written to `out` (part_acc), divided by their sums.
+constexpr int kGroupWaves = 8;
+constexpr int kGroupRing = 2;
+constexpr int kGroupMaxMembers = 4;
+
+struct RunState {
+    float m, l;
+    f32x4 o[4];
+};
+
+__device__ __forceinline__ void state_init(RunState &st)
+{
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        st.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// dst <- dst (+) src by the running maximum / sum rule; a state with
+// m = -inf holds nothing and weighs 0.
+__device__ __forceinline__ void state_merge(RunState &dst, const RunState &src)
+{
+    if (src.m == -INFINITY)
+        return;
+    const float mm = fmaxf(dst.m, src.m);
+    const float ad = dst.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(dst.m - mm);
+    const float as = __builtin_amdgcn_exp2f(src.m - mm);
+    dst.l = fmaf(src.l, as, dst.l * ad);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        dst.o[j] = dst.o[j] * ad + src.o[j] * as;
+    dst.m = mm;
+}
+
+// The group of whole-group workgroup k of a head: groups ranked by their
+// tile count (shared tiles once plus every member's own) in the pairing
+// order when they outnumber the head's compute units, else in their own
+// order.
+__device__ int group_unit(const DecodeArgs &a, int k, int lane)
+{
+    const int NG = a.num_groups;
+    const int C = a.plan_width;
+    if (NG <= C || NG > 64 * kPlanChunks)
+        return k;
+    int tiles[kPlanChunks];
+#pragma unroll
+    for (int kk = 0; kk < kPlanChunks; ++kk) {
+        const int gi = kk * 64 + lane;
+        tiles[kk] = -1;                          // -1: no group
+        if (gi < NG) {
+            const int f = gi * a.group_size;
+            const int cnt = min(a.group_size, a.num_seqs - f);
+            int sh = a.shared_len[gi];
+            int sum = 0;
+            for (int m = 0; m < cnt; ++m) {
+                int n = a.context_lens[f + m];
+                n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
+                sh = min(sh, n);
+                sum += (n + BS - 1) / BS;
+            }
+            const int st = sh > 0 ? (sh / (a.part_tiles * BS)) * a.part_tiles : 0;
+            tiles[kk] = sum - (cnt - 1) * st;    // the shared tiles counted once
+        }
+    }
+    const int bound = kGroupMaxMembers * ((a.max_context_len + BS - 1) / BS);
+    return ranked_unit(tiles, NG, bound, C, k);
+}
+
+template <bool APPEND>
+__global__ __launch_bounds__(64 * kGroupWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void paged_decode_group_kernel(DecodeArgs a)
+{
+    const int lane = (int)(threadIdx.x & 63);
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int kvh = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
+    const int grp = group_unit(a, (int)(blockIdx.x / (unsigned)a.num_kv_heads), lane);
+    const int first = grp * a.group_size;
+    const int cnt = min(a.group_size, a.num_seqs - first);
+    const int G = a.group;
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const float c = a.scale_log2;
+
+    // Lane m < cnt: member m's context length (clamped).  The shared length
+    // is cut to every member's context and to whole partitions.
+    int n_lane = 0;
+    if (lane < cnt) {
+        n_lane = a.context_lens[first + lane];
+        n_lane = n_lane < 0 ? 0 : (n_lane > a.max_context_len ? a.max_context_len : n_lane);
+    }
+    int sh = a.shared_len[grp];
+    for (int m = 0; m < cnt; ++m)
+        sh = min(sh, __builtin_amdgcn_readlane(n_lane, m));
+    const int ST = sh > 0 ? (sh / (a.part_tiles * BS)) * a.part_tiles : 0;   // shared tiles
+
+    // The group's tiles in one sequence: the shared tiles [0, ST), then member
+    // 0's own tiles, member 1's, ...; g_end (lane m) is one past member m's
+    // last place in it.  Wavefront wv takes places [v_lo, v_hi), an eighth.
+    const int t_all = (n_lane + BS - 1) / BS;
+    const int pt = lane < cnt ? max(0, t_all - ST) : 0;
+    int g_end = pt;
+#pragma unroll
+    for (int d = 1; d < kGroupMaxMembers; d <<= 1) {
+        const int y = __shfl_up(g_end, d);
+        if (lane >= d)
+            g_end += y;
+    }
+    g_end += ST;
+    const int total = __builtin_amdgcn_readlane(g_end, cnt - 1);   // cnt >= 1
+    const int v_lo = (int)((int64_t)wv * total / kGroupWaves);
+    const int v_hi = (int)((int64_t)(wv + 1) * total / kGroupWaves);
+    const int nv = v_hi - v_lo;
+
+    // Columns: member r / G (r < cnt * G), query head kvh * G + r % G.
+    const bool col_ok = r < cnt * G;
+    const int col_mem = col_ok ? r / G : 0;
+    bf16x8 qb0 = {}, qb1 = {};
+    if (col_ok) {
+        const uint16_t *qp =
+            a.q + ((int64_t)(first + col_mem) * a.num_kv_heads * G + (int64_t)kvh * G + r % G) * D +
+            g * 8;
+        qb0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp));
+        qb1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 32));
+    }
+
+    // Append: lane m < cnt -- does this wavefront hold member m's last tile
+    // (position n_m - 1 past the shared tiles), its slot, and the table entry
+    // of position n_m - 1.  The new rows of the members it holds are staged
+    // in LDS after the first tile loads are out.
+    __shared__ uint16_t s_new[kGroupWaves][kGroupMaxMembers][2 * D];
+    const int last_t = (n_lane - 1) / BS;
+    const bool hold_lane = APPEND && lane < cnt && n_lane > 0 && last_t >= ST &&
+                           g_end - 1 >= v_lo && g_end - 1 < v_hi;   // its last place
+    const uint64_t held = __ballot(hold_lane);
+    int64_t wslot_lane = -1;
+    int32_t tblk_lane = -1;
+    if (hold_lane) {
+        wslot_lane = a.slot_mapping[first + lane];
+        tblk_lane = a.block_tables[(int64_t)(first + lane) * a.max_blocks + last_t];
+    }
+    uint32_t new_pair[kGroupMaxMembers];
+#pragma unroll
+    for (int m = 0; m < kGroupMaxMembers; ++m) {
+        new_pair[m] = 0;
+        if (APPEND && ((held >> m) & 1ull))
+            new_pair[m] = *reinterpret_cast<const uint32_t *>(
+                (lane < 32 ? a.k_new : a.v_new) +
+                ((int64_t)(first + m) * a.num_kv_heads + kvh) * D + 2 * (lane & 31));
+    }
+    int sub_lane = -1;        // lane m: token of member m's last tile replaced (-1: none)
+    bool done_lane = false;   // lane m: member m's row went out with its tile
+
+    const char *kpool = reinterpret_cast<const char *>(a.k_cache) + (int64_t)kvh * kTileBytes;
+    const char *vpool = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * kTileBytes;
+    const int64_t tile_stride = (int64_t)a.num_kv_heads * kTileBytes;
+    const uint32_t koff = (uint32_t)lane * 16u;
+    const uint32_t voff = (uint32_t)(r * BS + g * 4) * 2u;
+    auto issue = [&](Tile &t, int32_t b) {
+        const int64_t bb = (b >= 0 && b < a.num_blocks) ? (int64_t)b : 0;
+        load_tile(t, kpool + bb * tile_stride, vpool + bb * tile_stride, koff, voff);
+    };
+
+    // The wavefront's accumulated state, in LDS (also the final merge's input).
+    __shared__ float s_m[kGroupWaves][64], s_l[kGroupWaves][64];
+    __shared__ f32x4 s_o[kGroupWaves][4][64];
+    s_m[wv][lane] = -INFINITY;
+    s_l[wv][lane] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        s_o[wv][j][lane] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto fold_into_lds = [&](const RunState &R) {
+        RunState A;
+        A.m = s_m[wv][lane];
+        A.l = s_l[wv][lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            A.o[j] = s_o[wv][j][lane];
+        state_merge(A, R);
+        s_m[wv][lane] = A.m;
+        s_l[wv][lane] = A.l;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            s_o[wv][j][lane] = A.o[j];
+    };
+
+    RunState R;               // the range being folded
+    state_init(R);
+    int cur = -1;             // the range being folded: -1 shared, m >= 0 member m
+    int cur_end = min(max(ST - v_lo, 0), nv);   // its end, local place
+    int cur_tile0 = v_lo;     // tile index of local place 0 in this range
+    int cur_n = ST * BS;      // tokens of the range's sequence (masking)
+    // Close the ranges that end at or before virtual index k: fold R into the
+    // accumulated state (every column after the shared range, the member's
+    // own after a member's) and step to the next range.
+    auto advance_to = [&](int k) {
+        while (k >= cur_end && cur + 1 < cnt) {
+            if (cur < 0 || (col_ok && col_mem == cur))
+                fold_into_lds(R);
+            state_init(R);
+            ++cur;
+            const int ge = __builtin_amdgcn_readlane(g_end, cur);
+            const int gb = ge - __builtin_amdgcn_readlane(pt, cur);
+            cur_end = min(max(ge - v_lo, 0), nv);
+            cur_tile0 = v_lo - gb + ST;
+            cur_n = __builtin_amdgcn_readlane(n_lane, cur);
+        }
+    };
+
+    auto consume = [&](const Tile &t, int k, int32_t b) {
+        advance_to(k);
+        if (b < 0 || b >= a.num_blocks)
+            return;                                     // entry outside the pool: skipped
+        const int tile = cur_tile0 + k;
+        const int valid = cur_n - tile * BS - 4 * g;
+        const bool partial = (tile + 1) * BS > cur_n;
+        const int so = APPEND && cur >= 0 ? __builtin_amdgcn_readlane(sub_lane, cur) : -1;
+        const bool sub = APPEND && so >= 0 && tile == (cur_n - 1) / BS;
+        if (!sub && !partial) {
+            attend_tile<false>(t, qb0, qb1, 4, c, R.m, R.l, R.o);
+            return;
+        }
+        Tile u = t;
+        if (sub) {                                      // position n-1 takes the new token
+            const uint16_t *sn = s_new[wv][cur];
+            if (r == so) {
+                u.k0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(sn + 8 * g));
+                u.k1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(sn + 32 + 8 * g));
+            }
+            if (g == (so >> 2)) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (i == (so & 3))
+                            u.v[j][i] = (short)sn[D + 16 * j + r];
+            }
+        }
+        attend_tile<true>(u, qb0, qb1, valid, c, R.m, R.l, R.o);
+        if (sub) {
+            char *kw = reinterpret_cast<char *>(a.k_cache_w) + (int64_t)b * tile_stride +
+                       (int64_t)kvh * kTileBytes;
+            char *vw = reinterpret_cast<char *>(a.v_cache_w) + (int64_t)b * tile_stride +
+                       (int64_t)kvh * kTileBytes;
+            *reinterpret_cast<u32x4 *>(kw + koff) = __builtin_bit_cast(u32x4, u.k0);
+            *reinterpret_cast<u32x4 *>(kw + 1024 + koff) = __builtin_bit_cast(u32x4, u.k1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<u32x2 *>(vw + voff + 512 * j) = __builtin_bit_cast(u32x2, u.v[j]);
+            done_lane = done_lane || lane == cur;
+        }
+    };
+
+    for (int c0 = 0; c0 < nv; c0 += 64) {
+        const int cn = min(64, nv - c0);
+        // Lane l: the table entry of virtual tile c0 + l.
+        int32_t phys_lane = 0;
+        {
+            const int gp = v_lo + c0 + lane;           // this lane's place in the sequence
+            int mem = 0;                               // member m: places [g_end(m-1), g_end(m))
+            for (int m = 0; m + 1 < cnt; ++m)
+                if (gp >= __builtin_amdgcn_readlane(g_end, m))
+                    mem = m + 1;
+            // Shuffles with every lane active: a lane outside exec would not
+            // deliver its value.
+            const int ge = __shfl(g_end, mem);
+            const int gb = ge - __shfl(pt, mem);
+            const bool in_shared = gp < ST;
+            const int seq = first + (in_shared ? 0 : mem);
+            const int tix = in_shared ? gp : ST + (gp - gb);
+            if (lane < cn)
+                phys_lane = a.block_tables[(int64_t)seq * a.max_blocks + tix];
+        }
+        auto block_of = [&](int k) -> int32_t {
+            return __builtin_amdgcn_readlane(phys_lane, min(k, cn - 1));
+        };
+        Tile ring[kGroupRing];
+#pragma unroll
+        for (int u = 0; u < kGroupRing; ++u)
+            issue(ring[u], block_of(u));
+        if (APPEND && c0 == 0 && held) {
+            // Stage the held members' rows; note which last tiles take them.
+#pragma unroll
+            for (int m = 0; m < kGroupMaxMembers; ++m)
+                if ((held >> m) & 1ull)
+                    reinterpret_cast<uint32_t *>(s_new[wv][m])[lane] = new_pair[m];
+            if (hold_lane) {
+                if (wslot_lane >= 0 && wslot_lane < a.num_blocks * BS) {
+                    if ((int64_t)tblk_lane * BS + (n_lane - 1) % BS == wslot_lane)
+                        sub_lane = (n_lane - 1) % BS;
+                } else {
+                    wslot_lane = -1;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);           // LDS stores done (lgkmcnt 0)
+            __builtin_amdgcn_wave_barrier();
+        }
+        const int nit = (cn + kGroupRing - 1) / kGroupRing;
+        for (int it = 0; it + 1 < nit; ++it) {
+#pragma unroll
+            for (int u = 0; u < kGroupRing; ++u) {
+                const int k = it * kGroupRing + u;
+                consume(ring[u], c0 + k, block_of(k));
+                issue(ring[u], block_of(k + kGroupRing));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kGroupRing; ++u) {
+            const int k = (nit - 1) * kGroupRing + u;
+            if (k < cn)
+                consume(ring[u], c0 + k, block_of(k));
+        }
+    }
+    // Close the ranges that remain (the last member's, and empty ones).
+    advance_to(INT32_MAX);
+    if (cur < 0 || (col_ok && col_mem == cur))
+        fold_into_lds(R);
+
+    // Rows whose slot is not position n-1's: the row alone.
+    if (APPEND && held) {
+#pragma unroll
+        for (int m = 0; m < kGroupMaxMembers; ++m) {
+            if (!((held >> m) & 1ull))
+                continue;
+            const int64_t ws =
+                (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(wslot_lane >> 32), m)
+                           << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)wslot_lane, m));
+            const bool dn = __builtin_amdgcn_readlane((int)done_lane, m) != 0;
+            if (ws < 0 || dn)
+                continue;
+            const int64_t wblk = ws / BS;
+            const int woff = (int)(ws - wblk * BS);
+            uint16_t *kt = a.k_cache_w + (wblk * a.num_kv_heads + kvh) * (int64_t)(BS * D);
+            uint16_t *vt = a.v_cache_w + (wblk * a.num_kv_heads + kvh) * (int64_t)(BS * D);
+            const uint16_t *sn = s_new[wv][m];
+            if (lane < D / 8)
+                *reinterpret_cast<uint4 *>(kt + (lane * BS + woff) * 8) =
+                    *reinterpret_cast<const uint4 *>(sn + 8 * lane);
+            vt[lane * BS + woff] = sn[D + lane];
+        }
+    }
+
+    // Merge the wavefronts' states in wavefront order and write the rows.
+    __syncthreads();
+    if (APPEND && wv == 0) {
+        // A member whose position n-1 lies in the shared tiles (a broken
+        // precondition): its token is still written, after every wavefront
+        // has read the shared tiles.
+        for (int m = 0; m < cnt; ++m) {
+            const int nm = __builtin_amdgcn_readlane(n_lane, m);
+            if (nm <= 0 || (nm - 1) / BS >= ST)
+                continue;
+            const int64_t ws = a.slot_mapping[first + m];
+            if (ws < 0 || ws >= a.num_blocks * BS)
+                continue;
+            const int64_t wblk = ws / BS;
+            const int woff = (int)(ws - wblk * BS);
+            uint16_t *kt = a.k_cache_w + (wblk * a.num_kv_heads + kvh) * (int64_t)(BS * D);
+            uint16_t *vt = a.v_cache_w + (wblk * a.num_kv_heads + kvh) * (int64_t)(BS * D);
+            const uint16_t *kn = a.k_new + ((int64_t)(first + m) * a.num_kv_heads + kvh) * D;
+            const uint16_t *vn = a.v_new + ((int64_t)(first + m) * a.num_kv_heads + kvh) * D;
+            if (lane < D / 8)
+                *reinterpret_cast<uint4 *>(kt + (lane * BS + woff) * 8) =
+                    *reinterpret_cast<const uint4 *>(kn + 8 * lane);
+            vt[lane * BS + woff] = vn[lane];
+        }
+    }
+    if (wv > 0)
+        return;
+    RunState S;
+    state_init(S);
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) {
+        RunState o;
+        o.m = s_m[w][lane];
+        o.l = s_l[w][lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o.o[j] = s_o[w][j][lane];
+        state_merge(S, o);
+    }
+    float l = S.l;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (col_ok) {
+        const int hq = a.num_kv_heads * G;
+        const int64_t row = (int64_t)(first + col_mem) * hq + (int64_t)kvh * G + r % G;
+        float *acc = a.part_acc + row * D + 4 * g;
+        const bool none = S.m == -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4 *>(acc + 16 * j) =
+                none ? make_float4(0.f, 0.f, 0.f, 0.f)
+                     : make_float4(S.o[j][0] / l, S.o[j][1] / l, S.o[j][2] / l, S.o[j][3] / l);
+    }
+}
+
 // A shared-prefix launch in one grid: workgroups [0, shared_groups) take the
 // group pass, the rest the per-sequence pass.  The two passes read disjoint
 // partitions and write disjoint partials, so one grid lets each fill the
@@ -810,6 +1247,29 @@ int seq_wgs_per_cu()
     return per_cu;
 }
 
+// Workgroups of the whole-group kernel one compute unit holds at once
+// (cached per device; 0 if unknown).
+int group_wgs_per_cu()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 0;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(paged_decode_group_kernel<true>),
+            64 * kGroupWaves, 0) != hipSuccess)
+        return 0;
+    if (dev < 64)
+        cache[dev].store(per_cu, std::memory_order_relaxed);
+    return per_cu;
+}
+
 template <bool APPEND, bool SHARED, bool PLAN, int SPLIT>
 void launch(const DecodeArgs &a, int64_t groups, hipStream_t stream)
 {
@@ -868,6 +1328,32 @@ hipError_t launch_paged_decode_seq(const DecodeArgs &args, hipStream_t stream)
         hipLaunchKernelGGL(paged_decode_seq_kernel<true>, grid, dim3(64 * kSeqWaves), 0, stream, a);
     else
         hipLaunchKernelGGL(paged_decode_seq_kernel<false>, grid, dim3(64 * kSeqWaves), 0, stream, a);
+    return hipGetLastError();
+}
+
+// The whole-group form serves a shared-prefix step (with its appends) with
+// groups of at most kGroupMaxMembers sequences in their own order (no
+// group_order) and every (group, K/V head) workgroup resident at once.
+bool paged_decode_group_fits(const DecodeArgs &a)
+{
+    if (!a.shared_len || !a.k_new || a.group_order || a.group_size > kGroupMaxMembers ||
+        a.num_parts < 1)
+        return false;
+    const DeviceShape dev = device_shape();
+    const int per_cu = group_wgs_per_cu();
+    return dev.cus > 0 && per_cu > 0 &&
+           (int64_t)a.num_groups * a.num_kv_heads <= (int64_t)per_cu * dev.cus;
+}
+
+// The whole shared-prefix step in one launch (a.part_acc = out); requires
+// paged_decode_group_fits(a).
+hipError_t launch_paged_decode_group(const DecodeArgs &args, hipStream_t stream)
+{
+    DecodeArgs a = args;
+    const DeviceShape dev = device_shape();
+    a.plan_width = dev.cus / std::gcd(a.num_kv_heads, dev.cus);
+    const dim3 grid((unsigned)((int64_t)a.num_groups * a.num_kv_heads));
+    hipLaunchKernelGGL(paged_decode_group_kernel<true>, grid, dim3(64 * kGroupWaves), 0, stream, a);
     return hipGetLastError();
 }
 

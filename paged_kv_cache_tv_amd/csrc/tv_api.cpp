@@ -364,6 +364,98 @@ tv_status tv_paged_attention_decode_shared_append(
     return from_hip(tv::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+tv_status tv_paged_attention_decode_shared_step(
+    float *out, float *part_acc, float *part_max, float *part_sum, const uint16_t *q,
+    const uint16_t *k_new, const uint16_t *v_new, const int64_t *slot_mapping, uint16_t *k_cache,
+    uint16_t *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+    const int32_t *shared_len, const int32_t *group_order, int32_t group_size, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+    int32_t partition_size, float scale, void *stream)
+{
+    if (group_size < 1)
+        return TV_ERR_SHAPE;
+    if (num_kv_heads > 0 && num_q_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+        (int64_t)group_size * (num_q_heads / num_kv_heads) > tv::kMaxGroup)
+        return TV_ERR_UNSUPPORTED;
+    tv::DecodeArgs a;
+    const tv_status st = check_decode(a, part_acc, part_max, part_sum, q, k_cache, v_cache,
+                                      block_tables, context_lens, num_seqs, num_q_heads,
+                                      num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                      num_blocks, max_context_len, partition_size, scale);
+    if (st != TV_OK || num_seqs == 0)
+        return st;
+    if (a.num_parts == 0)                         // max_context_len == 0: out rows are 0
+        return tv_paged_attention_reduce(out, part_acc, part_max, part_sum, context_lens,
+                                         num_seqs, num_q_heads, head_dim, max_context_len,
+                                         partition_size, stream);
+    if (!out || !shared_len || !k_new || !v_new || !slot_mapping)
+        return TV_ERR_NULL;
+    if ((int64_t)num_seqs * num_q_heads > 0xffffff)
+        return TV_ERR_UNSUPPORTED;
+    if (!aligned(out, 16) || !aligned(shared_len, 4) || !aligned(group_order, 4) ||
+        !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 8))
+        return TV_ERR_ALIGNMENT;
+    if (num_blocks > INT64_MAX / block_size)
+        return TV_ERR_SHAPE;
+    a.shared_len = shared_len;
+    a.group_order = group_order;
+    a.group_size = group_size;
+    a.num_groups = (int32_t)ceil_div(num_seqs, group_size);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.slot_mapping = slot_mapping;
+    a.k_cache_w = k_cache;
+    a.v_cache_w = v_cache;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (tv::paged_decode_group_fits(a)) {
+        // One workgroup per (group, K/V head): the group's shared tiles once,
+        // every member's own tiles, the appends and the merge, in one launch.
+        a.part_acc = out;
+        a.part_max = nullptr;
+        a.part_sum = nullptr;
+        return from_hip(tv::launch_paged_decode_group(a, hs));
+    }
+    const tv_status sd = from_hip(tv::launch_paged_decode(a, hs));
+    if (sd != TV_OK)
+        return sd;
+    tv::ReduceArgs r{out, part_acc, part_max, part_sum, context_lens, num_seqs, num_q_heads,
+                     a.num_parts, partition_size, max_context_len};
+    return from_hip(tv::launch_paged_reduce(r, hs));
+}
+
+int32_t tv_paged_attention_decode_shared_step_form(int32_t num_seqs, int32_t num_q_heads,
+                                                   int32_t num_kv_heads, int32_t head_dim,
+                                                   int32_t block_size, int32_t max_context_len,
+                                                   int32_t partition_size, int32_t group_size,
+                                                   int32_t has_group_order)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || max_context_len < 0 || partition_size <= 0 || group_size < 1 ||
+        num_q_heads % num_kv_heads != 0 || partition_size % block_size != 0)
+        return -1;
+    if (head_dim != tv::kHeadDim || block_size != tv::kBlockSize ||
+        (int64_t)group_size * (num_q_heads / num_kv_heads) > tv::kMaxGroup)
+        return -1;
+    if (num_seqs == 0 || max_context_len == 0)
+        return 0;
+    tv::DecodeArgs a{};
+    static const int32_t one = 0;
+    static const uint16_t dummy = 0;
+    a.shared_len = &one;                       // only the pointers' presence is consulted
+    a.group_order = has_group_order ? &one : nullptr;
+    a.k_new = &dummy;
+    a.group_size = group_size;
+    a.num_groups = (int32_t)ceil_div(num_seqs, group_size);
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.num_parts = (int32_t)ceil_div(max_context_len, partition_size);
+    a.part_tiles = partition_size / block_size;
+    a.max_context_len = max_context_len;
+    return tv::paged_decode_group_fits(a) ? 1 : 2;
+}
+
 tv_status tv_paged_attention_decode_step(float *out, float *part_acc, float *part_max,
                                          float *part_sum, const uint16_t *q,
                                          const uint16_t *k_new, const uint16_t *v_new,

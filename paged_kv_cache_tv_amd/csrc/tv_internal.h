@@ -136,6 +136,8 @@ hipError_t launch_paged_prefill(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream);
 bool paged_decode_seq_fits(const DecodeArgs &a);
 hipError_t launch_paged_decode_seq(const DecodeArgs &a, hipStream_t stream);
+bool paged_decode_group_fits(const DecodeArgs &a);
+hipError_t launch_paged_decode_group(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_paged_reduce(const ReduceArgs &a, hipStream_t stream);
 hipError_t launch_stream_read(const StreamReadArgs &a, hipStream_t stream);
 

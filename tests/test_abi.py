@@ -412,3 +412,45 @@ def test_decode_step_noalloc_refuses_oversized_workspace(lib):
     assert call(-1, 4096, 512) == TV_ERR_SHAPE
     assert call(0, 4096, 512) == TV_OK
     assert lib.tv_status_string(TV_ERR_SCRATCH).startswith(b"TV_ERR_SCRATCH")
+
+
+def _shs(lib, S=2, hq=32, hkv=8, gs=4, mctx=64, part=32, ptrs=(BAD,) * 14):
+    return lib.tv_paged_attention_decode_shared_step(*ptrs, gs, S, hq, hkv, 64, 16, 4, 8, mctx,
+                                                     part, 0.125, None)
+
+
+def test_decode_shared_step_validation(lib):
+    """tv_paged_attention_decode_shared_step: argument errors before any launch
+    (pointer order: out, part_acc, part_max, part_sum, q, k_new, v_new,
+    slot_mapping, k_cache, v_cache, block_tables, context_lens, shared_len,
+    group_order)."""
+    assert _shs(lib, S=-1) == TV_ERR_SHAPE
+    assert _shs(lib, gs=0) == TV_ERR_SHAPE
+    assert _shs(lib, gs=5) == TV_ERR_UNSUPPORTED          # 5 x 4 columns > 16
+    assert _shs(lib, part=24) == TV_ERR_SHAPE
+    assert _shs(lib, S=0) == TV_OK
+    assert _shs(lib) == TV_ERR_ALIGNMENT                  # the decode arguments first
+    for i in (0, 5, 6, 7, 12):                            # out, k_new, v_new, slot_mapping, shared_len
+        ptrs = [ALIGNED] * 13 + [None]
+        ptrs[i] = None
+        assert _shs(lib, ptrs=tuple(ptrs)) == TV_ERR_NULL, i
+        ptrs[i] = BAD
+        assert _shs(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT, i
+    ptrs = [ALIGNED] * 13 + [BAD]                         # group_order misaligned
+    assert _shs(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
+    ptrs = [ALIGNED] * 13 + [None]
+    ptrs[1] = None                                        # the workspace is always required
+    assert _shs(lib, ptrs=tuple(ptrs)) == TV_ERR_NULL
+    # max_context_len == 0: the merge alone zeroes out; out is still checked.
+    assert _shs(lib, mctx=0, ptrs=(None,) + (BAD,) * 13) == TV_ERR_NULL
+
+
+def test_decode_shared_step_form_host_cases(lib):
+    f = lib.tv_paged_attention_decode_shared_step_form
+    assert f(0, 32, 8, 64, 16, 4096, 512, 4, 0) == 0
+    assert f(64, 32, 8, 64, 16, 0, 512, 4, 0) == 0
+    assert f(64, 32, 8, 64, 16, 4096, 512, 5, 0) == -1   # 5 x 4 columns > 16
+    assert f(64, 32, 8, 64, 16, 4096, 512, 0, 0) == -1
+    assert f(64, 32, 8, 128, 16, 4096, 512, 4, 0) == -1
+    assert f(64, 32, 8, 64, 16, 4096, 500, 4, 0) == -1
+    assert f(-1, 32, 8, 64, 16, 4096, 512, 4, 0) == -1

@@ -255,3 +255,137 @@ def test_shared_groups_in_any_order(dev, append):
     _same_partials(part_s, part_c, b.context_lens, part)
     assert np.array_equal(out_s.view(np.uint32), out_c.view(np.uint32))
     assert np.array_equal(pools_s[0], pools_c[0]) and np.array_equal(pools_s[1], pools_c[1])
+
+
+# ---------------------------------------------------------------------------
+# tv_paged_attention_decode_shared_step: the parallel-sampling step in one
+# call.  In its one-launch form (groups of up to 4 in their own order, every
+# (group, K/V head) workgroup resident) the shared tiles and each member's own
+# tiles are cut into 8 equal parts per range instead of the workspace's
+# partitions, so the output equals the two-call step (shared append + merge)
+# to rounding; the pools equal it bit for bit.
+# ---------------------------------------------------------------------------
+
+def _run_shared_step(b, dev, part, shared, group_size, lens=None, group_order=None):
+    import torch
+    import paged_kv_cache_tv_amd as tv
+    lens = b.context_lens if lens is None else lens
+    kc, vc = tv.new_pools(b.num_blocks, b.num_kv_heads, b.head_dim, b.block_size, dev,
+                          fill=W.BF16_NAN)
+    k, v, sl = b.fill_inputs()
+    live = sl >= 0
+    tv.cache_write(_to_dev(k[live], dev), _to_dev(v[live], dev), kc, vc, _to_dev(sl[live], dev))
+    sk, sv, ss = b.step_inputs()
+    mc = int(lens.max())
+    ws = tv.new_workspace(b.num_seqs, b.num_q_heads, b.head_dim, mc, part, dev)
+    for t in ws:
+        t.fill_(float("nan"))
+    out = torch.full((b.num_seqs, b.num_q_heads, b.head_dim), float("nan"), dtype=torch.float32,
+                     device=dev)
+    q, bt, cl = _to_dev(b.q, dev), _to_dev(b.block_tables, dev), _to_dev(lens, dev)
+    go = None if group_order is None else _to_dev(group_order, dev)
+    tv.paged_attention_decode_shared_step(out, ws, q, _to_dev(sk, dev), _to_dev(sv, dev),
+                                          _to_dev(ss.astype(np.int64), dev), kc, vc, bt, cl,
+                                          _to_dev(shared, dev), group_size, mc, part, b.scale,
+                                          group_order=go)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (kc.cpu().numpy().view(np.uint16), vc.cpu().numpy().view(np.uint16))
+
+
+def test_shared_step_workload(dev, oracle_lib):
+    """The shared-prefix workload's step in one launch: pools bit-exact against
+    the oracle's cache write, output within the oracle bars, run-to-run
+    identical, and within 2e-6 of the two-call step."""
+    import paged_kv_cache_tv_amd as tv
+    b = W.make_workload(4)
+    shared = np.full(64, 1024, np.int32)
+    mc = int(b.context_lens.max())
+    assert tv.decode_shared_step_form(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                      b.block_size, mc, 512, 4) == 1
+    out, (kc, vc) = _run_shared_step(b, dev, 512, shared, 4)
+    out2, _ = _run_shared_step(b, dev, 512, shared, 4)
+    assert np.array_equal(out.view(np.uint32), out2.view(np.uint32)), "two calls differ"
+    two, _, _ = _run_append(b, dev, 512, shared, 4)
+    d = np.abs(out - two).max()
+    print(f"shared step vs two calls: max_abs={d:.3e}", flush=True)
+    assert d <= 2e-6
+    ref, kc_ref, vc_ref = O.decode_step(oracle_lib, b)
+    assert np.array_equal(kc, kc_ref), "K pool differs from the oracle's cache write"
+    assert np.array_equal(vc, vc_ref), "V pool differs from the oracle's cache write"
+    err = np.abs(out.astype(np.float64) - ref)
+    print(f"shared step: max_abs={err.max():.3e} mean_abs={err.mean():.3e}", flush=True)
+    assert err.max() <= 1e-4 and err.mean() <= 1e-6
+
+
+@pytest.mark.parametrize("samples,prefix,part,hq,hkv", [
+    (3, 704, 64, 32, 8),       # prefix not a whole number of partitions
+    (4, 256, 64, 32, 8),       # a member's last position in a shared partition
+    (2, 1536, 512, 32, 8),
+    (1, 512, 128, 32, 8),      # groups of one
+    (4, 608, 128, 16, 16),     # one query head per K/V head: 4 columns
+    (2, 304, 64, 16, 2),       # 8 query heads per K/V head: 16 columns
+])
+def test_shared_step_ragged_groups(dev, samples, prefix, part, hq, hkv):
+    """Ragged groups in one launch: a partial last group, a member cut below the
+    prefix, a group that declares no sharing, an empty context and a skipped
+    slot; output within 2e-6 of the two-call step (zero rows for the empty
+    context; the sequence whose slot is skipped attends its NaN-poisoned last
+    position in both), pools bit for bit the two-call step's."""
+    import paged_kv_cache_tv_amd as tv
+    rng = np.random.default_rng(150 + samples + part + hkv)
+    prompts = 5
+    priv = rng.integers(0, 300, prompts * samples)
+    b = W.make_shared_prefix_batch(prompts, samples, prefix, priv, 151 + prefix,
+                                   num_q_heads=hq, num_kv_heads=hkv)
+    S = b.num_seqs - 1 if samples > 1 else b.num_seqs
+    b.context_lens = b.context_lens[:S].copy()
+    b.block_tables = b.block_tables[:S]
+    b.q = b.q[:S]
+    b.new_slots = b.new_slots[:S].copy()
+    b.new_rows = b.new_rows[:S]
+    lens = b.context_lens.copy()
+    if samples > 1:
+        lens[samples] = prefix // 2                  # member of group 1 cut below the prefix
+    lens[-1] = 0                                     # an empty context
+    b.new_slots[1] = -1                              # a skipped slot
+    ngroups = -(-S // samples)
+    shared = np.full(ngroups, prefix, np.int32)
+    shared[min(2, ngroups - 1)] = 0                  # no sharing declared
+    mc = int(lens.max())
+    assert tv.decode_shared_step_form(S, hq, hkv, 64, 16, mc, part, samples) == 1
+    out, pools = _run_shared_step(b, dev, part, shared, samples, lens)
+    two, _, pools2 = _run_append(b, dev, part, shared, samples, lens)
+    nan = np.isnan(out)
+    assert np.array_equal(nan, np.isnan(two)), "NaN rows differ from the two-call step"
+    assert not np.delete(nan, 1, axis=0).any(), "NaN outside the skipped slot's sequence"
+    assert not out[lens == 0].any(), "an empty context gives zero rows"
+    d = np.abs(np.where(nan, 0.0, out - two)).max()
+    print(f"ragged shared step ({samples}, {prefix}, {part}, {hq}/{hkv}): max_abs={d:.3e}",
+          flush=True)
+    assert d <= 2e-6
+    assert np.array_equal(pools[0], pools2[0]) and np.array_equal(pools[1], pools2[1])
+
+
+@pytest.mark.parametrize("case", ["group_order", "group_of_8"])
+def test_shared_step_two_launch_forms(dev, case):
+    """Outside the one-launch form (a member order, or groups of more than 4)
+    the step is the shared append and the merge: bit for bit the two calls."""
+    import paged_kv_cache_tv_amd as tv
+    b = W.make_workload(4)
+    S = b.num_seqs
+    part = 512
+    mc = int(b.context_lens.max())
+    if case == "group_order":
+        gs, order = 4, np.arange(S, dtype=np.int32)
+        shared = np.full(S // 4, 1024, np.int32)
+    else:
+        b.q = b.q[:, :16].copy()                     # 16 query heads: G = 2, groups of 8
+        b.num_q_heads = 16
+        gs, order = 8, None
+        shared = np.full(S // 8, 1024, np.int32)
+    assert tv.decode_shared_step_form(S, b.num_q_heads, b.num_kv_heads, 64, 16, mc, part, gs,
+                                      order is not None) == 2
+    out, pools = _run_shared_step(b, dev, part, shared, gs, group_order=order)
+    two, _, pools2 = _run_append(b, dev, part, shared, gs)
+    assert np.array_equal(out.view(np.uint32), two.view(np.uint32))
+    assert np.array_equal(pools[0], pools2[0]) and np.array_equal(pools[1], pools2[1])
