@@ -1,4 +1,5 @@
-// Paged GQA decode attention, partition pass, for gfx950.
+// Paged GQA decode attention for gfx950: the partition pass, and the whole
+// decode step in one launch (whole-sequence and whole-group forms).
 //
 // What is computed ("vLLM" page, sections "가상 메모리 방식의 해결" and "Flash
 // Attention"; "tiny-vllm 씹뜯맛즐 - (1)" page, section 2 on GQA): for one
@@ -7,7 +8,14 @@
 // through the sequence's block table.  The softmax is accumulated online: a
 // running maximum and running sum per query head, rescaling the partial
 // output whenever the maximum grows.  The partition's (max, sum, output)
-// triple is written for the merge kernel.
+// triple is written for the merge kernel.  In the one-launch forms a
+// workgroup takes a whole (sequence, K/V head) -- or a whole (group of
+// sequences sharing a prefix, K/V head) -- cuts its tiles into equal ranges,
+// one per wavefront, merges the ranges' triples in LDS by the same rule and
+// writes the normalised output rows (paged_decode_seq_kernel,
+// paged_decode_group_kernel).  With the cache write folded in, the
+// wavefront holding a sequence's last tile substitutes the new token in
+// registers and stores that tile back whole.
 //
 // Mapping to CDNA4:
 //   * One workgroup per (sequence, K/V head, partition), of 4 wavefronts or
