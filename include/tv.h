@@ -343,12 +343,13 @@ tv_status tv_paged_attention_decode_shared_append(
  *   MI355X): one launch with one 8-wavefront workgroup per (group, K/V
  *   head).  The group's shared tiles (its shared length cut as for
  *   tv_paged_attention_decode_shared) are read once with every member's
- *   query heads, each member's other tiles with its own; each of these
- *   ranges is cut into 8 equal consecutive parts, one per wavefront, and
- *   the parts merge in on-chip memory.  The workspace is neither read nor
- *   written (it must still be non-NULL and aligned), and out equals the
- *   two-call result up to fp32 rounding (the parts are not its 512-token
- *   partitions).
+ *   query heads, each member's other tiles with its own; the group's tiles
+ *   (the shared ones, then each member's) are cut into 8 equal consecutive
+ *   parts, one per wavefront, and the parts merge in on-chip memory.  The
+ *   workspace is neither read nor written (it must still be non-NULL and
+ *   aligned), and out equals the two-call result up to rounding, within
+ *   2^-16 * max|V| as for tv_paged_attention_decode_step's one-launch forms
+ *   (the parts are not its 512-token partitions).
  *   otherwise: tv_paged_attention_decode_shared_append, then
  *   tv_paged_attention_reduce, on `stream`; out bitwise the two calls'.
  * With max_context_len == 0 every row of out is set to zero.
@@ -427,14 +428,17 @@ tv_status tv_paged_attention_reduce(float *out, const float *part_acc,
  *   P == 1: the partition pass divides by the sum itself and writes out; one
  *     launch; out is bitwise what tv_paged_attention_decode_append followed
  *     by tv_paged_attention_reduce gives.
- *   2 <= P <= 8, num_seqs <= 512 and num_seqs * num_kv_heads within one
+ *   2 <= P <= 8, num_seqs <= 256 and num_seqs * num_kv_heads within one
  *     resident wave of workgroups on the device: one launch with one
  *     workgroup per (sequence, K/V head); each sequence's context is cut
  *     into 8 equal consecutive ranges (each at most partition_size tokens),
  *     one per wavefront, and the 8 partial results are merged in on-chip
  *     memory by the same log-sum-exp rule.  The ranges differ from the
  *     partition_size partitions of the two-call form, so out equals that
- *     form's result up to fp32 rounding (a few ulp), not bitwise.
+ *     form's result up to rounding, not bitwise: both fold the softmax
+ *     weights into V with at least 16 significant bits against an exact
+ *     fp32 sum, so the two are within 2^-16 * max|V| (plus fp32 summation
+ *     order) of each other.
  *   otherwise: tv_paged_attention_decode_append followed by
  *     tv_paged_attention_reduce on the same stream, two launches through the
  *     workspace; out is bitwise what those two calls give.

@@ -106,6 +106,17 @@ def _call_step(db):
     return got.cpu().numpy()
 
 
+def _forms_bar(batch):
+    """How far two correct orders of the same step may differ.  Each form
+    folds P into V as bf16 hi + lo parts, at least 16 significant bits
+    (relative error <= 2^-17 per weight), against an exact fp32 sum, so each
+    output is within 2^-17 * max|V| of the exactly weighted mean, and two
+    forms that weight against different maxima within twice that; 1e-6
+    covers their different fp32 summation orders."""
+    v = W.bf16_bits_to_float32(batch.kv_v)
+    return 2.0 ** -16 * float(np.abs(v[np.isfinite(v)]).max()) + 1e-6
+
+
 # The form tv_paged_attention_decode_step takes per workload on MI355X: the
 # whole-sequence launch (2 to 8 partitions, every (sequence, K/V head)
 # workgroup resident at once) for 8 x U[128, 1024] and 64 x U[512, 4096]; one
@@ -122,7 +133,7 @@ def test_decode_step_call_workloads(dev, oracle_lib, index):
     launches, the output is the two-launch step's bit for bit; in the
     whole-sequence form each context is split into 8 equal ranges instead of
     the workspace's 512-token partitions (none longer than a partition), so
-    the two agree to rounding (2e-6)."""
+    the two agree to rounding (_forms_bar)."""
     batch = W.make_workload(index)
     ref, kc_ref, vc_ref = _oracle_step(oracle_lib, ("workload", index), batch)
     two, db = _gpu_step(batch, dev, fused=True)
@@ -133,8 +144,9 @@ def test_decode_step_call_workloads(dev, oracle_lib, index):
     assert form == _STEP_FORM[index], f"workload {index}: step form {form}"
     got = _call_step(db)
     assert np.array_equal(got, _call_step(db)), f"workload {index}: two calls differ"
-    if form == 2:
-        assert np.abs(got - two).max() <= 2e-6, f"workload {index}: one call far from two launches"
+    if form == 2:                                 # one launch: other ranges
+        assert np.abs(got - two).max() <= _forms_bar(batch), \
+            f"workload {index}: one call far from two launches"
     else:
         assert np.array_equal(got, two), f"workload {index}: one call differs from two launches"
     kc, vc = db.pools_numpy()
@@ -151,6 +163,8 @@ _WHOLE_SEQUENCE_CASES = [
     (84, (9, 1, 2048), 16, 1, 512, None),            # the largest group (16 query heads)
     (85, (40, 1, 1000), 8, 8, 256, None),            # one query head per K/V head
     (86, (3, 3000, 4000), 32, 8, 1024, None),        # 4 partitions of 1024
+    (87, (63, 0, 2000), 32, 8, 512, 2048),           # an odd count of sequences
+    (88, [0] * 20 + [4096] * 20 + [1] * 20, 32, 8, 512, None),   # empty, full and 1-token
 ]
 
 
@@ -167,7 +181,7 @@ def test_decode_step_whole_sequence_form(dev, oracle_lib, case):
         lens = np.random.default_rng(seed).integers(lo, hi, size=n_seq, endpoint=True)
     lens = np.asarray(lens)
     mc = int(lens.max()) if bound is None else bound
-    assert 2 <= -(-mc // part) <= 8 and len(lens) * hkv <= 512
+    assert 2 <= -(-mc // part) <= 8
     batch = W.make_batch(lens, seed, num_q_heads=hq, num_kv_heads=hkv, table_width=mc // 16 + 1)
     ref, kc_ref, vc_ref = O.decode_step(oracle_lib, batch)
     two, db = _gpu_step(batch, dev, partition_size=part, max_context_len=mc, fused=True)
@@ -175,7 +189,7 @@ def test_decode_step_whole_sequence_form(dev, oracle_lib, case):
     assert tv.decode_step_form(len(lens), hq, hkv, 64, 16, mc, part) == 2
     got = _call_step(db)
     assert np.array_equal(got, _call_step(db)), "two calls differ"
-    assert np.abs(got - two).max() <= 2e-6, "one call far from the two-launch step"
+    assert np.abs(got - two).max() <= _forms_bar(batch), "one call far from the two-launch step"
     assert not got[lens == 0].any(), "empty contexts must give zero rows"
     kc, vc = db.pools_numpy()
     assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)

@@ -266,6 +266,15 @@ def test_shared_groups_in_any_order(dev, append):
 # to rounding; the pools equal it bit for bit.
 # ---------------------------------------------------------------------------
 
+def _forms_bar(b):
+    """How far two correct orders of the same step may differ: each folds P
+    into V as bf16 hi + lo parts (relative error <= 2^-17 per weight) against
+    an exact fp32 sum, so each is within 2^-17 * max|V| of the exactly
+    weighted mean; 1e-6 covers their fp32 summation orders."""
+    v = W.bf16_bits_to_float32(b.kv_v)
+    return 2.0 ** -16 * float(np.abs(v[np.isfinite(v)]).max()) + 1e-6
+
+
 def _run_shared_step(b, dev, part, shared, group_size, lens=None, group_order=None):
     import torch
     import paged_kv_cache_tv_amd as tv
@@ -295,7 +304,7 @@ def _run_shared_step(b, dev, part, shared, group_size, lens=None, group_order=No
 def test_shared_step_workload(dev, oracle_lib):
     """The shared-prefix workload's step in one launch: pools bit-exact against
     the oracle's cache write, output within the oracle bars, run-to-run
-    identical, and within 2e-6 of the two-call step."""
+    identical, and within rounding (_forms_bar) of the two-call step."""
     import paged_kv_cache_tv_amd as tv
     b = W.make_workload(4)
     shared = np.full(64, 1024, np.int32)
@@ -308,7 +317,7 @@ def test_shared_step_workload(dev, oracle_lib):
     two, _, _ = _run_append(b, dev, 512, shared, 4)
     d = np.abs(out - two).max()
     print(f"shared step vs two calls: max_abs={d:.3e}", flush=True)
-    assert d <= 2e-6
+    assert d <= _forms_bar(b)
     ref, kc_ref, vc_ref = O.decode_step(oracle_lib, b)
     assert np.array_equal(kc, kc_ref), "K pool differs from the oracle's cache write"
     assert np.array_equal(vc, vc_ref), "V pool differs from the oracle's cache write"
@@ -328,7 +337,7 @@ def test_shared_step_workload(dev, oracle_lib):
 def test_shared_step_ragged_groups(dev, samples, prefix, part, hq, hkv):
     """Ragged groups in one launch: a partial last group, a member cut below the
     prefix, a group that declares no sharing, an empty context and a skipped
-    slot; output within 2e-6 of the two-call step (zero rows for the empty
+    slot; output within rounding of the two-call step (zero rows for the empty
     context; the sequence whose slot is skipped attends its NaN-poisoned last
     position in both), pools bit for bit the two-call step's."""
     import paged_kv_cache_tv_amd as tv
@@ -362,7 +371,7 @@ def test_shared_step_ragged_groups(dev, samples, prefix, part, hq, hkv):
     d = np.abs(np.where(nan, 0.0, out - two)).max()
     print(f"ragged shared step ({samples}, {prefix}, {part}, {hq}/{hkv}): max_abs={d:.3e}",
           flush=True)
-    assert d <= 2e-6
+    assert d <= _forms_bar(b)
     assert np.array_equal(pools[0], pools2[0]) and np.array_equal(pools[1], pools2[1])
 
 
