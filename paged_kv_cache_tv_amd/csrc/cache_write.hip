@@ -14,6 +14,23 @@
 namespace tv {
 namespace {
 
+// Streaming (non-temporal) 16-byte loads and stores for the bulk form: a
+// prompt's K/V rows are read once and its pool tiles are not read back by
+// this kernel, so neither should displace other data in the caches.
+// Measured on 16,384 prompt tokens: the plain write 17.1 -> 12.7 us and the
+// RoPE write 20.9 -> 17.0 us (launch loops, same process).
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void nt_store(const uint4 &x, uint4 *p)
+{
+    const nt_u32x4 v = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<nt_u32x4 *>(p));
+}
+__device__ __forceinline__ uint4 nt_load(const uint4 *p)
+{
+    const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4 *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 constexpr int kWavesPerGroup = 4;      // wavefronts per workgroup (one token each, unstaged forms)
 constexpr int kTokensPerGroup = 16;    // tokens per workgroup, staged form (4 per wavefront)
 constexpr int64_t kStagedFrom = 512;   // launches of at least this many tokens use the staged form
@@ -49,30 +66,42 @@ void cache_write_kernel(CacheWriteArgs a)
     // the 16 tokens of one chunk sit on distinct banks.
     constexpr int kKStride = 65;
     __shared__ uint4 s_k[STAGED ? kTokensPerGroup * kKStride : 1];
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar token loads
     const int lane = threadIdx.x & 63;
     const int row = a.num_kv_heads * a.head_dim;
     const int chunks = row >> 3;
     // Wavefront w takes tokens kPerWave*w .. kPerWave*w + kPerWave - 1 of the
     // workgroup.  Every load the common case (num_kv_heads * head_dim <= 512)
-    // needs -- each token's slot, its first K and V chunk per lane and, with
-    // ROPE, its position -- is issued before any is used, so the wavefront
-    // waits on memory once.
-    int64_t toks[kPerWave], slots[kPerWave];
+    // needs is issued before any is used, so the wavefront waits on memory
+    // once: first each token's slot and, with ROPE, its position (wave-uniform
+    // addresses: scalar loads), then its first K and V chunk per lane.  The
+    // row loads are unconditional (a token past the end reads the last token's
+    // row, a lane past the row its last chunk; neither value is used), so no
+    // wait is tied to a branch around them.
+    int64_t toks[kPerWave], tcs[kPerWave], slots[kPerWave];
     uint4 k0s[kPerWave], v0s[kPerWave];
     int poss[kPerWave];
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
         toks[i] = (int64_t)blockIdx.x * kTok + w * kPerWave + i;
-        const bool live = toks[i] < a.num_tokens;
-        const bool have0 = live && lane < chunks;
-        k0s[i] = have0 ? reinterpret_cast<const uint4 *>(a.k + toks[i] * row)[lane]
-                       : make_uint4(0, 0, 0, 0);
-        v0s[i] = have0 ? reinterpret_cast<const uint4 *>(a.v + toks[i] * row)[lane]
-                       : make_uint4(0, 0, 0, 0);
-        slots[i] = live ? a.slot_mapping[toks[i]] : -1;
-        poss[i] = ROPE && live ? a.positions[toks[i]] : 0;
+        tcs[i] = toks[i] < a.num_tokens ? toks[i] : a.num_tokens - 1;
+        slots[i] = a.slot_mapping[tcs[i]];
+        poss[i] = ROPE ? a.positions[tcs[i]] : 0;
     }
+    const int cl = lane < chunks ? lane : chunks - 1;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+        const uint4 *krow = reinterpret_cast<const uint4 *>(a.k + tcs[i] * row) + cl;
+        const uint4 *vrow = reinterpret_cast<const uint4 *>(a.v + tcs[i] * row) + cl;
+        // RoPE reads K with cached loads: style 1 re-reads the row as 8-byte
+        // pieces, which a streaming load would have pushed out.
+        k0s[i] = STAGED && !ROPE ? nt_load(krow) : *krow;
+        v0s[i] = STAGED ? nt_load(vrow) : *vrow;
+    }
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i)
+        if (toks[i] >= a.num_tokens)
+            slots[i] = -1;
     const float f_lane = ROPE ? a.inv_freq[lane % (a.head_dim >> 1)] : 0.f;
     bool full = false;
     int64_t s0 = 0;
@@ -210,8 +239,8 @@ void cache_write_kernel(CacheWriteArgs a)
     const int64_t vblk = s0 / kTokensPerGroup;
     // K: piece u = chunk * 16 + token of the block's contiguous K region.
     for (int u = threadIdx.x; u < chunks * kTokensPerGroup; u += 64 * kWavesPerGroup)
-        reinterpret_cast<uint4 *>(a.k_cache + vblk * (int64_t)row * kTokensPerGroup)[u] =
-            s_k[(u & (kTokensPerGroup - 1)) * kKStride + (u >> 4)];
+        nt_store(s_k[(u & (kTokensPerGroup - 1)) * kKStride + (u >> 4)],
+                 reinterpret_cast<uint4 *>(a.k_cache + vblk * (int64_t)row * kTokensPerGroup) + u);
     for (int t = threadIdx.x; t < 2 * row; t += 64 * kWavesPerGroup) {
         const int e = t >> 1;                                  // h * head_dim + d
         const int t0 = 8 * (t & 1);
@@ -222,9 +251,9 @@ void cache_write_kernel(CacheWriteArgs a)
                    ((uint32_t)sv[(t0 + 2 * i + 1) * 512 + e] << 16);
         const int h = e / a.head_dim;
         const int d = e - h * a.head_dim;
-        *reinterpret_cast<uint4 *>(a.v_cache + ((vblk * a.num_kv_heads + h) * a.head_dim + d) *
-                                                   a.block_size + t0) =
-            make_uint4(o[0], o[1], o[2], o[3]);
+        nt_store(make_uint4(o[0], o[1], o[2], o[3]),
+                 reinterpret_cast<uint4 *>(a.v_cache + ((vblk * a.num_kv_heads + h) * a.head_dim + d) *
+                                           a.block_size + t0));
     }
 }
 
