@@ -88,6 +88,7 @@ void cache_write_kernel(CacheWriteArgs a)
         slots[i] = a.slot_mapping[tcs[i]];
         poss[i] = ROPE ? a.positions[tcs[i]] : 0;
     }
+    const float f_lane = ROPE ? a.inv_freq[lane % (a.head_dim >> 1)] : 0.f;
     const int cl = lane < chunks ? lane : chunks - 1;
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
@@ -102,7 +103,6 @@ void cache_write_kernel(CacheWriteArgs a)
     for (int i = 0; i < kPerWave; ++i)
         if (toks[i] >= a.num_tokens)
             slots[i] = -1;
-    const float f_lane = ROPE ? a.inv_freq[lane % (a.head_dim >> 1)] : 0.f;
     bool full = false;
     int64_t s0 = 0;
     if (STAGED) {
