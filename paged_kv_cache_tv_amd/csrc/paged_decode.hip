@@ -215,9 +215,15 @@ __device__ Unit plan_unit(const DecodeArgs &a, int j, int lane)
     int len[kPlanChunks];
 #pragma unroll
     for (int k = 0; k < kPlanChunks; ++k) {
+        // Unconditional loads (a lane past the batch reads the last length),
+        // so all of them are in flight before the first is waited for.
         const int s = k * 64 + lane;
-        len[k] = s < a.num_seqs ? a.context_lens[s] : 0;
+        len[k] = a.context_lens[s < a.num_seqs ? s : a.num_seqs - 1];
     }
+#pragma unroll
+    for (int k = 0; k < kPlanChunks; ++k)
+        if (k * 64 + lane >= a.num_seqs)
+            len[k] = 0;
     int last[kPlanChunks], nparts[kPlanChunks];
     int F = 0, L = 0;                            // partitions in step 1; sequences in step 2
     Unit u = {-1, 0};
@@ -354,7 +360,12 @@ __device__ int seq_unit(const DecodeArgs &a, int k, int lane)
 #pragma unroll
     for (int kk = 0; kk < kPlanChunks; ++kk) {
         const int s = kk * 64 + lane;
-        int n = s < S ? a.context_lens[s] : 0;
+        tiles[kk] = a.context_lens[s < S ? s : S - 1];   // all loads issued before any is used
+    }
+#pragma unroll
+    for (int kk = 0; kk < kPlanChunks; ++kk) {
+        const int s = kk * 64 + lane;
+        int n = tiles[kk];
         n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
         tiles[kk] = s < S ? (n + BS - 1) / BS : -1;   // -1: no sequence
     }
@@ -835,19 +846,30 @@ __device__ int group_unit(const DecodeArgs &a, int k, int lane)
     for (int kk = 0; kk < kPlanChunks; ++kk) {
         const int gi = kk * 64 + lane;
         tiles[kk] = -1;                          // -1: no group
-        if (gi < NG) {
-            const int f = gi * a.group_size;
+        if (kk * 64 < NG) {
+            // Every length and the shared length are loaded (clamped to the
+            // batch) before any is used, so the lane waits on memory once.
+            const int gc = gi < NG ? gi : NG - 1;
+            const int f = gc * a.group_size;
             const int cnt = min(a.group_size, a.num_seqs - f);
-            int sh = a.shared_len[gi];
+            int sh = a.shared_len[gc];
+            int nm[kGroupMaxMembers];
+#pragma unroll
+            for (int m = 0; m < kGroupMaxMembers; ++m)
+                nm[m] = a.context_lens[min(f + m, a.num_seqs - 1)];
             int sum = 0;
-            for (int m = 0; m < cnt; ++m) {
-                int n = a.context_lens[f + m];
+#pragma unroll
+            for (int m = 0; m < kGroupMaxMembers; ++m) {
+                // Selects, not a branch on m < cnt: a branch would let the
+                // compiler sink each load into it and wait for each in turn.
+                int n = nm[m];
                 n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
-                sh = min(sh, n);
-                sum += (n + BS - 1) / BS;
+                sh = m < cnt ? min(sh, n) : sh;
+                sum += m < cnt ? (n + BS - 1) / BS : 0;
             }
             const int st = sh > 0 ? (sh / (a.part_tiles * BS)) * a.part_tiles : 0;
-            tiles[kk] = sum - (cnt - 1) * st;    // the shared tiles counted once
+            if (gi < NG)
+                tiles[kk] = sum - (cnt - 1) * st;    // the shared tiles counted once
         }
     }
     const int bound = kGroupMaxMembers * ((a.max_context_len + BS - 1) / BS);
