@@ -7,7 +7,8 @@ smaller launches.  The large call here mixes both, plus a ragged tail and a
 V pool that is only 2-byte aligned (which must fall back to the per-token
 path), with and without RoPE; the small call writes the same pattern once.
 Pools are compared bit for bit (K within the RoPE bound of
-tests/test_gpu_rope.py when rotated).
+tests/test_gpu_rope.py when rotated).  The bulk form is also run at rows
+narrower and wider than a wavefront's 64 sixteen-byte chunks.
 """
 
 import numpy as np
@@ -109,3 +110,53 @@ def test_cache_write_paths(dev, oracle_lib, aligned, rope_style, reps):
     assert np.array_equal(kc_h[mask], kr[mask]), "K outside the written slots"
     got_k = kc_h[blk, :, :, off, :].reshape(live.sum(), HKV, D)
     _check_rotated(oracle_lib, got_k, k[live], pos[live], f, rope_style, "K of both paths")
+
+
+@pytest.mark.parametrize("heads,head_dim", [(2, 64), (1, 16), (4, 128), (16, 64)],
+                         ids=["row128", "row16", "row512-d128", "row1024"])
+@pytest.mark.parametrize("rope_style", [None, 0, 1], ids=["plain", "rope0", "rope1"])
+def test_cache_write_bulk_row_widths(dev, oracle_lib, heads, head_dim, rope_style):
+    """The bulk form (launches of 512 tokens or more) at rows narrower than a
+    wavefront's 64 chunks (lanes past the row re-read its last chunk and
+    store nothing) and wider (the chunks past 64 go round again), with full
+    blocks in order, a block written backwards, skipped slots and a ragged
+    last group of tokens: pools bit-exact against the oracle (K within the
+    RoPE bound when rotated), every other element untouched."""
+    import torch
+    import paged_kv_cache_tv_amd as tv
+    from test_gpu_rope import _check_rotated
+    rng = np.random.default_rng(130 + heads * head_dim + (rope_style or 0))
+    nb, bs = 80, 16
+    full = np.arange(40 * bs)                                   # blocks 0..39 in order
+    back = 41 * bs + np.arange(bs)[::-1]                         # block 41 backwards
+    tail = 50 * bs + np.arange(13)                               # ragged end of the launch
+    slots = np.concatenate([full, back, [-1, nb * bs, -7], tail]).astype(np.int64)
+    T = len(slots)
+    assert T >= 512
+    k = W.round_to_bf16_bits(rng.standard_normal((T, heads, head_dim)).astype(np.float32))
+    v = W.round_to_bf16_bits(rng.standard_normal((T, heads, head_dim)).astype(np.float32))
+    pos = rng.integers(0, 100000, T).astype(np.int32)
+    f = W.rope_inv_freq(head_dim, 500000.0)
+    kc, vc = tv.new_pools(nb, heads, head_dim, bs, dev, fill=W.BF16_NAN)
+    if rope_style is None:
+        tv.cache_write(_to_dev(k, dev), _to_dev(v, dev), kc, vc, _to_dev(slots, dev))
+        kin = k
+    else:
+        tv.cache_write_rope(_to_dev(k, dev), _to_dev(v, dev), kc, vc, _to_dev(slots, dev),
+                            _to_dev(pos, dev), _to_dev(f, dev), rope_style)
+        kin = oracle_lib.rope(k, pos, f, rope_style)[1]
+    torch.cuda.synchronize()
+    kr, vr = O.Oracle.new_pools(nb, heads, head_dim, bs)
+    oracle_lib.cache_write(kin, v, kr, vr, slots)
+    kc_h, vc_h = kc.cpu().numpy().view(np.uint16), vc.cpu().numpy().view(np.uint16)
+    assert np.array_equal(vc_h, vr), "V pool"
+    if rope_style is None:
+        assert np.array_equal(kc_h, kr), "K pool"
+        return
+    live = (slots >= 0) & (slots < nb * bs)
+    blk, off = slots[live] // bs, slots[live] % bs
+    mask = np.ones(kc_h.shape, bool)
+    mask[blk, :, :, off, :] = False
+    assert np.array_equal(kc_h[mask], kr[mask]), "K outside the written slots"
+    got_k = kc_h[blk, :, :, off, :].reshape(live.sum(), heads, head_dim)
+    _check_rotated(oracle_lib, got_k, k[live], pos[live], f, rope_style, "K, bulk form")
