@@ -86,7 +86,7 @@ constexpr int kPairs = kChunkBlocks / 2;         // 32-key steps of a chunk, one
 constexpr int kTileBytes = BS * D * 2;           // one (block, K/V head) tile: 2 KiB
 constexpr int kHalfBytes = kChunkBlocks * kTileBytes;   // K (or V) of one chunk: 16 KiB
 constexpr int kBufBytes = 2 * kHalfBytes;        // K then V of one chunk
-constexpr float kLaneSumLimit = 256.0f;          // a lane's weights of 32 keys may sum to this
+constexpr float kLaneSumLimit = 256.0f;          // a lane's 16 weights of a 32-key step may sum to this
 static_assert(D == 64 && BS == 16, "tile layout assumes 64 dims and 16-token blocks");
 
 __device__ __forceinline__ unsigned zero_from(unsigned w, int lim, int e)
@@ -126,8 +126,9 @@ __device__ __forceinline__ float pair_sum(float x)
     return a + b;
 }
 
-// Copy 1 KiB with one wavefront: lane l moves the 16 bytes at src + off(l)
-// to lds + 16 l, straight from memory to LDS (no registers).
+// Copy 1 KiB with one wavefront: lane l moves the 16 bytes at its own src
+// to lds + 16 l (lds is the wavefront's base, the same in every lane),
+// straight from memory to LDS without passing through registers.
 __device__ __forceinline__ void copy_to_lds(const char *src, char *lds)
 {
     __builtin_amdgcn_global_load_lds((const TV_GLOBAL void *)src, (TV_LDS void *)lds, 16, 0, 0);
@@ -183,8 +184,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
     const int pos = base_pos + qi;
     {
         const u32x4 zero = {0u, 0u, 0u, 0u};
+        const int qa = row_ok ? qi : 0;                       // an existing row for the address
         const u32x4 *qp = reinterpret_cast<const u32x4 *>(
-            a.q + ((int64_t)(q0 + qi) * Hq + kvh * G + col % G) * D + 8 * hh);
+            a.q + ((int64_t)(q0 + qa) * Hq + kvh * G + col % G) * D + 8 * hh);
 #pragma unroll
         for (int d16 = 0; d16 < 4; ++d16)
             qop[d16] = __builtin_bit_cast(bf16x8, row_ok ? qp[2 * d16] : zero);
