@@ -14,9 +14,10 @@
 namespace tv {
 namespace {
 
-// Streaming (non-temporal) 16-byte loads and stores for the bulk form: a
-// prompt's K/V rows are read once and its pool tiles are not read back by
-// this kernel, so neither should displace other data in the caches.
+// Streaming (non-temporal) 16-byte loads and stores for the bulk form and
+// the in-place rotation: a prompt's K/V rows (or q) are read once and what is
+// written is not read back by the same kernel, so neither should displace
+// other data in the caches.
 // Measured on 16,384 prompt tokens: the plain write 17.1 -> 12.7 us and the
 // RoPE write 20.9 -> 17.0 us (launch loops, same process).
 typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
@@ -260,7 +261,10 @@ void cache_write_kernel(CacheWriteArgs a)
 // In-place rotary embedding of x [tokens][heads][head_dim], one wavefront per
 // token, with the same lane layout as the cache write above.  A lane's
 // chunks (up to kRopeChunks rounds of 64) are all loaded before the first is
-// turned, so a token waits on memory once.
+// turned, so a token waits on memory once.  Style 0 reads and writes its
+// 16-byte chunks with streaming accesses (each is read once and written
+// once: 27.4 -> 24.1 us on 16,384 x 32 heads); style 1's two 8-byte pieces
+// of one line stay cached (streaming them was slower).
 constexpr int kRopeChunks = 8;
 
 __global__ __launch_bounds__(64 * kWavesPerGroup) void rope_kernel(RopeArgs a)
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void rope_kernel(RopeArgs a)
         if (it * 64 < groups && c < groups) {
             uint16_t *pa = piece_a(c);
             if (a.style == 0) {
-                in[it] = *reinterpret_cast<const uint4 *>(pa);
+                in[it] = nt_load(reinterpret_cast<const uint4 *>(pa));
             } else {
                 const uint2 lo = *reinterpret_cast<const uint2 *>(pa);
                 const uint2 hi = *reinterpret_cast<const uint2 *>(pa + half);
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void rope_kernel(RopeArgs a)
                 o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ra) |
                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rb) << 16);
             }
-            *reinterpret_cast<uint4 *>(piece_a(c)) = make_uint4(o[0], o[1], o[2], o[3]);
+            nt_store(make_uint4(o[0], o[1], o[2], o[3]), reinterpret_cast<uint4 *>(piece_a(c)));
         } else {
             const uint32_t wa[2] = {kk.x, kk.y}, wb[2] = {kk.z, kk.w};
             uint32_t oa[2] = {0u, 0u}, ob[2] = {0u, 0u};
