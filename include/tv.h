@@ -338,10 +338,10 @@ tv_status tv_paged_attention_decode_shared_append(
  * tv_paged_attention_reduce would.
  *
  * Forms (from the shapes alone, never the data; a call is deterministic):
- *   group_size <= 4, no group_order, and every (group, K/V head) workgroup
- *   resident at once on the device (num_groups * num_kv_heads <= 2 * 256 on
- *   MI355X): one launch with one 8-wavefront workgroup per (group, K/V
- *   head).  The group's shared tiles (its shared length cut as for
+ *   group_size <= 4 (with or without group_order) and every (group, K/V
+ *   head) workgroup resident at once on the device (num_groups *
+ *   num_kv_heads <= 2 * 256 on MI355X): one launch with one 8-wavefront
+ *   workgroup per (group, K/V head).  The group's shared tiles (its shared length cut as for
  *   tv_paged_attention_decode_shared) are read once with every member's
  *   query heads, each member's other tiles with its own; the group's tiles
  *   (the shared ones, then each member's) are cut into 8 equal consecutive
@@ -377,7 +377,8 @@ tv_status tv_paged_attention_decode_shared_step(
  * the current device: 0 nothing is launched (num_seqs == 0 or
  * max_context_len == 0), 1 one launch (one workgroup per (group, K/V head)),
  * 2 two launches through the workspace, -1 the step would reject these
- * shapes.  has_group_order: nonzero if a group_order array is passed.
+ * shapes.  has_group_order: nonzero if a group_order array is passed (it
+ * does not change the form).
  * Host-only; reads the current device's compute-unit count and occupancy.
  */
 int32_t tv_paged_attention_decode_shared_step_form(int32_t num_seqs, int32_t num_q_heads,

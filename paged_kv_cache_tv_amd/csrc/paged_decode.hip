@@ -797,6 +797,10 @@ void paged_decode_seq_kernel(DecodeArgs a)
 //     as the append pass does; a slot elsewhere gets its row alone at the end.
 //   * The kGroupWaves states merge in LDS in wavefront order and the rows are
 //     written to `out` (part_acc), divided by their sums.
+//   * Member m of group g is the sequence at position g * group_size + m, or
+//     group_order's entry for it; an entry outside the batch leaves that
+//     member out (no length, so the group shares nothing; no row written),
+//     as the group pass does.
 constexpr int kGroupWaves = 8;
 constexpr int kGroupRing = 2;
 constexpr int kGroupMaxMembers = 4;
@@ -854,9 +858,24 @@ __device__ int group_unit(const DecodeArgs &a, int k, int lane)
             const int cnt = min(a.group_size, a.num_seqs - f);
             int sh = a.shared_len[gc];
             int nm[kGroupMaxMembers];
+            if (a.group_order) {
+                // Member m is sequence group_order[f + m]; an entry outside
+                // the batch counts as an empty member.
+                int sq[kGroupMaxMembers];
 #pragma unroll
-            for (int m = 0; m < kGroupMaxMembers; ++m)
-                nm[m] = a.context_lens[min(f + m, a.num_seqs - 1)];
+                for (int m = 0; m < kGroupMaxMembers; ++m)
+                    sq[m] = a.group_order[min(f + m, a.num_seqs - 1)];
+#pragma unroll
+                for (int m = 0; m < kGroupMaxMembers; ++m) {
+                    const bool ok = sq[m] >= 0 && sq[m] < a.num_seqs;
+                    nm[m] = a.context_lens[ok ? sq[m] : 0];
+                    nm[m] = ok ? nm[m] : 0;
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < kGroupMaxMembers; ++m)
+                    nm[m] = a.context_lens[min(f + m, a.num_seqs - 1)];
+            }
             int sum = 0;
 #pragma unroll
             for (int m = 0; m < kGroupMaxMembers; ++m) {
@@ -891,13 +910,29 @@ void paged_decode_group_kernel(DecodeArgs a)
     const int g = lane >> 4;
     const float c = a.scale_log2;
 
-    // Lane m < cnt: member m's context length (clamped).  The shared length
-    // is cut to every member's context and to whole partitions.
+    // Lane m < cnt: member m's sequence (position first + m, through
+    // group_order when given; -1 for an entry outside the batch, a member
+    // left out: no length, no tiles, no row) and its context length
+    // (clamped).  The shared length is cut to every member's context and to
+    // whole partitions, so a left-out member leaves its group nothing shared.
+    int seq_lane = -1;
     int n_lane = 0;
     if (lane < cnt) {
-        n_lane = a.context_lens[first + lane];
+        const int sq = a.group_order ? a.group_order[first + lane] : first + lane;
+        seq_lane = sq >= 0 && sq < a.num_seqs ? sq : -1;
+        n_lane = seq_lane >= 0 ? a.context_lens[seq_lane] : 0;
         n_lane = n_lane < 0 ? 0 : (n_lane > a.max_context_len ? a.max_context_len : n_lane);
     }
+    // The members' sequences as uniform values (scalar registers), picked per
+    // lane by member index where a lane needs one.
+    static_assert(kGroupMaxMembers == 4, "one scalar per member below");
+    const int sq0 = __builtin_amdgcn_readlane(seq_lane, 0);
+    const int sq1 = __builtin_amdgcn_readlane(seq_lane, 1);
+    const int sq2 = __builtin_amdgcn_readlane(seq_lane, 2);
+    const int sq3 = __builtin_amdgcn_readlane(seq_lane, 3);
+    auto seq_of_member = [&](int m) {
+        return m == 0 ? sq0 : (m == 1 ? sq1 : (m == 2 ? sq2 : sq3));
+    };
     int sh = a.shared_len[grp];
     for (int m = 0; m < cnt; ++m)
         sh = min(sh, __builtin_amdgcn_readlane(n_lane, m));
@@ -921,13 +956,15 @@ void paged_decode_group_kernel(DecodeArgs a)
     const int v_hi = (int)((int64_t)(wv + 1) * total / kGroupWaves);
     const int nv = v_hi - v_lo;
 
-    // Columns: member r / G (r < cnt * G), query head kvh * G + r % G.
-    const bool col_ok = r < cnt * G;
-    const int col_mem = col_ok ? r / G : 0;
+    // Columns: member r / G (r < cnt * G, the member not left out), query
+    // head kvh * G + r % G.
+    const int col_mem = r < cnt * G ? r / G : 0;
+    const int col_seq = seq_of_member(col_mem);
+    const bool col_ok = r < cnt * G && col_seq >= 0;
     bf16x8 qb0 = {}, qb1 = {};
     if (col_ok) {
         const uint16_t *qp =
-            a.q + ((int64_t)(first + col_mem) * a.num_kv_heads * G + (int64_t)kvh * G + r % G) * D +
+            a.q + ((int64_t)col_seq * a.num_kv_heads * G + (int64_t)kvh * G + r % G) * D +
             g * 8;
         qb0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp));
         qb1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 32));
@@ -944,9 +981,9 @@ void paged_decode_group_kernel(DecodeArgs a)
     const uint64_t held = __ballot(hold_lane);
     int64_t wslot_lane = -1;
     int32_t tblk_lane = -1;
-    if (hold_lane) {
-        wslot_lane = a.slot_mapping[first + lane];
-        tblk_lane = a.block_tables[(int64_t)(first + lane) * a.max_blocks + last_t];
+    if (hold_lane) {                      // n_lane > 0: a member in the batch
+        wslot_lane = a.slot_mapping[seq_lane];
+        tblk_lane = a.block_tables[(int64_t)seq_lane * a.max_blocks + last_t];
     }
     uint32_t new_pair[kGroupMaxMembers];
 #pragma unroll
@@ -955,7 +992,8 @@ void paged_decode_group_kernel(DecodeArgs a)
         if (APPEND && ((held >> m) & 1ull))
             new_pair[m] = *reinterpret_cast<const uint32_t *>(
                 (lane < 32 ? a.k_new : a.v_new) +
-                ((int64_t)(first + m) * a.num_kv_heads + kvh) * D + 2 * (lane & 31));
+                ((int64_t)seq_of_member(m) * a.num_kv_heads + kvh) * D +
+                2 * (lane & 31));
     }
     int sub_lane = -1;        // lane m: token of member m's last tile replaced (-1: none)
     bool done_lane = false;   // lane m: member m's row went out with its tile
@@ -1075,7 +1113,7 @@ void paged_decode_group_kernel(DecodeArgs a)
             const int ge = __shfl(g_end, mem);
             const int gb = ge - __shfl(pt, mem);
             const bool in_shared = gp < ST;
-            const int seq = first + (in_shared ? 0 : mem);
+            const int seq = seq_of_member(in_shared ? 0 : mem);   // >= 0 wherever a tile lies
             const int tix = in_shared ? gp : ST + (gp - gb);
             if (lane < cn)
                 phys_lane = a.block_tables[(int64_t)seq * a.max_blocks + tix];
@@ -1160,15 +1198,16 @@ void paged_decode_group_kernel(DecodeArgs a)
             const int nm = __builtin_amdgcn_readlane(n_lane, m);
             if (nm <= 0 || (nm - 1) / BS >= ST)
                 continue;
-            const int64_t ws = a.slot_mapping[first + m];
+            const int sm = seq_of_member(m);                         // nm > 0: in the batch
+            const int64_t ws = a.slot_mapping[sm];
             if (ws < 0 || ws >= a.num_blocks * BS)
                 continue;
             const int64_t wblk = ws / BS;
             const int woff = (int)(ws - wblk * BS);
             uint16_t *kt = a.k_cache_w + (wblk * a.num_kv_heads + kvh) * (int64_t)(BS * D);
             uint16_t *vt = a.v_cache_w + (wblk * a.num_kv_heads + kvh) * (int64_t)(BS * D);
-            const uint16_t *kn = a.k_new + ((int64_t)(first + m) * a.num_kv_heads + kvh) * D;
-            const uint16_t *vn = a.v_new + ((int64_t)(first + m) * a.num_kv_heads + kvh) * D;
+            const uint16_t *kn = a.k_new + ((int64_t)sm * a.num_kv_heads + kvh) * D;
+            const uint16_t *vn = a.v_new + ((int64_t)sm * a.num_kv_heads + kvh) * D;
             if (lane < D / 8)
                 *reinterpret_cast<uint4 *>(kt + (lane * BS + woff) * 8) =
                     *reinterpret_cast<const uint4 *>(kn + 8 * lane);
@@ -1194,7 +1233,7 @@ void paged_decode_group_kernel(DecodeArgs a)
     l += __shfl_xor(l, 32);
     if (col_ok) {
         const int hq = a.num_kv_heads * G;
-        const int64_t row = (int64_t)(first + col_mem) * hq + (int64_t)kvh * G + r % G;
+        const int64_t row = (int64_t)seq_of_member(col_mem) * hq + (int64_t)kvh * G + r % G;
         float *acc = a.part_acc + row * D + 4 * g;
         const bool none = S.m == -INFINITY;
 #pragma unroll
@@ -1362,12 +1401,11 @@ hipError_t launch_paged_decode_seq(const DecodeArgs &args, hipStream_t stream)
 }
 
 // The whole-group form serves a shared-prefix step (with its appends) with
-// groups of at most kGroupMaxMembers sequences in their own order (no
+// groups of at most kGroupMaxMembers sequences (in their own order or through
 // group_order) and every (group, K/V head) workgroup resident at once.
 bool paged_decode_group_fits(const DecodeArgs &a)
 {
-    if (!a.shared_len || !a.k_new || a.group_order || a.group_size > kGroupMaxMembers ||
-        a.num_parts < 1)
+    if (!a.shared_len || !a.k_new || a.group_size > kGroupMaxMembers || a.num_parts < 1)
         return false;
     const DeviceShape dev = device_shape();
     const int per_cu = group_wgs_per_cu();

@@ -117,7 +117,7 @@ def test_shared_prefix_ragged_groups(dev, samples, prefix, part):
 # bit for bit: pools and partials.
 # ---------------------------------------------------------------------------
 
-def _run_append(b, dev, part, shared, group_size, lens=None):
+def _run_append(b, dev, part, shared, group_size, lens=None, group_order=None):
     """Cached tokens written with tv_cache_write, then the shared pass with the
     new tokens appended: (out, partials, pools)."""
     import torch
@@ -134,9 +134,11 @@ def _run_append(b, dev, part, shared, group_size, lens=None):
     for t in ws:
         t.fill_(float("nan"))
     q, bt, cl = _to_dev(b.q, dev), _to_dev(b.block_tables, dev), _to_dev(lens, dev)
+    go = None if group_order is None else _to_dev(group_order, dev)
     tv.paged_attention_decode_shared_append(*ws, q, _to_dev(sk, dev), _to_dev(sv, dev),
                                             _to_dev(ss.astype(np.int64), dev), kc, vc, bt, cl,
-                                            _to_dev(shared, dev), group_size, mc, part, b.scale)
+                                            _to_dev(shared, dev), group_size, mc, part, b.scale,
+                                            group_order=go)
     out = torch.empty((b.num_seqs, b.num_q_heads, b.head_dim), dtype=torch.float32, device=dev)
     tv.paged_attention_reduce(out, *ws, cl, mc, part)
     torch.cuda.synchronize()
@@ -259,8 +261,9 @@ def test_shared_groups_in_any_order(dev, append):
 
 # ---------------------------------------------------------------------------
 # tv_paged_attention_decode_shared_step: the parallel-sampling step in one
-# call.  In its one-launch form (groups of up to 4 in their own order, every
-# (group, K/V head) workgroup resident) the shared tiles and each member's own
+# call.  In its one-launch form (groups of up to 4, in their own order or
+# through group_order, every (group, K/V head) workgroup resident) the shared
+# tiles and each member's own
 # tiles are cut into 8 equal parts per range instead of the workspace's
 # partitions, so the output equals the two-call step (shared append + merge)
 # to rounding; the pools equal it bit for bit.
@@ -375,26 +378,65 @@ def test_shared_step_ragged_groups(dev, samples, prefix, part, hq, hkv):
     assert np.array_equal(pools[0], pools2[0]) and np.array_equal(pools[1], pools2[1])
 
 
-@pytest.mark.parametrize("case", ["group_order", "group_of_8"])
-def test_shared_step_two_launch_forms(dev, case):
-    """Outside the one-launch form (a member order, or groups of more than 4)
-    the step is the shared append and the merge: bit for bit the two calls."""
+def test_shared_step_two_launch_form(dev):
+    """Outside the one-launch form (groups of more than 4) the step is the
+    shared append and the merge: bit for bit the two calls."""
     import paged_kv_cache_tv_amd as tv
     b = W.make_workload(4)
     S = b.num_seqs
     part = 512
     mc = int(b.context_lens.max())
-    if case == "group_order":
-        gs, order = 4, np.arange(S, dtype=np.int32)
-        shared = np.full(S // 4, 1024, np.int32)
-    else:
-        b.q = b.q[:, :16].copy()                     # 16 query heads: G = 2, groups of 8
-        b.num_q_heads = 16
-        gs, order = 8, None
-        shared = np.full(S // 8, 1024, np.int32)
+    b.q = b.q[:, :16].copy()                         # 16 query heads: G = 2, groups of 8
+    b.num_q_heads = 16
+    gs = 8
+    shared = np.full(S // 8, 1024, np.int32)
     assert tv.decode_shared_step_form(S, b.num_q_heads, b.num_kv_heads, 64, 16, mc, part, gs,
-                                      order is not None) == 2
-    out, pools = _run_shared_step(b, dev, part, shared, gs, group_order=order)
+                                      False) == 2
+    out, pools = _run_shared_step(b, dev, part, shared, gs)
     two, _, pools2 = _run_append(b, dev, part, shared, gs)
     assert np.array_equal(out.view(np.uint32), two.view(np.uint32))
     assert np.array_equal(pools[0], pools2[0]) and np.array_equal(pools[1], pools2[1])
+
+
+@pytest.mark.parametrize("left_out", [False, True], ids=["permuted", "one-left-out"])
+def test_shared_step_group_order(dev, oracle_lib, left_out):
+    """Groups given by group_order in the one-launch form: the prompts' groups
+    and their members in a shuffled order (each group still its prompt's 4
+    samples, so the shared blocks are shared), and optionally one position
+    whose entry lies outside the batch (its sequence is then not computed and
+    its group shares nothing).  Output within rounding of the two-call step
+    with the same order and within the oracle bars, pools bit-exact against
+    the two-call step's (and the oracle's when nothing is left out)."""
+    import paged_kv_cache_tv_amd as tv
+    b = W.make_workload(4)
+    S = b.num_seqs
+    part = 512
+    mc = int(b.context_lens.max())
+    rng = np.random.default_rng(73)
+    order = np.concatenate([4 * g + rng.permutation(4) for g in rng.permutation(S // 4)])
+    order = order.astype(np.int32)
+    skipped = None
+    if left_out:
+        skipped = int(order[5])
+        order[5] = -1                                # position 5: outside the batch
+    shared = np.full(S // 4, 1024, np.int32)
+    assert tv.decode_shared_step_form(S, b.num_q_heads, b.num_kv_heads, 64, 16, mc, part, 4,
+                                      True) == 1
+    out, pools = _run_shared_step(b, dev, part, shared, 4, group_order=order)
+    out2, _ = _run_shared_step(b, dev, part, shared, 4, group_order=order)
+    assert np.array_equal(out.view(np.uint32), out2.view(np.uint32)), "two calls differ"
+    two, _, pools2 = _run_append(b, dev, part, shared, 4, group_order=order)
+    keep = np.ones(S, bool)
+    if skipped is not None:
+        keep[skipped] = False
+        assert np.isnan(out[skipped]).all(), "a sequence not listed keeps its row"
+    d = np.abs(out[keep] - two[keep]).max()
+    print(f"group_order shared step vs two calls: max_abs={d:.3e}", flush=True)
+    assert d <= _forms_bar(b)
+    assert np.array_equal(pools[0], pools2[0]) and np.array_equal(pools[1], pools2[1])
+    ref, kc_ref, vc_ref = O.decode_step(oracle_lib, b)
+    if skipped is None:
+        assert np.array_equal(pools[0], kc_ref) and np.array_equal(pools[1], vc_ref)
+    err = np.abs(out[keep].astype(np.float64) - ref[keep])
+    print(f"group_order shared step: max_abs={err.max():.3e} mean_abs={err.mean():.3e}", flush=True)
+    assert err.max() <= 1e-4 and err.mean() <= 1e-6
