@@ -680,6 +680,20 @@ def main(argv=None):
                      for name, f in steps.items()}
     t_flush_write = timed_loop(lambda i: (flush(i), db.write_step(stream)), K)
     t_flush_decode = timed_loop(lambda i: (flush(i), db.decode(stream)), K)
+    # The same partition pass with its contractions on the vector ALUs
+    # (tv_paged_attention_decode_vector, 4 query heads per K/V head only).
+    vector_ok = batch.num_q_heads == 4 * batch.num_kv_heads
+
+    def vector_pass():
+        pa, pm, ps = db.workspace
+        tv.paged_attention_decode_vector(pa, pm, ps, db.q, db.k_cache, db.v_cache,
+                                         db.block_tables, db.context_lens, db.max_context_len,
+                                         db.partition_size, batch.scale, stream)
+    if vector_ok:
+        for i in range(args.warmup):
+            vector_pass()
+    t_flush_vector = (timed_loop(lambda i: (flush(i), vector_pass()), K) if vector_ok
+                      else float("nan"))
     t_flush_append = timed_loop(lambda i: (flush(i), db.decode_append(stream)), K)
     t_flush_reduce = timed_loop(lambda i: (flush(i), db.reduce(stream)), K)
     if args.no_flush:
@@ -687,6 +701,7 @@ def main(argv=None):
     step_ms_cold = t_flush_step - t_flush
     forms_ms = {name: t - t_flush for name, t in t_flush_forms.items()}
     decode_ms = t_flush_decode - t_flush
+    vector_ms = t_flush_vector - t_flush
     append_ms = t_flush_append - t_flush
     write_ms = t_flush_write - t_flush
     reduce_ms = t_flush_reduce - t_flush
@@ -789,6 +804,16 @@ def main(argv=None):
                        "paged_decode": round(decode_ms * 1e3, 2),
                        "paged_decode_append": round(append_ms * 1e3, 2),
                        "paged_reduce": round(reduce_ms * 1e3, 2)},
+        "vector_path": ({
+            "what": "the plain partition pass (no cache write) with its QK and PV "
+                    "contractions on the vector ALUs, against the same pass on MFMA; "
+                    "cold cache, same timing method",
+            "kernel": "paged_decode_vec_kernel", "us": round(vector_ms * 1e3, 2),
+            "GB_per_s": round(dec_bytes / (vector_ms * 1e-3) / 1e9, 2),
+            "matrix_kernel": "paged_decode_kernel", "matrix_us": round(decode_ms * 1e3, 2),
+            "matrix_GB_per_s": round(dec_bytes / (decode_ms * 1e-3) / 1e9, 2),
+            "vector_over_matrix_time": round(vector_ms / decode_ms, 3)}
+            if vector_ok else None),
         "eviction_us": round(t_flush * 1e3, 2),
         "hot_cache": {"ms_per_step": round(hot_ms, 5),
                       "GB_per_s": round(step_bytes / (hot_ms * 1e-3) / 1e9, 2),

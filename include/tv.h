@@ -209,6 +209,30 @@ tv_status tv_paged_attention_decode(float *part_acc, float *part_max, float *par
                                     float scale, void *stream);
 
 /*
+ * The same partition pass with the QK and PV contractions on the vector ALUs
+ * (v_dot2_f32_bf16 scores, lane-swap and DPP reductions, the weights read out
+ * to scalar registers for the PV multiply-adds) instead of MFMA: the same
+ * partials as tv_paged_attention_decode, from the same softmax definition,
+ * up to fp32 rounding order.  It exists as the measured alternative to the
+ * matrix form ("vLLM" page, section "Flash Attention": the score and
+ * weighted-sum products of each partition); on MI355X it is the slower of the
+ * two on every workload measured, so no other call takes it.
+ * Arguments, layouts, alignment and defined behaviour on odd data are those of
+ * tv_paged_attention_decode.  Supported shapes: as there, with exactly 4 query
+ * heads per K/V head (num_q_heads == 4 * num_kv_heads); other groupings give
+ * TV_ERR_UNSUPPORTED.
+ */
+tv_status tv_paged_attention_decode_vector(float *part_acc, float *part_max, float *part_sum,
+                                           const uint16_t *q, const uint16_t *k_cache,
+                                           const uint16_t *v_cache, const int32_t *block_tables,
+                                           const int32_t *context_lens, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t max_blocks_per_seq, int64_t num_blocks,
+                                           int32_t max_context_len, int32_t partition_size,
+                                           float scale, void *stream);
+
+/*
  * Partition pass for sequences that share a prompt prefix ("vLLM" page,
  * section "가상 메모리 방식의 해결": the samples of one prompt share its
  * blocks).  The same partials as tv_paged_attention_decode; the shared

@@ -11,6 +11,7 @@ from .binding import (LIB_PATH, STREAM_CHUNK_BYTES, DECODE_STEP_FORMS, BlockMana
                       decode_shared_step_form, decode_step_form, lib, load_library,
                       new_pools, new_workspace, num_partitions, paged_attention,
                       paged_attention_decode, paged_attention_decode_append,
+                      paged_attention_decode_vector,
                       paged_attention_decode_shared, paged_attention_decode_shared_append,
                       paged_attention_decode_shared_step, paged_attention_decode_step,
                       paged_attention_decode_step_noalloc, paged_attention_prefill,
@@ -23,4 +24,5 @@ __all__ = ["LIB_PATH", "STREAM_CHUNK_BYTES", "DECODE_STEP_FORMS", "BlockManager"
            "paged_attention_decode_append", "paged_attention_decode_shared",
            "paged_attention_decode_shared_append", "paged_attention_decode_shared_step",
            "paged_attention_decode_step", "paged_attention_decode_step_noalloc",
-           "paged_attention_prefill", "paged_attention_reduce", "rope", "stream_read"]
+           "paged_attention_decode_vector", "paged_attention_prefill", "paged_attention_reduce",
+           "rope", "stream_read"]

@@ -53,6 +53,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_paged_attention_decode.restype = ctypes.c_int
     lib.tv_paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                               i32, i32, i64, i32, i32, f32, vp]
+    lib.tv_paged_attention_decode_vector.restype = ctypes.c_int
+    lib.tv_paged_attention_decode_vector.argtypes = lib.tv_paged_attention_decode.argtypes
     lib.tv_paged_attention_decode_append.restype = ctypes.c_int
     lib.tv_paged_attention_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                      i32, i32, i32, i32, i32, i32, i64, i32, i32,
@@ -228,11 +230,8 @@ def cache_write(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
     _check("tv_cache_write", st)
 
 
-def paged_attention_decode(part_acc, part_max, part_sum, q, k_cache, v_cache, block_tables,
-                           context_lens, max_context_len: int, partition_size: int,
-                           scale: float, stream=None) -> None:
-    """tv_paged_attention_decode.  q: [S, Hq, D]; block_tables: int32 [S, max_blocks];
-    context_lens: int32 [S]; part_acc: float32 [S, Hq, P, D]; part_max/part_sum: [S, Hq, P]."""
+def _decode_pass(name, part_acc, part_max, part_sum, q, k_cache, v_cache, block_tables,
+                 context_lens, max_context_len, partition_size, scale, stream):
     import torch
     _need(q, "q", itemsize=2, ndim=3)
     _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
@@ -249,12 +248,32 @@ def paged_attention_decode(part_acc, part_max, part_sum, q, k_cache, v_cache, bl
         raise ValueError(f"workspace must be [S, Hq, P(={P}), D] and [S, Hq, P]")
     if block_tables.shape[0] != S or context_lens.shape[0] != S:
         raise ValueError("block_tables / context_lens must have one row per sequence")
-    st = lib().tv_paged_attention_decode(
+    st = getattr(lib(), name)(
         part_acc.data_ptr(), part_max.data_ptr(), part_sum.data_ptr(), q.data_ptr(),
         k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
         S, hq, hkv, d, bs, block_tables.shape[1], nb, int(max_context_len), int(partition_size),
         float(scale), _stream_handle(stream, q.device))
-    _check("tv_paged_attention_decode", st)
+    _check(name, st)
+
+
+def paged_attention_decode(part_acc, part_max, part_sum, q, k_cache, v_cache, block_tables,
+                           context_lens, max_context_len: int, partition_size: int,
+                           scale: float, stream=None) -> None:
+    """tv_paged_attention_decode.  q: [S, Hq, D]; block_tables: int32 [S, max_blocks];
+    context_lens: int32 [S]; part_acc: float32 [S, Hq, P, D]; part_max/part_sum: [S, Hq, P]."""
+    _decode_pass("tv_paged_attention_decode", part_acc, part_max, part_sum, q, k_cache, v_cache,
+                 block_tables, context_lens, max_context_len, partition_size, scale, stream)
+
+
+def paged_attention_decode_vector(part_acc, part_max, part_sum, q, k_cache, v_cache,
+                                  block_tables, context_lens, max_context_len: int,
+                                  partition_size: int, scale: float, stream=None) -> None:
+    """tv_paged_attention_decode_vector: the same partition pass with the
+    contractions on the vector ALUs (4 query heads per K/V head only).
+    Arguments as for paged_attention_decode."""
+    _decode_pass("tv_paged_attention_decode_vector", part_acc, part_max, part_sum, q, k_cache,
+                 v_cache, block_tables, context_lens, max_context_len, partition_size, scale,
+                 stream)
 
 
 def cache_write_rope(k, v, k_cache, v_cache, slot_mapping, positions, inv_freq,

@@ -1339,6 +1339,337 @@ int group_wgs_per_cu()
     return per_cu;
 }
 
+// The vector-ALU form of the partition pass (tv_paged_attention_decode_vector):
+// the same grid, partition split, table handling, tile ring, merge of the 4
+// wavefronts and epilogue as paged_decode_kernel<false, false, PLAN, 4>, with
+// the QK and PV contractions done by the vector ALUs instead of MFMA, for a
+// group of 4 query heads per K/V head.  It is the measured alternative to the
+// matrix form: on MI355X it is slower on every workload measured (the MFMA
+// form issues 10 matrix and about 40 vector instructions per tile, this one
+// about 230 vector instructions).
+//   * K arrives as in the matrix form: lane (r = lane % 16, g = lane / 16)
+//     holds token r's dims 8g..8g+7 and 32+8g..32+8g+7.  Each lane takes its
+//     16-dim part of token r's score for each of the 4 heads (8
+//     v_dot2_f32_bf16 per head), and the 4 lane rows' parts are summed with
+//     v_permlane16_swap / v_permlane32_swap, in the same order in every row,
+//     so all 4 lanes of column r hold token r's 4 scores.
+//   * The tile maximum per head is a DPP butterfly within a 16-lane row.
+//   * V arrives as one 32-byte row per lane: lane d holds V[dim d][tokens
+//     0..15], so the output O[h][d] of all 4 heads stays in lane d; the 64
+//     weights go to scalar registers (v_readlane) and PV is 64 FMAs per lane.
+//   * At the end of its range a wavefront passes its (max, sum, output)
+//     through LDS into the matrix form's lane layout (lane (r, g), r < 4:
+//     head r, dims 16j + 4g + i), and the matrix form's merge and stores
+//     follow unchanged.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr int kVecGroup = 4;
+
+struct VecTile {
+    bf16x8 k0, k1;
+    u32x4 va, vb;        // V[dim lane][tokens 0..7], [tokens 8..15]
+};
+
+__device__ __forceinline__ void load_vec_tile(VecTile &t, const char *kt, const char *vt,
+                                              uint32_t koff, uint32_t vdoff)
+{
+    t.k0 = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+                                          reinterpret_cast<const u32x4 *>(kt + koff)));
+    t.k1 = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+                                          reinterpret_cast<const u32x4 *>(kt + 1024 + koff)));
+    t.va = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vt + vdoff));
+    t.vb = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vt + vdoff + 16));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum / sum over the 16 lanes of each row, in every lane of the row:
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+__device__ __forceinline__ float row_max16(float x)
+{
+    x = fmaxf(x, dpp_move<0xB1>(x));
+    x = fmaxf(x, dpp_move<0x4E>(x));
+    x = fmaxf(x, dpp_move<0x141>(x));
+    return fmaxf(x, dpp_move<0x140>(x));
+}
+__device__ __forceinline__ float row_sum16(float x)
+{
+    x = x + dpp_move<0xB1>(x);
+    x = x + dpp_move<0x4E>(x);
+    x = x + dpp_move<0x141>(x);
+    return x + dpp_move<0x140>(x);
+}
+
+// Sum over lanes l, l ^ 16, l ^ 32, l ^ 48 as (x[row 0] + x[row 1]) +
+// (x[row 2] + x[row 3]) for the lane's column, in every row.
+__device__ __forceinline__ float sum_over_rows(float x)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned a0 = a[0], a1 = a[1];
+    const float y = __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1);
+    const unsigned w = __builtin_bit_cast(unsigned, y);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    const unsigned b0 = b[0], b1 = b[1];
+    return __builtin_bit_cast(float, b0) + __builtin_bit_cast(float, b1);
+}
+
+// Fold one tile into the running state: m[h] (base-2 units, the same in every
+// lane), l[h] (this lane's column's weights; every row holds the same), o[h]
+// = O[h][dim lane].  `valid`: tokens of the tile inside the context (MASK only).
+template <bool MASK>
+__device__ __forceinline__ void attend_vec_tile(const VecTile &t, const bf16x8 (&qa)[kVecGroup],
+                                                const bf16x8 (&qb)[kVecGroup], int valid, float c,
+                                                int r, float (&m)[kVecGroup],
+                                                float (&l)[kVecGroup], float (&o)[kVecGroup])
+{
+#pragma clang fp contract(off)
+    float s2[kVecGroup];
+#pragma unroll
+    for (int h = 0; h < kVecGroup; ++h) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bf16x2 kk = {t.k0[2 * i], t.k0[2 * i + 1]};
+            const bf16x2 qq = {qa[h][2 * i], qa[h][2 * i + 1]};
+            acc = __builtin_amdgcn_fdot2_f32_bf16(kk, qq, acc, false);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bf16x2 kk = {t.k1[2 * i], t.k1[2 * i + 1]};
+            const bf16x2 qq = {qb[h][2 * i], qb[h][2 * i + 1]};
+            acc = __builtin_amdgcn_fdot2_f32_bf16(kk, qq, acc, false);
+        }
+        s2[h] = sum_over_rows(acc) * c;           // base-2 units, rounded once
+        if (MASK && r >= valid)
+            s2[h] = -INFINITY;
+    }
+    float p[kVecGroup];
+#pragma unroll
+    for (int h = 0; h < kVecGroup; ++h) {
+        const float m_new = fmaxf(m[h], row_max16(s2[h]));
+        const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);
+        p[h] = __builtin_amdgcn_exp2f(s2[h] - m_new);
+        m[h] = m_new;
+        l[h] = fmaf(l[h], alpha, p[h]);
+        o[h] *= alpha;
+    }
+    // V[dim lane][t] as fp32; tokens past the context forced to 0, since stale
+    // slots may hold NaN and 0 * NaN is NaN.
+    float v[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        v[2 * w] = __builtin_bit_cast(float, t.va[w] << 16);
+        v[2 * w + 1] = __builtin_bit_cast(float, t.va[w] & 0xFFFF0000u);
+        v[8 + 2 * w] = __builtin_bit_cast(float, t.vb[w] << 16);
+        v[9 + 2 * w] = __builtin_bit_cast(float, t.vb[w] & 0xFFFF0000u);
+    }
+    if (MASK) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (i >= valid)
+                v[i] = 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < kVecGroup; ++h) {
+        const int pb = __builtin_bit_cast(int, p[h]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            o[h] = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(pb, i)), v[i], o[h]);
+    }
+}
+
+template <bool PLAN>
+__device__ __forceinline__ void decode_unit_vec(const DecodeArgs &a, unsigned bid)
+{
+    constexpr int SPLIT = 4;
+    constexpr int kRing = kRingFor<SPLIT>;
+    const int lane = (int)(threadIdx.x & 63);
+    const int wv = (int)(threadIdx.x >> 6);
+    const int kvh = (int)(bid % (unsigned)a.num_kv_heads);
+    const int rest = (int)(bid / (unsigned)a.num_kv_heads);
+    int part = rest / a.num_seqs;
+    int s = rest % a.num_seqs;
+    const int ptiles = a.part_tiles;
+    if (PLAN) {
+        const Unit u = plan_unit(a, rest, lane);
+        if (u.s < 0)
+            return;
+        s = u.s;
+        part = u.part;
+    }
+    // Table entries loaded with the context length, as in the matrix form.
+    const int64_t row0 = (int64_t)s * a.max_blocks + (int64_t)part * ptiles;
+    const bool table_ahead = ptiles <= 64;
+    const int32_t ahead_lane = table_ahead && lane < min(ptiles, a.max_blocks - part * ptiles)
+                                   ? a.block_tables[row0 + lane]
+                                   : 0;
+    int n = a.context_lens[s];
+    n = n < 0 ? 0 : (n > a.max_context_len ? a.max_context_len : n);
+    const int first_tok = part * ptiles * BS;
+    if (first_tok >= n)
+        return;
+    const int ptok = min(n - first_tok, ptiles * BS);
+    const int ntiles = (ptok + BS - 1) / BS;
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const float c = a.scale_log2;
+
+    // q of the group's 4 heads: lane (r, g) holds dims 8g..8g+7 (qa) and
+    // 32+8g..32+8g+7 (qb).
+    bf16x8 qa[kVecGroup], qb[kVecGroup];
+#pragma unroll
+    for (int h = 0; h < kVecGroup; ++h) {
+        const uint16_t *qp =
+            a.q + ((int64_t)s * a.num_kv_heads * kVecGroup + (int64_t)kvh * kVecGroup + h) * D + g * 8;
+        qa[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp));
+        qb[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 32));
+    }
+    const int per = (ntiles + SPLIT - 1) / SPLIT;
+    const int t_lo = min(ntiles, wv * per);
+    const int t_hi = min(ntiles, t_lo + per);
+
+    float m[kVecGroup], l[kVecGroup], o[kVecGroup];
+#pragma unroll
+    for (int h = 0; h < kVecGroup; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+        o[h] = 0.f;
+    }
+    const int32_t *bt = a.block_tables + row0 + t_lo;
+    const char *kpool = reinterpret_cast<const char *>(a.k_cache) + (int64_t)kvh * kTileBytes;
+    const char *vpool = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * kTileBytes;
+    const int64_t tile_stride = (int64_t)a.num_kv_heads * kTileBytes;
+    const uint32_t koff = (uint32_t)lane * 16u;
+    const uint32_t vdoff = (uint32_t)lane * 32u;
+    auto issue = [&](VecTile &t, int32_t b) {
+        const int64_t bb = (b >= 0 && b < a.num_blocks) ? (int64_t)b : 0;
+        load_vec_tile(t, kpool + bb * tile_stride, vpool + bb * tile_stride, koff, vdoff);
+    };
+    auto consume = [&](const VecTile &t, int tile, int32_t b) {
+        if (b < 0 || b >= a.num_blocks)
+            return;                                   // entry outside the pool: skipped
+        if ((tile + 1) * BS <= ptok)
+            attend_vec_tile<false>(t, qa, qb, BS, c, r, m, l, o);
+        else
+            attend_vec_tile<true>(t, qa, qb, ptok - tile * BS, c, r, m, l, o);
+    };
+    // The ring as in the matrix form.
+    const int nt = t_hi - t_lo;
+    for (int c0 = 0; c0 < nt; c0 += 64) {
+        const int cn = min(64, nt - c0);
+        const int32_t phys_lane = table_ahead ? ahead_lane : (lane < cn ? bt[c0 + lane] : 0);
+        const int first = table_ahead ? t_lo : 0;
+        auto block_of = [&](int k) -> int32_t {
+            return __builtin_amdgcn_readlane(phys_lane, first + min(k, cn - 1));
+        };
+        VecTile ring[kRing];
+#pragma unroll
+        for (int u = 0; u < kRing; ++u)
+            issue(ring[u], block_of(u));
+        const int nit = (cn + kRing - 1) / kRing;
+        for (int it = 0; it + 1 < nit; ++it) {
+#pragma unroll
+            for (int u = 0; u < kRing; ++u) {
+                const int k = it * kRing + u;
+                consume(ring[u], t_lo + c0 + k, block_of(k));
+                issue(ring[u], block_of(k + kRing));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRing; ++u) {
+            const int k = (nit - 1) * kRing + u;
+            if (k < cn)
+                consume(ring[u], t_lo + c0 + k, block_of(k));
+        }
+    }
+
+    // Into the matrix form's layout: lane (r, g), r < 4, holds head r's max,
+    // dims 16j + 4g .. 16j + 4g + 3, and (in its g = 0 lane) its sum.
+    __shared__ __attribute__((aligned(16))) float s_vo[SPLIT][kVecGroup][64];
+#pragma unroll
+    for (int h = 0; h < kVecGroup; ++h)
+        s_vo[wv][h][lane] = o[h];
+    float lt[kVecGroup];
+#pragma unroll
+    for (int h = 0; h < kVecGroup; ++h)
+        lt[h] = row_sum16(l[h]);
+    __builtin_amdgcn_s_waitcnt(0xC07F);               // LDS stores done (lgkmcnt 0)
+    __builtin_amdgcn_wave_barrier();
+    const bool head_lane = r < kVecGroup;
+    const int hr = head_lane ? r : 0;
+    const float m_h = hr == 0 ? m[0] : (hr == 1 ? m[1] : (hr == 2 ? m[2] : m[3]));
+    const float l_h = hr == 0 ? lt[0] : (hr == 1 ? lt[1] : (hr == 2 ? lt[2] : lt[3]));
+    float m_run = head_lane ? m_h : -INFINITY;
+    float l_run = head_lane && g == 0 && m_run != -INFINITY ? l_h : 0.f;
+    f32x4 oo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(&s_vo[wv][hr][16 * j + 4 * g]);
+        oo[j] = head_lane ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Merge the 4 wavefronts in range order and store, as the matrix form does.
+    __shared__ float s_m[SPLIT][64], s_l[SPLIT][64];
+    __shared__ f32x4 s_o[SPLIT][4][64];
+    if (wv > 0) {
+        s_m[wv][lane] = m_run;
+        s_l[wv][lane] = l_run;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            s_o[wv][j][lane] = oo[j];
+    }
+    __syncthreads();
+    if (wv > 0)
+        return;
+    float mm = m_run;
+#pragma unroll
+    for (int w = 1; w < SPLIT; ++w)
+        mm = fmaxf(mm, s_m[w][lane]);
+    if (mm != -INFINITY) {
+        const float a0 = __builtin_amdgcn_exp2f(m_run - mm);
+        l_run *= a0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            oo[j] *= a0;
+#pragma unroll
+        for (int w = 1; w < SPLIT; ++w) {
+            const float aw = __builtin_amdgcn_exp2f(s_m[w][lane] - mm);
+            l_run = fmaf(s_l[w][lane], aw, l_run);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                oo[j] += s_o[w][j][lane] * aw;
+        }
+        m_run = mm;
+    }
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (head_lane) {
+        const int64_t row =
+            ((int64_t)s * a.num_kv_heads * kVecGroup + (int64_t)kvh * kVecGroup + r) * a.num_parts + part;
+        float *acc = a.part_acc + row * D + 4 * g;
+        if (g == 0) {
+            a.part_max[row] = m_run;
+            a.part_sum[row] = l_run;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4 *>(acc + 16 * j) =
+                make_float4(oo[j][0], oo[j][1], oo[j][2], oo[j][3]);
+    }
+}
+
+template <bool PLAN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void paged_decode_vec_kernel(DecodeArgs a)
+{
+    decode_unit_vec<PLAN>(a, blockIdx.x);
+}
+
 template <bool APPEND, bool SHARED, bool PLAN, int SPLIT>
 void launch(const DecodeArgs &a, int64_t groups, hipStream_t stream)
 {
@@ -1492,6 +1823,29 @@ hipError_t launch_paged_decode(const DecodeArgs &args, hipStream_t stream)
         else
             launch<false, false, false, 1>(a, groups, stream);
     }
+    return hipGetLastError();
+}
+
+// The vector-ALU form of the plain partition pass: 4 wavefronts per
+// partition always, in the balanced order when the grid is larger than the
+// device holds (as the matrix form's policy), for 4 query heads per K/V head.
+hipError_t launch_paged_decode_vector(const DecodeArgs &args, hipStream_t stream)
+{
+    DecodeArgs a = args;
+    if (a.group != kVecGroup || a.k_new || a.shared_len || a.normalize)
+        return hipErrorInvalidValue;
+    const DeviceShape dev = device_shape();
+    const int64_t groups = (int64_t)a.num_kv_heads * a.num_seqs * a.num_parts;
+    const int64_t resident = (int64_t)dev.cus * dev.waves_per_cu;
+    a.plan_width = 0;
+    if (groups > resident && a.num_seqs <= 64 * kPlanChunks && dev.cus > 0)
+        a.plan_width = dev.cus / std::gcd(a.num_kv_heads, dev.cus);
+    if (a.plan_width > 0)
+        hipLaunchKernelGGL(paged_decode_vec_kernel<true>, dim3((unsigned)groups), dim3(256), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL(paged_decode_vec_kernel<false>, dim3((unsigned)groups), dim3(256), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

@@ -202,6 +202,30 @@ tv_status tv_paged_attention_decode(float *part_acc, float *part_max, float *par
     return from_hip(tv::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+tv_status tv_paged_attention_decode_vector(float *part_acc, float *part_max, float *part_sum,
+                                           const uint16_t *q, const uint16_t *k_cache,
+                                           const uint16_t *v_cache, const int32_t *block_tables,
+                                           const int32_t *context_lens, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t max_blocks_per_seq, int64_t num_blocks,
+                                           int32_t max_context_len, int32_t partition_size,
+                                           float scale, void *stream)
+{
+    tv::DecodeArgs a;
+    const tv_status st = check_decode(a, part_acc, part_max, part_sum, q, k_cache, v_cache,
+                                      block_tables, context_lens, num_seqs, num_q_heads,
+                                      num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                      num_blocks, max_context_len, partition_size, scale);
+    if (st != TV_OK)
+        return st;
+    if (num_q_heads != 4 * num_kv_heads)
+        return TV_ERR_UNSUPPORTED;
+    if (a.num_parts == 0)
+        return TV_OK;
+    return from_hip(tv::launch_paged_decode_vector(a, static_cast<hipStream_t>(stream)));
+}
+
 tv_status tv_paged_attention_decode_append(float *part_acc, float *part_max, float *part_sum,
                                            const uint16_t *q, const uint16_t *k_new,
                                            const uint16_t *v_new, const int64_t *slot_mapping,

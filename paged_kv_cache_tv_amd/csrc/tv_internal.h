@@ -134,6 +134,7 @@ hipError_t launch_rope(const RopeArgs &a, hipStream_t stream);
 hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t stream);
 hipError_t launch_paged_prefill(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_paged_decode_vector(const DecodeArgs &a, hipStream_t stream);
 bool paged_decode_seq_fits(const DecodeArgs &a);
 hipError_t launch_paged_decode_seq(const DecodeArgs &a, hipStream_t stream);
 bool paged_decode_group_fits(const DecodeArgs &a);
