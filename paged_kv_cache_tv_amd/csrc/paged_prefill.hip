@@ -253,6 +253,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
     float l_run = 0.f;
     const float cs = a.scale_log2;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // Whether every row of the wavefront has a reference maximum.  Uniform;
+    // set only where the reference moves, so the common step tests a scalar.
+    bool all_ref = false;
 
     unsigned valid_next = 0;
     int32_t e_next = -1;                                      // entries of chunk c + 1 (lanes 0..7)
@@ -277,7 +280,10 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
             continue;                                        // this wave's rows are done
         // V of keys past the context end or in dropped blocks is zeroed in
         // registers (LDS may hold stale data there, NaN included).
-        const bool vfix = c * kChunkKeys + kChunkKeys > n || valid != (1u << kChunkBlocks) - 1;
+        // (Kept as a uniform integer: as a bool the compiler carried it
+        // through a vector register and back on every step.)
+        const int vfix = __builtin_amdgcn_readfirstlane(
+            (c * kChunkKeys + kChunkKeys > n || valid != (1u << kChunkBlocks) - 1) ? 1 : 0);
 
 #pragma unroll
         for (int kp = 0; kp < kPairs; ++kp) {
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
                 return csum;
             };
             float csum = 0.f;
-            bool fresh = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0;
+            bool fresh = !all_ref;
             if (!fresh) {
                 csum = weights(m_use);
                 fresh = __builtin_amdgcn_ballot_w64(!(csum <= kLaneSumLimit)) != 0;
@@ -340,6 +346,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
                 for (int dt = 0; dt < 2; ++dt)
                     o[dt] *= alpha;
                 csum = weights(m_use);
+                all_ref = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) == 0;
             }
             l_run += csum;
 
