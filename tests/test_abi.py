@@ -157,6 +157,34 @@ def test_decode_append_validation(lib):
         assert _app(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
 
 
+def _vec(lib, S=2, hq=32, hkv=8, d=64, bs=16, mb=4, nb=8, mctx=64, part=32, scale=0.125,
+         ptrs=(BAD,) * 8):
+    return lib.tv_paged_attention_decode_vector(*ptrs, S, hq, hkv, d, bs, mb, nb, mctx, part,
+                                                scale, None)
+
+
+def test_decode_vector_validation(lib):
+    """The vector-ALU form checks its arguments as tv_paged_attention_decode
+    does, then refuses every grouping other than 4 query heads per K/V head
+    (empty batches included) before any launch."""
+    assert _vec(lib, S=-1) == TV_ERR_SHAPE
+    assert _vec(lib, hq=30) == TV_ERR_SHAPE
+    assert _vec(lib, part=24) == TV_ERR_SHAPE
+    assert _vec(lib, mctx=65) == TV_ERR_SHAPE
+    assert _vec(lib, scale=0.0) == TV_ERR_SHAPE
+    assert _vec(lib, d=128) == TV_ERR_UNSUPPORTED
+    assert _vec(lib, S=0) == TV_OK
+    assert _vec(lib, mctx=0) == TV_OK
+    assert _vec(lib, ptrs=(BAD,) * 7 + (None,)) == TV_ERR_NULL
+    assert _vec(lib) == TV_ERR_ALIGNMENT
+    ptrs = [ALIGNED] * 8
+    ptrs[0] = 0x1004                                      # part_acc: 16-byte stores
+    assert _vec(lib, ptrs=tuple(ptrs)) == TV_ERR_ALIGNMENT
+    for hq, hkv in ((16, 8), (8, 8), (64, 8), (12, 4)):
+        assert _vec(lib, hq=hq, hkv=hkv, ptrs=(ALIGNED,) * 8) == TV_ERR_UNSUPPORTED
+        assert _vec(lib, S=0, hq=hq, hkv=hkv) == TV_ERR_UNSUPPORTED
+
+
 def test_partition_pass_part_acc_alignment(lib):
     """The partition pass writes part_acc with 16-byte stores: every call that
     takes the workspace refuses a part_acc that is only 4-byte aligned."""
