@@ -1344,9 +1344,9 @@ int group_wgs_per_cu()
 // wavefronts and epilogue as paged_decode_kernel<false, false, PLAN, 4>, with
 // the QK and PV contractions done by the vector ALUs instead of MFMA, for a
 // group of 4 query heads per K/V head.  It is the measured alternative to the
-// matrix form: on MI355X it is slower on every workload measured (the MFMA
-// form issues 10 matrix and about 40 vector instructions per tile, this one
-// about 230 vector instructions).
+// matrix form: on MI355X it is slower on every workload measured (per
+// 16-token tile the MFMA form's compiled step is 10 matrix and about 75
+// vector instructions, this one's about 300 vector instructions).
 //   * K arrives as in the matrix form: lane (r = lane % 16, g = lane / 16)
 //     holds token r's dims 8g..8g+7 and 32+8g..32+8g+7.  Each lane takes its
 //     16-dim part of token r's score for each of the 4 heads (8
