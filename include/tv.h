@@ -575,7 +575,11 @@ tv_status tv_paged_attention_decode_step_noalloc(
  * num_kv_heads in {1, 2, 4, 8, 16}; num_kv_heads * num_seqs *
  * ceil(max_query_len / (256 / (num_q_heads / num_kv_heads))) < 2^23 (the
  * launch grid).  Arithmetic: bf16 products accumulated
- * in fp32, softmax weights rounded to bf16 for the product with V.
+ * in fp32, softmax weights rounded to bf16 for the product with V.  The
+ * summation order, and so the last bits of the result, follows from the
+ * host bounds and the device: a launch of fewer workgroups than two per
+ * compute unit splits each row's keys into two interleaved shares merged at
+ * the end.  The same call on the same device gives the same bits.
  * Odd device data as for the decode call: context lengths are clamped to
  * [0, max_context_len], table entries outside [0, num_blocks) drop their
  * tokens (a row left with no token is 0), positions >= n are never read.

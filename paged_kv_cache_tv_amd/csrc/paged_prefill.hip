@@ -16,6 +16,13 @@
 //     every head of the group.  Launch index: K/V head fastest (one XCD per
 //     head, so the tiles of one (sequence, head) share an L2), and the last,
 //     heaviest tiles of every sequence first.
+//   * Small grids (fewer workgroups than two per compute unit: chunked
+//     prefill of a few sequences) take two key shares: the workgroup's 8
+//     wavefronts are 4 row wavefronts (128 / G chunk rows) times 2 shares,
+//     share h taking the 32-key steps kp with kp % 2 == h of every chunk, so
+//     a long context's chain of steps per wavefront halves and the grid
+//     doubles.  At the end share 1 leaves its (reference, sum, output) in the
+//     chunk buffers and share 0 folds it in by the running-maximum rule.
 //   * Keys go in chunks of 128 (8 blocks), double-buffered in LDS with one
 //     barrier per chunk.  Wavefront w copies block w of the next chunk
 //     straight from memory into LDS (global_load_lds, 16 bytes per lane, no
@@ -61,6 +68,8 @@
 #include "tv_internal.h"
 
 #include <math.h>
+
+#include <atomic>
 
 namespace tv {
 namespace {
@@ -134,11 +143,12 @@ __device__ __forceinline__ void copy_to_lds(const char *src, char *lds)
     __builtin_amdgcn_global_load_lds((const TV_GLOBAL void *)src, (TV_LDS void *)lds, 16, 0, 0);
 }
 
-template <int G>
+template <int G, int KS>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(PrefillArgs a)
 {
+    constexpr int kRowWaves = kWaves / KS;             // wavefronts per key share
     constexpr int kTokPerWave = kRows / G;
-    constexpr int kTokPerWg = kWaves * kTokPerWave;
+    constexpr int kTokPerWg = kRowWaves * kTokPerWave;
     __shared__ __attribute__((aligned(16))) char lds[2 * kBufBytes];
 
     const int kvh = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
@@ -158,6 +168,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar row ranges
+    const int rw = wave % kRowWaves;                          // row wavefront
+    const int kh = wave / kRowWaves;                          // key share: steps kp with kp % KS == kh
     const int lane = tid & 63;
     const int col = lane & 31;                                // this lane's row (MFMA column)
     const int hh = lane >> 5;                                 // which half of the k-slots
@@ -170,7 +182,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
     const int nchunks = wg_last_pos >= 0 ? wg_last_pos / kChunkKeys + 1 : 0;
 
     // This wavefront's rows.
-    const int iw0 = i0 + wave * kTokPerWave;
+    const int iw0 = i0 + rw * kTokPerWave;
     const int iw1 = min(i1, iw0 + kTokPerWave);
     const int wave_first_pos = base_pos + iw0;
     const int wave_last_pos = iw1 > iw0 ? base_pos + iw1 - 1 : -1;   // -1: no rows
@@ -290,6 +302,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
             const int key_base = c * kChunkKeys + 32 * kp;
             if (key_base > wave_last_pos)
                 break;                                       // keys past this wave's rows
+            if (KS > 1 && kp % KS != kh)
+                continue;                                    // the other key share's step
             const bool mask = key_base + 31 > wave_first_pos || ((valid >> (2 * kp)) & 3u) != 3u;
             const char *kb = buf + 2 * kp * kTileBytes + k_rd;
             f32x16 sc = {};
@@ -373,6 +387,47 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
         }
     }
 
+    if (KS > 1) {
+        // Fold the other key shares' states into share 0's, through the chunk
+        // buffers (free once every wavefront is past its last chunk).
+        constexpr int kF = 2 + 32;                           // m, l, o: floats per lane
+        float *st = reinterpret_cast<float *>(lds);
+        auto at = [&](int share, int f) -> float & {
+            return st[((share - 1) * kF + f) * (kRowWaves * 64) + rw * 64 + lane];
+        };
+        __syncthreads();
+        if (kh > 0) {
+            at(kh, 0) = m_ref;
+            at(kh, 1) = l_run;
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    at(kh, 2 + 16 * dt + j) = o[dt][j];
+        }
+        __syncthreads();
+        if (kh > 0)
+            return;
+#pragma unroll
+        for (int sh = 1; sh < KS; ++sh) {
+            const float mb = at(sh, 0);
+            const float mm = max2(m_ref, mb);
+            if (mm != -INFINITY) {
+                // A state with no reference yet holds l = 0 and o = 0 (its
+                // values are relative to 0), so it weighs 0.
+                const float wa = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mm);
+                const float wb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb - mm);
+                l_run = l_run * wa + at(sh, 1) * wb;
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        o[dt][j] = o[dt][j] * wa + at(sh, 2 + 16 * dt + j) * wb;
+                m_ref = mm;
+            }
+        }
+    }
+
     // Normalise and store: element j of dim tile dt is dim 32 dt + 8 (j / 4) + 4 hh + j % 4.
     const float l = pair_sum(l_run);
     if (!row_ok)
@@ -389,19 +444,53 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void paged_prefill_kernel(
         }
 }
 
-template <int G>
-hipError_t launch_g(const PrefillArgs &a, hipStream_t stream)
+// Compute units of the current device (cached; 0 if unknown).
+int prefill_cus()
 {
-    constexpr int kTokPerWg = kWaves * kRows / G;
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 0;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (dev < 64)
+        cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+template <int G, int KS>
+hipError_t launch_gk(const PrefillArgs &a, hipStream_t stream)
+{
+    constexpr int kTokPerWg = (kWaves / KS) * kRows / G;
     const int64_t tiles = (a.max_query_len + kTokPerWg - 1) / kTokPerWg;
     const int64_t grid = tiles * a.num_seqs * a.num_kv_heads;
     if (grid == 0)
         return hipSuccess;
     if (grid > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(paged_prefill_kernel<G>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       a);
+    hipLaunchKernelGGL((paged_prefill_kernel<G, KS>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       stream, a);
     return hipGetLastError();
+}
+
+// Grids smaller than the device's two workgroup slots per compute unit
+// (chunked prefill of a few sequences) take two key shares per row tile.
+template <int G>
+hipError_t launch_g(const PrefillArgs &a, hipStream_t stream)
+{
+    constexpr int kTokPerWg = kWaves * kRows / G;
+    const int64_t grid1 = (int64_t)((a.max_query_len + kTokPerWg - 1) / kTokPerWg) * a.num_seqs *
+                          a.num_kv_heads;
+    const int cus = prefill_cus();
+    if (cus > 0 && grid1 < 2 * (int64_t)cus)
+        return launch_gk<G, 2>(a, stream);
+    return launch_gk<G, 1>(a, stream);
 }
 
 }  // namespace

@@ -106,6 +106,14 @@ def _check(got, ref, what, vrange):
     assert err.max() <= 2.0 ** -9 * vrange and err.mean() <= INTERNAL_MEAN, what
 
 
+# The launch takes two key shares per row tile when its grid (sized by the
+# host bound max_query_len) is smaller than two workgroups per compute unit,
+# as for every small batch here with its tight bound; a loose bound of 4096
+# rows sizes the grid past that (64 tiles x 8 K/V heads already at 4 query
+# heads per K/V head) and takes the one-share form on the same data.
+FORMS = {"two-share": None, "one-share": 4096}
+
+
 @pytest.mark.parametrize("index", [1, 2])
 def test_prefill_workloads_full(dev, oracle_lib, index):
     pb = W.make_prefill_workload(index)
@@ -159,9 +167,10 @@ def test_prefill_workload_3_full(dev, oracle_lib):
     ([0, 5, 63, 64, 100], [64, 65, 1, 255, 256]),
     ([1000, 7, 0, 2049, 300], [257, 129, 300, 40, 511]),
 ])
-def test_prefill_tile_edges(dev, oracle_lib, prior, chunk):
+@pytest.mark.parametrize("form", list(FORMS))
+def test_prefill_tile_edges(dev, oracle_lib, prior, chunk, form):
     pb = W.make_prefill_batch(prior, chunk, 40 + sum(chunk))
-    got = _run_gpu(pb, dev, *_gpu_pools(pb, dev))
+    got = _run_gpu(pb, dev, *_gpu_pools(pb, dev), max_query_len=FORMS[form])
     kc, vc = _oracle_pools(oracle_lib, pb)
     ref = oracle_lib.paged_prefill(pb.q, pb.query_start, kc, vc, pb.base.block_tables,
                                    pb.context_lens, pb.base.scale)
@@ -169,17 +178,19 @@ def test_prefill_tile_edges(dev, oracle_lib, prior, chunk):
 
 
 @pytest.mark.parametrize("group,hkv", [(1, 8), (2, 8), (8, 4), (16, 2), (4, 1)])
-def test_prefill_group_sizes(dev, oracle_lib, group, hkv):
+@pytest.mark.parametrize("form", list(FORMS))
+def test_prefill_group_sizes(dev, oracle_lib, group, hkv, form):
     pb = W.make_prefill_batch([0, 33, 200], [50, 100, 77], 60 + group,
                               num_q_heads=group * hkv, num_kv_heads=hkv)
-    got = _run_gpu(pb, dev, *_gpu_pools(pb, dev))
+    got = _run_gpu(pb, dev, *_gpu_pools(pb, dev), max_query_len=FORMS[form])
     kc, vc = _oracle_pools(oracle_lib, pb)
     ref = oracle_lib.paged_prefill(pb.q, pb.query_start, kc, vc, pb.base.block_tables,
                                    pb.context_lens, pb.base.scale)
     _check(got, ref, f"group {group}, {hkv} K/V heads", _vrange(pb))
 
 
-def test_prefill_empty_and_overlong_chunks(dev, oracle_lib):
+@pytest.mark.parametrize("form", list(FORMS))
+def test_prefill_empty_and_overlong_chunks(dev, oracle_lib, form):
     """Sequences with no rows, an empty context, and a chunk longer than its
     context (rows before position 0 must be exactly 0)."""
     pb = W.make_prefill_batch([0, 10, 0, 30], [20, 0, 0, 45], 70)
@@ -187,7 +198,7 @@ def test_prefill_empty_and_overlong_chunks(dev, oracle_lib):
     lens = pb.context_lens.copy()
     lens[0] = 12                      # 20 rows over 12 positions: rows 0..7 see nothing
     lens[3] = 0                       # 45 rows over an empty context
-    got = _run_gpu(pb, dev, kc_d, vc_d, context_lens=lens)
+    got = _run_gpu(pb, dev, kc_d, vc_d, context_lens=lens, max_query_len=FORMS[form])
     kc, vc = _oracle_pools(oracle_lib, pb)
     ref = oracle_lib.paged_prefill(pb.q, pb.query_start, kc, vc, pb.base.block_tables, lens,
                                    pb.base.scale)
@@ -195,7 +206,8 @@ def test_prefill_empty_and_overlong_chunks(dev, oracle_lib):
     _check(got, ref, "empty and over-long chunks", _vrange(pb))
 
 
-def test_prefill_dropped_blocks(dev, oracle_lib):
+@pytest.mark.parametrize("form", list(FORMS))
+def test_prefill_dropped_blocks(dev, oracle_lib, form):
     """A table entry outside the pool drops that block's 16 positions: each row
     equals attention over its remaining positions, which the oracle computes on
     a table with the block removed."""
@@ -204,7 +216,7 @@ def test_prefill_dropped_blocks(dev, oracle_lib):
     tables = b.block_tables.copy()
     tables[0, 1] = -3                 # positions 16..31 of sequence 0
     tables[1, 4] = b.num_blocks + 5   # positions 64..79 of sequence 1
-    got = _run_gpu(pb, dev, *_gpu_pools(pb, dev), tables=tables)
+    got = _run_gpu(pb, dev, *_gpu_pools(pb, dev), tables=tables, max_query_len=FORMS[form])
     kc, vc = _oracle_pools(oracle_lib, pb)
     for s, dropped in ((0, 1), (1, 4)):
         m, n, r0 = int(pb.query_lens[s]), int(b.context_lens[s]), int(pb.query_start[s])
@@ -220,7 +232,8 @@ def test_prefill_dropped_blocks(dev, oracle_lib):
 
 
 @pytest.mark.parametrize("factor", [8.0, 64.0])
-def test_prefill_score_jumps(dev, oracle_lib, factor):
+@pytest.mark.parametrize("form", list(FORMS))
+def test_prefill_score_jumps(dev, oracle_lib, factor, form):
     """Keys whose scores jump far above everything before them, deep into
     the context: K at every 97th position is multiplied by `factor` (a power
     of two, so exact in bf16), and at every 211th by -`factor`.  With 64 a
@@ -236,20 +249,22 @@ def test_prefill_score_jumps(dev, oracle_lib, factor):
         k[rows[96:n:97]] *= factor
         k[rows[210:n:211]] *= -factor
     b.kv_k[...] = W.round_to_bf16_bits(k)
-    got = _run_gpu(pb, dev, *_gpu_pools(pb, dev))
+    got = _run_gpu(pb, dev, *_gpu_pools(pb, dev), max_query_len=FORMS[form])
     kc, vc = _oracle_pools(oracle_lib, pb)
     ref = oracle_lib.paged_prefill(pb.q, pb.query_start, kc, vc, b.block_tables,
                                    pb.context_lens, b.scale)
     _check(got, ref, f"score jumps x{factor:g}", _vrange(pb))
 
 
-def test_prefill_deterministic_and_block_permutation(dev):
+@pytest.mark.parametrize("form", list(FORMS))
+def test_prefill_deterministic_and_block_permutation(dev, form):
     import torch
     import paged_kv_cache_tv_amd as tv
     pb = W.make_prefill_batch([100, 0, 513], [300, 257, 64], 72)
     kc, vc = _gpu_pools(pb, dev)
-    a1 = _run_gpu(pb, dev, kc, vc)
-    a2 = _run_gpu(pb, dev, kc, vc)
+    mq = FORMS[form]
+    a1 = _run_gpu(pb, dev, kc, vc, max_query_len=mq)
+    a2 = _run_gpu(pb, dev, kc, vc, max_query_len=mq)
     assert np.array_equal(a1, a2), "two runs differ"
     b = pb.base
     perm = np.random.default_rng(5).permutation(b.num_blocks)
@@ -257,7 +272,7 @@ def test_prefill_deterministic_and_block_permutation(dev):
     p = torch.from_numpy(perm).to(dev)
     kc2[p] = kc
     vc2[p] = vc
-    a3 = _run_gpu(pb, dev, kc2, vc2, tables=perm[b.block_tables].astype(np.int32))
+    a3 = _run_gpu(pb, dev, kc2, vc2, tables=perm[b.block_tables].astype(np.int32), max_query_len=mq)
     assert np.array_equal(a1, a3), "output changed under block permutation"
     del tv
 
