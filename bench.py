@@ -843,6 +843,12 @@ def main(argv=None):
         result["block_manager"] = block_manager_rate(tv, K)
     if not args.no_prefill:
         result["prefill"] = prefill_rate(tv, dev, stream, flush, K)
+        # The other prefill workloads (3 short prompts; chunked prefill of 8
+        # sequences), whose grids take the two-key-share form.
+        result["prefill"]["workloads"] = {
+            r["workload"]: {k: r[k] for k in ("rows", "flops_per_launch", "us_per_launch",
+                                              "TFLOP_per_s", "output_finite")}
+            for r in (prefill_rate(tv, dev, stream, flush, K, index=i) for i in (1, 2))}
         result["rope"] = rope_rate(tv, dev, stream, flush, K)
         result["shared_prefix"] = shared_prefix_rate(tv, dev, stream, flush, K)
 
