@@ -301,7 +301,7 @@ def prefill_rate(tv, dev, stream, flush, steps, index=3):
     tflops = flops / (ms * 1e-3) / 1e12
     finite = bool(torch.isfinite(out).all().item())
     del kc, vc, out
-    return {"workload": pb.name, "kernel": "paged_prefill_kernel<4>", "rows": pb.num_rows,
+    return {"workload": pb.name, "kernel": "paged_prefill_kernel<4, 1>", "rows": pb.num_rows,
             "flops_per_launch": flops, "us_per_launch": round(ms * 1e3, 2),
             "us_per_launch_stats": {"median": round(ms * 1e3, 2),
                                     "mean": round(float(each.mean()) * 1e3, 2),
