@@ -126,13 +126,13 @@ namespace {
 
 // Checks shared by both decode entry points; fills `a` on success.  Returns
 // TV_OK with a.num_parts == 0 when there is nothing to launch.
-tv_status check_decode(tv::DecodeArgs &a, float *part_acc, float *part_max, float *part_sum,
-                       const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
-                       const int32_t *block_tables, const int32_t *context_lens,
-                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                       int64_t num_blocks, int32_t max_context_len, int32_t partition_size,
-                       float scale)
+static tv_status check_decode(tv::DecodeArgs &a, float *part_acc, float *part_max, float *part_sum,
+                              const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                              const int32_t *block_tables, const int32_t *context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, int32_t max_context_len, int32_t partition_size,
+                              float scale)
 {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 ||
